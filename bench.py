@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused W4 base + sparse 4-bit residual linear on one MI355X.
+
+One step = the decode hot path on the Llama-7B-shaped MLP up-projection
+(W 11008x4096, group 128, residual density 0.5 %): one fused linear at each
+of M = 1, 4 and 16 tokens. The packed layer is built on the GPU by mq_pack
+before the timed region (packing is timed separately), inputs are resident
+in HBM, and every launch reads a different packed copy so the 256 MB
+Infinity Cache cannot serve the weights.
+
+Printed: one JSON line with the decode GB/s (algorithmic bytes of the
+canonical packed format + X + Y over kernel time), its fraction of the 8 TB/s
+HBM roofline, the prefill TFLOP/s on the 70B-shaped MLP (28672x8192, M = 512
+and 2048) against the 2.5 PFLOP/s dense fp16 MFMA peak, and the CPU oracle
+timed on a bounded sample as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP16_PEAK_TFLOPS = 2516.6      # MI355X dense fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+MALL_BYTES = 256 << 20
+METRIC = "fused W4+sparse-residual linear: GB/s (decode) & TFLOP/s (prefill), % roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--skip-prefill", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+                    help="run one leg only (used for profiling runs)")
+    return ap.parse_args()
+
+
+def decode_bytes(p, M):
+    """Algorithmic bytes of one decode launch: canonical packed layer + X + Y."""
+    return p.canonical_bytes() + 2 * M * p.K + 2 * M * p.N
+
+
+def time_events(fn, n):
+    import torch
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)   # ms
+
+
+def bench_decode(args, mq, synth, torch):
+    wl = synth.WORKLOADS["decode-11008x4096"]
+    layer = wl.layers[0]
+    W = torch.from_numpy(layer.W()).cuda()
+    # packing, timed on its own (GPU events around mq_pack, which ends with a sync)
+    t0 = time.perf_counter()
+    first = mq.mq_pack(W, layer.group, layer.rho)
+    pack_wall_ms = (time.perf_counter() - t0) * 1e3
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    again = mq.mq_pack(W, layer.group, layer.rho)
+    ev1.record()
+    torch.cuda.synchronize()
+    pack_ms = ev0.elapsed_time(ev1)
+    copies = [first, again]
+    ncopy = max(2, math.ceil(2 * MALL_BYTES / first.device_bytes))
+    while len(copies) < ncopy:
+        copies.append(mq.mq_pack(W, layer.group, layer.rho))
+    del W
+    Ms = list(wl.batch)
+    Xs = {M: torch.from_numpy(layer.X(M)).cuda() for M in Ms}
+    Ys = {M: torch.empty((M, layer.N), dtype=torch.float16, device="cuda") for M in Ms}
+
+    def step(i):
+        p = copies[i % ncopy]
+        for M in Ms:
+            mq.mq_linear_with(Xs[M], p, mq.KERNEL_GEMV, Ys[M])
+
+    time_events(step, args.warmup)
+    ms = time_events(step, args.steps)
+    bytes_step = sum(decode_bytes(first, M) for M in Ms)
+    per_m = {}
+    for M in Ms:
+        def one(i, M=M):
+            mq.mq_linear_with(Xs[M], copies[i % ncopy], mq.KERNEL_GEMV, Ys[M])
+        time_events(one, args.warmup)
+        mms = time_events(one, args.steps) / args.steps
+        per_m[str(M)] = {"us": round(mms * 1e3, 3), "GBps": round(decode_bytes(first, M) / mms / 1e6, 1)}
+    # warm, single copy (weights can stay in the Infinity Cache): context only
+    def warm(i):
+        mq.mq_linear_with(Xs[1], first, mq.KERNEL_GEMV, Ys[1])
+    time_events(warm, args.warmup)
+    warm_ms = time_events(warm, args.steps) / args.steps
+    return {
+        "layer": layer, "first": first, "ms_per_step": ms / args.steps, "bytes_step": bytes_step,
+        "launches_per_step": len(Ms), "per_m": per_m, "pack_ms": pack_ms, "pack_wall_ms": pack_wall_ms,
+        "copies": ncopy, "warm_us_m1": warm_ms * 1e3, "nnz": first.nnz,
+    }
+
+
+def bench_prefill(args, mq, synth, torch):
+    wl = synth.WORKLOADS["prefill-28672x8192"]
+    layer = wl.layers[0]
+    W = torch.from_numpy(layer.W()).cuda()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    p = mq.mq_pack(W, layer.group, layer.rho)
+    ev1.record()
+    torch.cuda.synchronize()
+    pack_ms = ev0.elapsed_time(ev1)
+    del W
+    out = {"workload": wl.name, "N": layer.N, "K": layer.K, "rho": layer.rho, "nnz": p.nnz,
+           "pack_ms": round(pack_ms, 3), "M": {}}
+    for M in wl.batch:
+        X = torch.from_numpy(layer.X(M)).cuda()
+        Y = torch.empty((M, layer.N), dtype=torch.float16, device="cuda")
+        n = max(3, min(args.steps, 50))
+
+        def run(i):
+            mq.mq_linear_with(X, p, mq.KERNEL_GEMM, Y)
+        time_events(run, max(2, args.warmup // 4))
+        ms = time_events(run, n) / n
+        tflops = 2.0 * M * layer.N * layer.K / (ms * 1e-3) / 1e12
+        out["M"][str(M)] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tflops, 1),
+                            "frac_mfma_peak": round(tflops / FP16_PEAK_TFLOPS, 4)}
+    p.free()
+    return out
+
+
+def cpu_baseline(layer, Ms):
+    """The oracle, as it stands, on the same decode layer: dequantisation plus
+    the float64 linear for M = 1, 4, 16 (packing by the oracle is done first
+    and reported apart). Bounded: about 10-30 s on a few host cores."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    W = layer.W()
+    t0 = time.perf_counter()
+    packed = oracle.pack(W, layer.group, layer.rho)
+    t_pack = time.perf_counter() - t0
+    Xs = {M: layer.X(M) for M in Ms}
+    t0 = time.perf_counter()
+    Wt = oracle.dequant(packed)
+    for M in Ms:
+        oracle.linear(Xs[M], Wt)
+    t_lin = time.perf_counter() - t0
+    canon = (layer.N * layer.K // 2 + 2 * layer.N * (layer.K // layer.group) + 4 * (layer.N + 1)
+             + 2 * packed["nnz"] + (packed["nnz"] + 1) // 2 + 4 * layer.N)
+    nbytes = sum(canon + 2 * M * layer.K + 2 * M * layer.N for M in Ms)
+    return {"value": round(nbytes / t_lin / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle dequant + float64 linear of the full {layer.N}x{layer.K} layer at M={Ms} "
+                      f"(one step); oracle pack of the layer took {t_pack:.1f} s, not included",
+            "seconds": round(t_lin, 3), "pack_seconds": round(t_pack, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    from bit_gemm_amd import mosaicq as mq
+    from bit_gemm_amd import synth
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    torch.cuda.set_device(0)
+
+    if args.only == "prefill":
+        print(json.dumps({"prefill": bench_prefill(args, mq, synth, torch)}), flush=True)
+        return
+    d = bench_decode(args, mq, synth, torch)
+    value = d["bytes_step"] / (d["ms_per_step"] * 1e-3) / 1e9
+    per_launch_bytes = d["bytes_step"] / d["launches_per_step"]
+    per_launch_ms = d["ms_per_step"] / d["launches_per_step"]
+    achieved = per_launch_bytes / (per_launch_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(d["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": "decode-11008x4096", "N": 11008, "K": 4096, "group": 128, "rho": 0.005,
+                   "nnz": d["nnz"], "M": [1, 4, 16], "kernel": "k_gemv", "packed_copies": d["copies"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "decode_per_M": d["per_m"],
+        "decode_warm_single_copy_us_M1": round(d["warm_us_m1"], 3),
+        "pack": {"workload": "decode-11008x4096", "gpu_ms": round(d["pack_ms"], 3),
+                 "wall_ms_first_call": round(d["pack_wall_ms"], 3)},
+    }
+    if args.only != "decode":
+        if not args.skip_prefill:
+            line["prefill"] = bench_prefill(args, mq, synth, torch)
+        if not args.skip_cpu:
+            line["cpu_baseline"] = cpu_baseline(d["layer"], [1, 4, 16])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,245 @@
+// Host side of the C ABI: argument validation, the packed-layer handle, and
+// dispatch to the HIP kernels. No kernel code lives here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <unordered_set>
+
+#include "mq_internal.h"
+
+#define MQ_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+std::mutex g_mu;
+std::unordered_set<const mq_packed*> g_live;   // handles returned by mq_pack and not yet freed
+
+bool is_live(const mq_packed* p) {
+  if (!p) return false;
+  std::lock_guard<std::mutex> lk(g_mu);
+  return g_live.count(p) != 0 && p->magic == mq::kMagic;
+}
+
+mq_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return MQ_OK;
+  if (e == hipErrorOutOfMemory) return MQ_ERR_OUT_OF_MEMORY;
+  return MQ_ERR_DEVICE;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+void release(mq_packed* p) {
+  void* bufs[] = {p->tiles, p->scales, p->row_ptr, p->col, p->rcodes, p->rscale, p->tile_ptr, p->entries};
+  for (void* b : bufs)
+    if (b) (void)hipFree(b);
+  p->magic = 0;
+  delete p;
+}
+
+}  // namespace
+
+MQ_API const char* mq_status_string(mq_status s) {
+  switch (s) {
+    case MQ_OK: return "MQ_OK";
+    case MQ_ERR_INVALID_ARG: return "MQ_ERR_INVALID_ARG";
+    case MQ_ERR_UNSUPPORTED: return "MQ_ERR_UNSUPPORTED";
+    case MQ_ERR_NONFINITE: return "MQ_ERR_NONFINITE";
+    case MQ_ERR_OUT_OF_MEMORY: return "MQ_ERR_OUT_OF_MEMORY";
+    case MQ_ERR_DEVICE: return "MQ_ERR_DEVICE";
+    case MQ_ERR_BAD_HANDLE: return "MQ_ERR_BAD_HANDLE";
+  }
+  return "MQ_ERR_UNKNOWN";
+}
+
+MQ_API mq_status mq_pack(const void* W_dev_fp16, int64_t N, int64_t K, int32_t group_size,
+                         double residual_density, void* hip_stream, mq_packed** out) {
+  if (out) *out = nullptr;
+  if (!W_dev_fp16 || !out) return MQ_ERR_INVALID_ARG;
+  if (N <= 0 || K <= 0) return MQ_ERR_INVALID_ARG;
+  if (!(residual_density >= 0.0 && residual_density <= 1.0)) return MQ_ERR_INVALID_ARG;   // NaN fails too
+  if (group_size != 32 && group_size != 64 && group_size != 128) return MQ_ERR_UNSUPPORTED;
+  if (K % group_size != 0) return MQ_ERR_INVALID_ARG;
+  if (K > 65536) return MQ_ERR_UNSUPPORTED;
+  if (N >= (int64_t(1) << 31) / K) return MQ_ERR_UNSUPPORTED;   // N * K < 2^31
+  if ((reinterpret_cast<uintptr_t>(W_dev_fp16) & 15u) != 0) return MQ_ERR_INVALID_ARG;
+
+  const int64_t nk = N * K;
+  int64_t nnz = (int64_t)std::floor(residual_density * (double)nk);   // one float64 product, then floor
+  if (nnz > nk) nnz = nk;
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return MQ_ERR_DEVICE;
+
+  mq_packed* p = new (std::nothrow) mq_packed();
+  if (!p) return MQ_ERR_OUT_OF_MEMORY;
+  std::memset(p, 0, sizeof(*p));
+  p->N = N;
+  p->K = K;
+  p->G = group_size;
+  p->rho = residual_density;
+  p->nnz = nnz;
+  p->Nb = ceil_div(N, mq::kRowsPerBlock);
+  p->Kt = ceil_div(K, mq::kTileCols);
+  p->sstride = round_up(p->Kt * mq::kTileCols / group_size, 8);
+  p->device = dev;
+
+  const size_t n_tiles = (size_t)(p->Nb * p->Kt);
+  const size_t sz_tiles = n_tiles * mq::kTileBytes;
+  const size_t sz_scales = (size_t)(p->Nb * mq::kRowsPerBlock * p->sstride) * sizeof(uint16_t);
+  const size_t sz_rowptr = (size_t)(N + 1) * sizeof(int32_t);
+  const size_t sz_col = (size_t)std::max<int64_t>(nnz, 1) * sizeof(uint16_t);
+  const size_t sz_rcodes = (size_t)round_up((nnz + 1) / 2 + 1, 4);
+  const size_t sz_rscale = (size_t)N * sizeof(float);
+  const size_t sz_tptr = (n_tiles + 1) * sizeof(uint32_t);
+  const size_t sz_ent = (size_t)std::max<int64_t>(nnz, 1) * sizeof(uint32_t);
+  struct {
+    void** dst;
+    size_t n;
+  } allocs[] = {{(void**)&p->tiles, sz_tiles},   {(void**)&p->scales, sz_scales}, {(void**)&p->row_ptr, sz_rowptr},
+                {(void**)&p->col, sz_col},       {(void**)&p->rcodes, sz_rcodes}, {(void**)&p->rscale, sz_rscale},
+                {(void**)&p->tile_ptr, sz_tptr}, {(void**)&p->entries, sz_ent}};
+  size_t total = 0;
+  for (auto& a : allocs) {
+    e = hipMalloc(a.dst, a.n);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      release(p);
+      return e == hipErrorOutOfMemory ? MQ_ERR_OUT_OF_MEMORY : MQ_ERR_DEVICE;
+    }
+    total += a.n;
+  }
+  p->bytes = total;
+
+  uint32_t flags = 0;
+  e = mq::pack_on_device(static_cast<const uint16_t*>(W_dev_fp16), p, static_cast<hipStream_t>(hip_stream), &flags);
+  if (e != hipSuccess) {
+    release(p);
+    return from_hip(e);
+  }
+  if (flags & mq::kFlagNonFinite) {
+    release(p);
+    return MQ_ERR_NONFINITE;
+  }
+  if (flags & mq::kFlagScaleOverflow) {
+    release(p);
+    return MQ_ERR_UNSUPPORTED;
+  }
+  if (flags & mq::kFlagCountMismatch) {   // internal consistency check of the selection
+    release(p);
+    return MQ_ERR_DEVICE;
+  }
+  p->magic = mq::kMagic;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_live.insert(p);
+  }
+  *out = p;
+  return MQ_OK;
+}
+
+static mq_status linear_impl(const void* X, int64_t M, const mq_packed* p, void* Y, void* stream, int32_t kernel) {
+  if (!is_live(p)) return MQ_ERR_BAD_HANDLE;
+  if (!X || !Y || M <= 0) return MQ_ERR_INVALID_ARG;
+  if (M > (int64_t(1) << 31) / p->K || M > (int64_t(1) << 31) / p->N) return MQ_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(X) & 15u) != 0 || (reinterpret_cast<uintptr_t>(Y) & 7u) != 0)
+    return MQ_ERR_INVALID_ARG;
+  if (kernel < MQ_KERNEL_AUTO || kernel > MQ_KERNEL_GEMM) return MQ_ERR_INVALID_ARG;
+  bool gemv;
+  if (kernel == MQ_KERNEL_AUTO)
+    gemv = M <= mq::kGemvMaxM;
+  else if (kernel == MQ_KERNEL_GEMV) {
+    if (M > mq::kGemvMaxM) return MQ_ERR_UNSUPPORTED;
+    gemv = true;
+  } else
+    gemv = false;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = gemv ? mq::launch_gemv(p, static_cast<const uint16_t*>(X), M, static_cast<uint16_t*>(Y), s)
+                            : mq::launch_gemm(p, static_cast<const uint16_t*>(X), M, static_cast<uint16_t*>(Y), s);
+  return from_hip(e);
+}
+
+MQ_API mq_status mq_linear(const void* X_dev_fp16, int64_t M, const mq_packed* p, void* Y_dev_fp16,
+                           void* hip_stream) {
+  return linear_impl(X_dev_fp16, M, p, Y_dev_fp16, hip_stream, MQ_KERNEL_AUTO);
+}
+
+MQ_API mq_status mq_linear_with(const void* X_dev_fp16, int64_t M, const mq_packed* p, void* Y_dev_fp16,
+                                void* hip_stream, int32_t kernel) {
+  return linear_impl(X_dev_fp16, M, p, Y_dev_fp16, hip_stream, kernel);
+}
+
+MQ_API mq_status mq_packed_info(const mq_packed* p, int64_t* N, int64_t* K, int32_t* G, int64_t* nnz,
+                                size_t* bytes) {
+  if (!is_live(p)) return MQ_ERR_BAD_HANDLE;
+  if (N) *N = p->N;
+  if (K) *K = p->K;
+  if (G) *G = p->G;
+  if (nnz) *nnz = p->nnz;
+  if (bytes) *bytes = p->bytes;
+  return MQ_OK;
+}
+
+MQ_API mq_status mq_export_canonical(const mq_packed* p, void* codes_u8, void* scales_f16, void* row_ptr_i32,
+                                     void* col_u16, void* rcodes_u8, void* rscale_f32, void* hip_stream) {
+  if (!is_live(p)) return MQ_ERR_BAD_HANDLE;
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = hipSuccess;
+  if (codes_u8) {
+    if ((reinterpret_cast<uintptr_t>(codes_u8) & 15u) != 0) return MQ_ERR_INVALID_ARG;
+    e = mq::export_codes(p, static_cast<uint8_t*>(codes_u8), s);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  if (scales_f16) {
+    e = hipMemcpy2DAsync(scales_f16, (size_t)(p->K / p->G) * 2, p->scales, (size_t)p->sstride * 2,
+                         (size_t)(p->K / p->G) * 2, (size_t)p->N, hipMemcpyDefault, s);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  if (row_ptr_i32) {
+    e = hipMemcpyAsync(row_ptr_i32, p->row_ptr, (size_t)(p->N + 1) * 4, hipMemcpyDefault, s);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  if (p->nnz > 0) {
+    if (col_u16) {
+      e = hipMemcpyAsync(col_u16, p->col, (size_t)p->nnz * 2, hipMemcpyDefault, s);
+      if (e != hipSuccess) return from_hip(e);
+    }
+    if (rcodes_u8) {
+      e = hipMemcpyAsync(rcodes_u8, p->rcodes, (size_t)(p->nnz + 1) / 2, hipMemcpyDefault, s);
+      if (e != hipSuccess) return from_hip(e);
+    }
+  }
+  if (rscale_f32) {
+    e = hipMemcpyAsync(rscale_f32, p->rscale, (size_t)p->N * 4, hipMemcpyDefault, s);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  return MQ_OK;
+}
+
+MQ_API mq_status mq_export_tiled(const mq_packed* p, void* tiles_u8, void* tile_ptr_u32, void* entries_u32,
+                                 void* hip_stream) {
+  if (!is_live(p)) return MQ_ERR_BAD_HANDLE;
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const size_t n_tiles = (size_t)(p->Nb * p->Kt);
+  hipError_t e = hipSuccess;
+  if (tiles_u8) e = hipMemcpyAsync(tiles_u8, p->tiles, n_tiles * mq::kTileBytes, hipMemcpyDefault, s);
+  if (e == hipSuccess && tile_ptr_u32)
+    e = hipMemcpyAsync(tile_ptr_u32, p->tile_ptr, (n_tiles + 1) * 4, hipMemcpyDefault, s);
+  if (e == hipSuccess && entries_u32 && p->nnz > 0)
+    e = hipMemcpyAsync(entries_u32, p->entries, (size_t)p->nnz * 4, hipMemcpyDefault, s);
+  return from_hip(e);
+}
+
+MQ_API void mq_free(mq_packed* p) {
+  if (!p) return;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_live.erase(p)) return;   // unknown or already freed: ignore
+  }
+  release(p);
+}

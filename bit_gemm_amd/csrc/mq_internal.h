@@ -1,0 +1,80 @@
+// Internal declarations shared by the host API and the HIP kernels of the
+// packed 4-bit linear layer. Not part of the public ABI (see include/mosaicq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/mosaicq.h"
+
+namespace mq {
+
+// Geometry of the device layout.
+constexpr int kRowsPerBlock = 16;   // rows of one code tile (one MFMA row block)
+constexpr int kTileCols = 128;      // input columns of one code tile
+constexpr int kTileBytes = 1024;    // 16 rows x 128 columns x 4 bits
+constexpr int kColWindow = 4096;    // residual entries store column mod 4096
+
+struct Packed;  // layout of mq_packed (the opaque handle)
+
+// Residual selection state, written by the radix passes on the device.
+struct SelState {
+  uint64_t prefix;   // bits of the threshold key found so far (key = bits of |e| as a double)
+  uint64_t krem;     // entries still to take among keys equal to the current prefix
+  uint32_t flags;    // kFlag* bits raised by the kernels
+  uint32_t pad;
+};
+constexpr uint32_t kFlagNonFinite = 1u;
+constexpr uint32_t kFlagScaleOverflow = 2u;
+constexpr uint32_t kFlagCountMismatch = 4u;
+
+constexpr int kDigitBits = 13;                  // radix digit width of the top-k select
+constexpr int kDigitBins = 1 << kDigitBits;
+constexpr int kDigitPasses = 4;                 // digits at bits 51, 38, 25, 12 of the key
+// keys are |e| * 2^24 < 2^41 stored as doubles: bits 0..11 are always zero
+
+}  // namespace mq
+
+struct mq_packed {
+  uint64_t magic;
+  int64_t N, K;
+  int32_t G;
+  double rho;
+  int64_t nnz;
+  int64_t Nb;       // row blocks = ceil(N / 16)
+  int64_t Kt;       // column tiles = ceil(K / 128)
+  int64_t sstride;  // scale row stride in elements
+  int device;
+  // device buffers (owned)
+  uint8_t* tiles;       // [Nb][Kt][64][16] base codes
+  uint16_t* scales;     // [Nb*16][sstride] fp16 bits
+  int32_t* row_ptr;     // [N+1]
+  uint16_t* col;        // [nnz]
+  uint8_t* rcodes;      // [(nnz+1)/2 rounded up to 4]
+  float* rscale;        // [N]
+  uint32_t* tile_ptr;   // [Nb*Kt + 1]
+  uint32_t* entries;    // [nnz]
+  size_t bytes;
+};
+
+namespace mq {
+
+constexpr uint64_t kMagic = 0x4d6f736169635134ull;  // "MosaicQ4"
+
+// Packing pipeline (pack.hip). Runs every kernel on `stream`; returns the
+// first HIP error. Temporary buffers are allocated and freed inside.
+hipError_t pack_on_device(const uint16_t* W, mq_packed* p, hipStream_t stream, uint32_t* flags_out);
+
+// Canonical / tiled export (pack.hip).
+hipError_t export_codes(const mq_packed* p, uint8_t* codes, hipStream_t stream);
+
+// Decode kernel (gemv.hip): M <= 64.
+hipError_t launch_gemv(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
+
+// Prefill kernel (gemm.hip): any M >= 1.
+hipError_t launch_gemm(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
+
+constexpr int64_t kGemvMaxM = 64;
+
+}  // namespace mq

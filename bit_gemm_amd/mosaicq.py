@@ -1,0 +1,199 @@
+"""Python binding of include/mosaicq.h (ctypes).
+
+Argument marshalling only: every step of packing and of the fused linear runs
+in the HIP library. torch tensors supply device memory and the current HIP
+stream. Importing this module fails loudly when the library is not built --
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmosaicq.so")
+
+MQ_OK = 0
+STATUS = {
+    0: "MQ_OK", -1: "MQ_ERR_INVALID_ARG", -2: "MQ_ERR_UNSUPPORTED", -3: "MQ_ERR_NONFINITE",
+    -4: "MQ_ERR_OUT_OF_MEMORY", -5: "MQ_ERR_DEVICE", -6: "MQ_ERR_BAD_HANDLE",
+}
+KERNEL_AUTO, KERNEL_GEMV, KERNEL_GEMM = 0, 1, 2
+GEMV_MAX_M = 64
+
+EXPORTED = ("mq_pack", "mq_linear", "mq_linear_with", "mq_packed_info", "mq_export_canonical",
+            "mq_export_tiled", "mq_free", "mq_status_string")
+
+
+class MQError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS.get(code, code)}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built (run `python -m bit_gemm_amd.build`)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.mq_pack.argtypes = [vp, i64, i64, i32, ctypes.c_double, vp, ctypes.POINTER(vp)]
+    lib.mq_pack.restype = ctypes.c_int
+    lib.mq_linear.argtypes = [vp, i64, vp, vp, vp]
+    lib.mq_linear.restype = ctypes.c_int
+    lib.mq_linear_with.argtypes = [vp, i64, vp, vp, vp, i32]
+    lib.mq_linear_with.restype = ctypes.c_int
+    lib.mq_packed_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i32),
+                                   ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_size_t)]
+    lib.mq_packed_info.restype = ctypes.c_int
+    lib.mq_export_canonical.argtypes = [vp] * 8
+    lib.mq_export_canonical.restype = ctypes.c_int
+    lib.mq_export_tiled.argtypes = [vp] * 5
+    lib.mq_export_tiled.restype = ctypes.c_int
+    lib.mq_free.argtypes = [vp]
+    lib.mq_free.restype = None
+    lib.mq_status_string.argtypes = [ctypes.c_int]
+    lib.mq_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def mq_status_string(code: int) -> str:
+    return lib.mq_status_string(int(code)).decode()
+
+
+def _check(code: int, where: str):
+    if code != MQ_OK:
+        raise MQError(code, where)
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev_fp16(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float16:
+        raise TypeError(f"{name} must be a float16 tensor on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Packed:
+    """A packed layer (owns the library handle; freed with free() or on GC)."""
+
+    def __init__(self, handle: ctypes.c_void_p, N: int, K: int, G: int, rho: float):
+        self._h = handle
+        self.N, self.K, self.G, self.rho = N, K, G, rho
+        info = mq_packed_info(self)
+        self.nnz = info["nnz"]
+        self.device_bytes = info["bytes"]
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._h is None:
+            raise MQError(-6, "packed layer already freed")
+        return self._h
+
+    def canonical_bytes(self) -> int:
+        """Bytes of the canonical format: codes, fp16 scales, CSR residual."""
+        return (self.N * self.K // 2 + 2 * self.N * (self.K // self.G) + 4 * (self.N + 1)
+                + 2 * self.nnz + (self.nnz + 1) // 2 + 4 * self.N)
+
+    def free(self):
+        if self._h is not None:
+            lib.mq_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def mq_pack(W, group_size: int = 128, residual_density: float = 0.0, stream=None) -> Packed:
+    """Pack an fp16 [N, K] device tensor (see mq_pack in include/mosaicq.h)."""
+    ptr = _dev_fp16(W, "W")
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [N, K]")
+    N, K = W.shape
+    out = ctypes.c_void_p()
+    _check(lib.mq_pack(ptr, N, K, group_size, float(residual_density), _stream_handle(stream),
+                       ctypes.byref(out)), "mq_pack")
+    return Packed(out, N, K, group_size, float(residual_density))
+
+
+def mq_linear_with(X, packed: Packed, kernel: int = KERNEL_AUTO, Y=None, stream=None):
+    """Y = X (deq(base) + deq(residual))^T, enqueued on `stream` (no sync)."""
+    import torch
+    xp = _dev_fp16(X, "X")
+    if X.dim() != 2 or X.shape[1] != packed.K:
+        raise ValueError(f"X must be [M, {packed.K}]")
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty((M, packed.N), dtype=torch.float16, device=X.device)
+    yp = _dev_fp16(Y, "Y")
+    if tuple(Y.shape) != (M, packed.N):
+        raise ValueError(f"Y must be [{M}, {packed.N}]")
+    _check(lib.mq_linear_with(xp, M, packed.handle, yp, _stream_handle(stream), int(kernel)), "mq_linear")
+    return Y
+
+
+def mq_linear(X, packed: Packed, Y=None, stream=None):
+    return mq_linear_with(X, packed, KERNEL_AUTO, Y, stream)
+
+
+def mq_packed_info(packed: Packed) -> dict:
+    N, K, nnz = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    G, nbytes = ctypes.c_int32(), ctypes.c_size_t()
+    _check(lib.mq_packed_info(packed.handle, ctypes.byref(N), ctypes.byref(K), ctypes.byref(G),
+                              ctypes.byref(nnz), ctypes.byref(nbytes)), "mq_packed_info")
+    return {"N": N.value, "K": K.value, "G": G.value, "nnz": nnz.value, "bytes": nbytes.value}
+
+
+def mq_export_canonical(packed: Packed, stream=None) -> dict:
+    """Canonical arrays as device tensors (synchronises the stream)."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device())
+    N, K, G, nnz = packed.N, packed.K, packed.G, packed.nnz
+    out = {
+        "codes": torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
+        "scales": torch.empty((N, K // G), dtype=torch.float16, device=dev),
+        "row_ptr": torch.empty(N + 1, dtype=torch.int32, device=dev),
+        "col": torch.empty(max(nnz, 1), dtype=torch.int16, device=dev),
+        "rcodes": torch.empty(max((nnz + 1) // 2, 1), dtype=torch.uint8, device=dev),
+        "rscale": torch.empty(N, dtype=torch.float32, device=dev),
+    }
+    s = _stream_handle(stream)
+    _check(lib.mq_export_canonical(packed.handle, *[ctypes.c_void_p(out[k].data_ptr()) for k in
+                                                    ("codes", "scales", "row_ptr", "col", "rcodes", "rscale")],
+                                   s), "mq_export_canonical")
+    torch.cuda.synchronize()
+    out["col"] = out["col"][:nnz]
+    out["rcodes"] = out["rcodes"][:(nnz + 1) // 2]
+    return out
+
+
+def mq_export_tiled(packed: Packed, stream=None) -> dict:
+    """Device layout read by the kernels (synchronises the stream)."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device())
+    Nb = -(-packed.N // 16)
+    Kt = -(-packed.K // 128)
+    out = {
+        "tiles": torch.empty((Nb, Kt, 64, 16), dtype=torch.uint8, device=dev),
+        "tile_ptr": torch.empty(Nb * Kt + 1, dtype=torch.int32, device=dev),
+        "entries": torch.empty(max(packed.nnz, 1), dtype=torch.int32, device=dev),
+    }
+    _check(lib.mq_export_tiled(packed.handle, *[ctypes.c_void_p(out[k].data_ptr()) for k in
+                                                ("tiles", "tile_ptr", "entries")], _stream_handle(stream)),
+           "mq_export_tiled")
+    torch.cuda.synchronize()
+    out["entries"] = out["entries"][:packed.nnz]
+    return out

@@ -1,0 +1,156 @@
+/*
+ * mosaicq.h -- C ABI of the MI355X (gfx950) fused "dense 4-bit base + sparse
+ * 4-bit residual" linear layer.
+ *
+ * What is computed (MosaicQuant explainer, gist.science, Technical Summary,
+ * Methodology section 1, Eq. (1); section 3 "ZipperEngine"):
+ *   the weight W [N, K] (fp16, nn.Linear layout [out, in]) is split into a
+ *   dense INT4 base Q(W) and a sparse INT4 residual R, and the layer computes
+ *   Y = X (Q(W) + R)^T  with X [M, K] and Y [M, N] in fp16, fp32 accumulation,
+ *   in one fused kernel per call.
+ *
+ * Quantiser (readings of the pages, which leave these details open):
+ *   base     s[i,g] = fp16_rne(max_{j in group g} |W_ij| / 7), group = G
+ *            consecutive input columns; q = clamp(rne(W/s), -7, 7) (0 if s = 0);
+ *   error    e = W - s q (exact);
+ *   residual the k = floor(rho N K) entries first in the order (|e| desc,
+ *            row-major index asc) -- the Hessian-weighted block score of the
+ *            pages' Methodology section 2 with an identity Hessian and 1x1
+ *            blocks; per row sr_i = fp32_rne(max selected |e| / 7) and
+ *            qr = clamp(rne(e/sr), -7, 7) (0 if sr = 0).
+ *
+ * Conventions for every entry point:
+ *   - pointers named *_dev are device pointers on the device that is current
+ *     when the call is made; W, X, Y must be contiguous row-major and 16-byte
+ *     aligned; they stay owned by the caller;
+ *   - hip_stream is a hipStream_t (NULL = the default stream); work is enqueued
+ *     on it in order;
+ *   - nothing throws across the ABI; each call returns an mq_status. Arguments
+ *     are validated before any HIP call is made.
+ */
+#ifndef MOSAICQ_H
+#define MOSAICQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mq_packed mq_packed; /* opaque; owns every device buffer of one packed layer */
+
+typedef enum {
+  MQ_OK = 0,
+  MQ_ERR_INVALID_ARG = -1,   /* null pointer, size <= 0, K % G != 0, rho outside [0,1] or NaN */
+  MQ_ERR_UNSUPPORTED = -2,   /* G not in {32,64,128}, K > 65536, N*K >= 2^31, a base scale whose
+                                7*s overflows fp16, or a kernel choice that cannot run this M */
+  MQ_ERR_NONFINITE = -3,     /* W holds Inf or NaN */
+  MQ_ERR_OUT_OF_MEMORY = -4, /* a device allocation failed */
+  MQ_ERR_DEVICE = -5,        /* a HIP call failed (no device, launch failure, fault seen at a sync) */
+  MQ_ERR_BAD_HANDLE = -6     /* the handle is NULL, freed, or was never returned by mq_pack */
+} mq_status;
+
+/*
+ * mq_pack -- disaggregate W into base codes, scales and the sparse residual
+ * (Eq. (1) and the top-K allocation of Methodology section 2, read as above).
+ *
+ *   W_dev_fp16         [N, K] fp16 weights (device, caller-owned, read only)
+ *   N, K               output / input features; K % group_size == 0, K <= 65536,
+ *                      N * K < 2^31
+ *   group_size         G in {32, 64, 128}
+ *   residual_density   rho in [0, 1]; nnz = floor(rho * N * K) residual entries
+ *   hip_stream         stream the packing kernels run on
+ *   out                receives a new handle; *out is set to NULL on failure
+ *
+ * The packing runs entirely on the GPU and is deterministic: the packed
+ * arrays are bit-identical run to run. The call synchronises hip_stream once
+ * at the end (to report MQ_ERR_NONFINITE / MQ_ERR_UNSUPPORTED found on the
+ * device), so it returns with the handle ready. Free it with mq_free.
+ */
+mq_status mq_pack(const void* W_dev_fp16, int64_t N, int64_t K, int32_t group_size,
+                  double residual_density, void* hip_stream, mq_packed** out);
+
+/*
+ * mq_linear -- Y = X (deq(Q_base) + deq(R))^T for one packed layer
+ * (ZipperEngine, Methodology section 3: the residual is applied inside the
+ * dense 4-bit kernel, not by a second kernel).
+ *
+ *   X_dev_fp16   [M, K] fp16 activations (device, caller-owned)
+ *   M            number of tokens, M >= 1
+ *   p            handle from mq_pack (read only; calls on several streams may
+ *                share it)
+ *   Y_dev_fp16   [M, N] fp16 output (device, caller-owned, fully overwritten)
+ *   hip_stream   stream to enqueue on; the call returns without synchronising
+ *
+ * Small M (decode) runs a GEMV-style kernel that streams the 4-bit tiles from
+ * HBM; large M (prefill) runs an MFMA GEMM. Both are deterministic.
+ */
+mq_status mq_linear(const void* X_dev_fp16, int64_t M, const mq_packed* p,
+                    void* Y_dev_fp16, void* hip_stream);
+
+/* Kernel choice for mq_linear_with. */
+typedef enum { MQ_KERNEL_AUTO = 0, MQ_KERNEL_GEMV = 1, MQ_KERNEL_GEMM = 2 } mq_kernel;
+
+/*
+ * mq_linear_with -- mq_linear with the kernel chosen by the caller (tests and
+ * benchmarks pin the dispatch with it). MQ_KERNEL_GEMV accepts M <= 64 and
+ * returns MQ_ERR_UNSUPPORTED above that; MQ_KERNEL_GEMM accepts any M >= 1.
+ */
+mq_status mq_linear_with(const void* X_dev_fp16, int64_t M, const mq_packed* p,
+                         void* Y_dev_fp16, void* hip_stream, int32_t kernel);
+
+/*
+ * mq_packed_info -- sizes of a packed layer; any output pointer may be NULL.
+ *   bytes = device bytes the handle owns.
+ */
+mq_status mq_packed_info(const mq_packed* p, int64_t* N, int64_t* K, int32_t* G,
+                         int64_t* nnz, size_t* bytes);
+
+/*
+ * mq_export_canonical -- copy the packed layer out in the canonical layout
+ * (all destinations are device buffers the caller allocated; any may be NULL
+ * to skip it). Enqueued on hip_stream; synchronise before reading.
+ *   codes_u8    [N, K/2]  base code u = q + 8; byte b of a row holds column 2b
+ *                         in the low nibble and 2b+1 in the high nibble
+ *   scales_f16  [N, K/G]  base scales
+ *   row_ptr_i32 [N+1]     CSR row pointer of the residual
+ *   col_u16     [nnz]     residual column, ascending within each row
+ *   rcodes_u8   [(nnz+1)/2] residual code u = qr + 8, entry 2t in the low
+ *                         nibble of byte t, 2t+1 in the high nibble; an unused
+ *                         last high nibble is 0
+ *   rscale_f32  [N]       residual row scale (0 for rows without entries)
+ */
+mq_status mq_export_canonical(const mq_packed* p, void* codes_u8, void* scales_f16,
+                              void* row_ptr_i32, void* col_u16, void* rcodes_u8,
+                              void* rscale_f32, void* hip_stream);
+
+/*
+ * mq_export_tiled -- copy out the device-side layout the kernels read (for
+ * tests of the packer; any destination may be NULL). With Nb = ceil(N/16) row
+ * blocks and Kt = ceil(K/128) column tiles:
+ *   tiles_u8      [Nb, Kt, 64, 16]  1 KiB per (row block, tile): lane l owns
+ *                 row 16*rb + (l % 16) and columns 128*kt + 32*(l / 16) + [0, 32);
+ *                 in each of its 4 dwords, column offset c (0..7) sits in nibble
+ *                 (c / 2) + 4 * (c % 2); padding holds code 8 (q = 0)
+ *   tile_ptr_u32  [Nb * Kt + 1]     start of each (row block, tile) segment in
+ *                 the residual stream
+ *   entries_u32   [nnz]             residual stream sorted by (row block, tile,
+ *                 row, column): bits 0-11 column mod 4096, bits 12-15 row mod 16,
+ *                 bits 16-31 the fp16 correction fp16(W~ - fp16(s q)) that the
+ *                 kernels add to the dequantised base weight
+ */
+mq_status mq_export_tiled(const mq_packed* p, void* tiles_u8, void* tile_ptr_u32,
+                          void* entries_u32, void* hip_stream);
+
+/* mq_free -- release a handle and its device memory (NULL is accepted). The
+ * caller must make sure no enqueued mq_linear still reads it. */
+void mq_free(mq_packed* p);
+
+/* mq_status_string -- static, human-readable name of a status code. */
+const char* mq_status_string(mq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOSAICQ_H */

@@ -1,0 +1,89 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point include/mosaicq.h declares, and rejects bad arguments before any HIP
+call (status codes only; nothing is computed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "bit_gemm_amd", "libmosaicq.so")
+HEADER = os.path.join(ROOT, "include", "mosaicq.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert os.path.exists(LIB), "libmosaicq.so is not built (python -m bit_gemm_amd.build)"
+    from bit_gemm_amd import mosaicq
+    return mosaicq.lib
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mq_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(
+        ["mq_pack", "mq_linear", "mq_linear_with", "mq_packed_info", "mq_export_canonical",
+         "mq_export_tiled", "mq_free", "mq_status_string"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # nothing else leaks out of the library
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert exported == declared_functions()
+
+
+def test_status_strings(lib):
+    from bit_gemm_amd import mosaicq
+    for code, name in mosaicq.STATUS.items():
+        assert mosaicq.mq_status_string(code) == name
+    assert mosaicq.mq_status_string(12345) == "MQ_ERR_UNKNOWN"
+
+
+FAKE = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced by validation
+
+
+def _pack(lib, W=FAKE, N=32, K=256, G=128, rho=0.1, out=True):
+    h = ctypes.c_void_p()
+    return lib.mq_pack(W, N, K, G, rho, None, ctypes.byref(h) if out else None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=None), -1), (dict(out=False), -1), (dict(N=0), -1), (dict(K=-128), -1),
+    (dict(rho=-0.01), -1), (dict(rho=1.5), -1), (dict(rho=math.nan), -1),
+    (dict(G=48), -2), (dict(G=256), -2), (dict(K=96, G=64), -1),
+    (dict(K=65536 + 128), -2), (dict(N=(1 << 31) // 4096 + 1, K=4096), -2),
+    (dict(W=ctypes.c_void_p((1 << 20) + 2)), -1),
+])
+def test_pack_argument_validation(lib, kw, code):
+    assert _pack(lib, **kw) == code
+
+
+def test_pack_without_a_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _pack(lib) == -5
+
+
+def test_bad_handles_are_rejected(lib):
+    from bit_gemm_amd import mosaicq
+    bogus = ctypes.c_void_p(0xDEADBEE0)
+    assert lib.mq_linear(FAKE, 1, None, FAKE, None) == -6
+    assert lib.mq_linear(FAKE, 1, bogus, FAKE, None) == -6
+    assert lib.mq_linear_with(FAKE, 1, bogus, FAKE, None, mosaicq.KERNEL_GEMV) == -6
+    n = ctypes.c_int64()
+    assert lib.mq_packed_info(bogus, ctypes.byref(n), None, None, None, None) == -6
+    assert lib.mq_export_canonical(bogus, None, None, None, None, None, None, None) == -6
+    assert lib.mq_export_tiled(bogus, None, None, None, None) == -6
+    lib.mq_free(None)        # accepted
+    lib.mq_free(bogus)       # unknown handle: ignored, no crash

@@ -1,0 +1,146 @@
+"""GPU packer vs the CPU oracle: canonical arrays must match bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+from bit_gemm_amd import synth
+from tests.gpu_util import assert_canonical_equal, gpu_canonical, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mq():
+    return require_gpu()
+
+
+def _matrix(kind, N, K, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+        W[:, rng.choice(K, max(1, K // 64), replace=False)] *= 20
+    elif kind == "ties":
+        W = rng.choice(np.array([0.0, 0.25, -0.25, 0.3, 0.31, 1.0, -2.0]), size=(N, K)).astype(np.float16)
+    elif kind == "grid":
+        W = (rng.integers(-40, 41, size=(N, K)) / 16.0).astype(np.float16)
+    elif kind == "tiny":          # subnormal scales and clamped codes
+        W = (rng.standard_normal((N, K)) * 3e-7).astype(np.float16)
+    elif kind == "wide":          # large magnitudes, still below the fp16 overflow guard
+        W = (rng.standard_normal((N, K)) * 3000).astype(np.float16)
+    else:
+        raise ValueError(kind)
+    return W
+
+
+CASES = [
+    (16, 128, 128, 0.05, "normal"),
+    (17, 96, 32, 0.1, "normal"),         # ragged rows, K below one tile
+    (33, 192, 64, 0.3, "ties"),
+    (5, 64, 32, 1.0, "normal"),
+    (40, 256, 128, 0.0, "normal"),
+    (48, 384, 128, 0.02, "grid"),
+    (100, 640, 32, 0.01, "ties"),
+    (31, 4224, 128, 0.004, "normal"),    # two 4096-column windows, ragged tile
+    (64, 512, 64, 0.2, "tiny"),
+    (24, 256, 128, 0.1, "wide"),
+    (3, 65536, 128, 0.001, "normal"),    # widest K the column index allows
+]
+
+
+@pytest.mark.parametrize("N,K,G,rho,kind", CASES)
+def test_pack_matches_oracle_bit_exact(mq, N, K, G, rho, kind):
+    print(f"[pack parity] N={N} K={K} G={G} rho={rho} kind={kind}", flush=True)
+    W = _matrix(kind, N, K, seed=N * 1000 + K)
+    p, got = gpu_canonical(mq, W, G, rho)
+    ref = oracle.pack(W, G, rho)
+    assert p.nnz == ref["nnz"]
+    assert_canonical_equal(got, ref)
+
+
+def test_pack_hand_example(mq):
+    W = np.zeros((2, 64), dtype=np.float16)
+    W[0, :5] = [7.0, -3.5, 2.5, 1.25, 0.5]
+    W[0, 32:36] = [-14.0, 3.0, 5.0, 0.75]
+    W[1, :2] = [0.5, 0.25]
+    p, got = gpu_canonical(mq, W, 32, 5 / 128)
+    assert got["col"].view(np.uint16).tolist() == [1, 2, 33, 34, 35]
+    assert got["rcodes"].tolist() == [0xBB, 0xF1, 0x0D]
+    assert_canonical_equal(got, oracle.pack(W, 32, 5 / 128))
+
+
+@pytest.mark.parametrize("name", ["tiny-1024x1024", "decode-11008x4096"])
+def test_pack_workload_layers_bit_exact(mq, name):
+    layer = synth.WORKLOADS[name].layers[0]
+    print(f"[pack parity] workload {name} N={layer.N} K={layer.K} rho={layer.rho}", flush=True)
+    W = layer.W()
+    p, got = gpu_canonical(mq, W, layer.group, layer.rho)
+    ref = oracle.pack(W, layer.group, layer.rho)
+    assert p.nnz == ref["nnz"] == oracle.budget(layer.rho, layer.N, layer.K)
+    assert_canonical_equal(got, ref)
+
+
+def test_pack_is_deterministic(mq):
+    W = synth.WORKLOADS["tiny-1024x1024"].layers[0].W()
+    _, a = gpu_canonical(mq, W, 128, 0.05)
+    _, b = gpu_canonical(mq, W, 128, 0.05)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_tiled_layout_round_trips_to_canonical(mq):
+    """The kernels' tile layout and residual stream hold exactly the canonical
+    codes and entries (with the documented nibble order and corrections)."""
+    N, K, G, rho = 37, 4224, 64, 0.01
+    W = _matrix("normal", N, K, 7)
+    p, got = gpu_canonical(mq, W, G, rho)
+    ref = oracle.pack(W, G, rho)
+    t = {k: v.cpu().numpy() for k, v in mq.mq_export_tiled(p).items()}
+    Nb, Kt = -(-N // 16), -(-K // 128)
+    tiles = t["tiles"].reshape(Nb, Kt, 64, 4, 4)          # [rb, kt, lane, dword, byte]
+    words = tiles.view(np.uint32).reshape(Nb, Kt, 64, 4)
+    q = ref["q"].astype(np.int16)
+    for i in range(N):
+        rb, r = divmod(i, 16)
+        for j in range(0, K, 7):
+            kt, rem = divmod(j, 128)
+            kq, c = divmod(rem, 32)
+            d, u = divmod(c, 8)
+            nib = (words[rb, kt, r + 16 * kq, d] >> (4 * ((u >> 1) + 4 * (u & 1)))) & 0xF
+            assert nib - 8 == q[i, j]
+    # stream: same entries as the CSR, grouped by (row block, tile)
+    tp = t["tile_ptr"].astype(np.int64)
+    ent = t["entries"].view(np.uint32)
+    assert tp[0] == 0 and tp[-1] == p.nnz
+    Wt = oracle.dequant(ref)
+    s = ref["s"].astype(np.float64)
+    seen = set()
+    for rb in range(Nb):
+        for kt in range(Kt):
+            seg = ent[tp[rb * Kt + kt]:tp[rb * Kt + kt + 1]]
+            keys = []
+            for e in seg.tolist():
+                r, jl, dbits = (e >> 12) & 15, e & 0xFFF, e >> 16
+                i = 16 * rb + r
+                j = (kt * 128 // 4096) * 4096 + jl
+                assert j // 128 == kt
+                keys.append((i, j))
+                base = np.float16(s[i, j // G] * q[i, j])
+                delta = np.array([dbits], np.uint16).view(np.float16)[0]
+                # base + delta reproduces W~ to fp16 precision
+                assert abs(float(base) + float(delta) - Wt[i, j]) <= 2 ** -10 * abs(Wt[i, j]) + 2 ** -24
+                seen.add(i * K + j)
+            assert keys == sorted(keys)
+    assert seen == set(ref["sel"].tolist())
+
+
+def test_pack_rejects_nonfinite_and_overflowing_scales(mq):
+    W = _matrix("normal", 16, 128, 3)
+    W[3, 5] = np.inf
+    with pytest.raises(mq.MQError) as ei:
+        mq.mq_pack(__import__("tests.gpu_util", fromlist=["to_dev"]).to_dev(W), 128, 0.1)
+    assert ei.value.code == -3
+    W = _matrix("normal", 16, 128, 3)
+    W[2, 7] = np.float16(65504.0)          # fp16(65504/7) = 9360 and 7 * 9360 overflows fp16
+    with pytest.raises(mq.MQError) as ei:
+        mq.mq_pack(__import__("tests.gpu_util", fromlist=["to_dev"]).to_dev(W), 128, 0.1)
+    assert ei.value.code == -2
