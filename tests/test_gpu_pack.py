@@ -105,7 +105,7 @@ def test_tiled_layout_round_trips_to_canonical(mq):
             kt, rem = divmod(j, 128)
             kq, c = divmod(rem, 32)
             d, u = divmod(c, 8)
-            nib = (words[rb, kt, r + 16 * kq, d] >> (4 * ((u >> 1) + 4 * (u & 1)))) & 0xF
+            nib = int((words[rb, kt, r + 16 * kq, d] >> (4 * ((u >> 1) + 4 * (u & 1)))) & 0xF)
             assert nib - 8 == q[i, j]
     # stream: same entries as the CSR, grouped by (row block, tile)
     tp = t["tile_ptr"].astype(np.int64)
