@@ -25,7 +25,7 @@ constexpr size_t kLdsBytes = 2ull * (BN + BM) * LDK * sizeof(_Float16);
 
 struct StageRegs {
   uint4 code[2];
-  uint32_t sbits[2];
+  uint32_t sbits[2][4];   // scale of each dword (32-column segment) of the lane
   uint4 x[8];
 };
 
@@ -33,18 +33,22 @@ __device__ __forceinline__ void load_stage(StageRegs& R, const uint4* __restrict
                                            const uint16_t* __restrict__ scales, int64_t sstride,
                                            const uint16_t* __restrict__ X, int M, int N, int K, int G, int Kt,
                                            int Nb, int rb0, int m0, int kt, int wave, int lane) {
-  const int r = lane & 15, g = lane >> 4;
-  const int c0 = kt * kTileCols + 32 * g;
+  const int r = lane & 15;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int rb = rb0 + 2 * wave + j;
     const int row = rb * kRowsPerBlock + r;
     if (rb < Nb) {
       R.code[j] = tiles[((int64_t)rb * Kt + kt) * 64 + lane];
-      R.sbits[j] = (row < N && c0 < K) ? scales[(int64_t)row * sstride + c0 / G] : 0u;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {   // dword t covers columns 128 kt + 32 t + ...
+        const int seg = kt * kTileCols + 32 * t;
+        R.sbits[j][t] = (row < N && seg < K) ? scales[(int64_t)row * sstride + seg / G] : 0u;
+      }
     } else {
       R.code[j] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-      R.sbits[j] = 0u;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) R.sbits[j][t] = 0u;
     }
   }
   const int tid = wave * 64 + lane;
@@ -62,11 +66,12 @@ __device__ __forceinline__ void store_stage(const StageRegs& R, _Float16* Ws, _F
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const half2_t s2 = splat_half(R.sbits[j]);
-    _Float16* dst = Ws + ((2 * wave + j) * kRowsPerBlock + r) * LDK + 32 * g;
+    // dword t of lane (r, g) holds columns 32 t + 8 g + 0..7 of its row
+    _Float16* dst = Ws + ((2 * wave + j) * kRowsPerBlock + r) * LDK + 8 * g;
     const uint32_t d[4] = {R.code[j].x, R.code[j].y, R.code[j].z, R.code[j].w};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) *reinterpret_cast<half8_t*>(dst + 8 * t) = dequant_dword(d[t], s2);
+    for (int t = 0; t < 4; ++t)
+      *reinterpret_cast<half8_t*>(dst + 32 * t) = dequant_dword(d[t], splat_half(R.sbits[j][t]));
   }
   const int tid = wave * 64 + lane;
 #pragma unroll
@@ -77,9 +82,13 @@ __device__ __forceinline__ void store_stage(const StageRegs& R, _Float16* Ws, _F
   }
 }
 
+// Residual entries of the stage: the weight becomes fp16(s q + sr qr), rounded
+// once. q is read back from the widened fp16(s q) in LDS (|q| <= 7, so
+// rint(fp16(s q) / s) recovers it exactly), s from the scale table.
 __device__ __forceinline__ void patch_stage(_Float16* Ws, const uint32_t* __restrict__ tile_ptr,
-                                            const uint32_t* __restrict__ entries, int Nb, int Kt, int rb0, int kt,
-                                            int wave, int lane) {
+                                            const uint32_t* __restrict__ entries,
+                                            const uint16_t* __restrict__ scales, int64_t sstride, int gshift,
+                                            int N, int Nb, int Kt, int rb0, int kt, int wave, int lane) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int rb = rb0 + 2 * wave + j;
@@ -87,8 +96,12 @@ __device__ __forceinline__ void patch_stage(_Float16* Ws, const uint32_t* __rest
     const uint32_t p0 = tile_ptr[(int64_t)rb * Kt + kt], p1 = tile_ptr[(int64_t)rb * Kt + kt + 1];
     for (uint32_t e = p0 + lane; e < p1; e += 64) {
       const uint32_t v = entries[e];
-      _Float16* w = Ws + ((2 * wave + j) * kRowsPerBlock + ent_row(v)) * LDK + (ent_col(v) & (kTileCols - 1));
-      *w = (_Float16)((float)*w + (float)__builtin_bit_cast(_Float16, (uint16_t)ent_delta(v)));
+      const int row = rb * kRowsPerBlock + (int)ent_row(v);
+      const int kk = (int)(ent_col(v) & (kTileCols - 1));
+      const float s = h_to_f(scales[(int64_t)row * sstride + ((kt * kTileCols + kk) >> gshift)]);
+      _Float16* w = Ws + ((2 * wave + j) * kRowsPerBlock + (int)ent_row(v)) * LDK + kk;
+      const float q = (s != 0.f) ? rintf((float)*w / s) : 0.f;
+      *w = (_Float16)fmaf(s, q, h_to_f(ent_delta(v)));
     }
   }
 }
@@ -99,6 +112,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const uint4* __restrict__ til
                                                    const uint32_t* __restrict__ entries,
                                                    const uint16_t* __restrict__ X, uint16_t* __restrict__ Y, int M,
                                                    int N, int K, int G, int Kt, int Nb) {
+  const int gshift = (G == 128) ? 7 : (G == 64) ? 6 : 5;
   extern __shared__ __attribute__((aligned(16))) _Float16 lds[];
   // buffer b: weights at lds + b * BN * LDK, activations after both weight buffers
   _Float16* const Wlds = lds;
@@ -120,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const uint4* __restrict__ til
   load_stage(R, tiles, scales, sstride, X, M, N, K, G, Kt, Nb, rb0, m0, 0, wave, lane);
   store_stage(R, Wlds, Xlds, wave, lane);
   __syncthreads();
-  patch_stage(Wlds, tile_ptr, entries, Nb, Kt, rb0, 0, wave, lane);
+  patch_stage(Wlds, tile_ptr, entries, scales, sstride, gshift, N, Nb, Kt, rb0, 0, wave, lane);
   __syncthreads();
 
   for (int kt = 0; kt < Kt; ++kt) {
@@ -146,7 +160,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const uint4* __restrict__ til
     if (more) {
       store_stage(R, Wlds + (b ^ 1) * BN * LDK, Xlds + (b ^ 1) * BM * LDK, wave, lane);
       __syncthreads();
-      patch_stage(Wlds + (b ^ 1) * BN * LDK, tile_ptr, entries, Nb, Kt, rb0, kt + 1, wave, lane);
+      patch_stage(Wlds + (b ^ 1) * BN * LDK, tile_ptr, entries, scales, sstride, gshift, N, Nb, Kt, rb0, kt + 1,
+                  wave, lane);
     }
     __syncthreads();
   }

@@ -10,10 +10,11 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// One dword of the tile layout holds 8 codes u = q + 8 of columns c0..c0+7,
-// column c in nibble (c / 2) + 4 (c % 2). OR-ing a nibble into the mantissa of
-// fp16 1024.0 (0x6400) gives exactly 1024 + u, so (1024 + u) - 1032 = q exactly
-// and one fp16 multiply by the group scale gives fp16(s q), correctly rounded.
+// One dword of the tile layout holds 8 codes u = q + 8 of 8 consecutive
+// columns, column c in nibble (c / 2) + 4 (c % 2). OR-ing a nibble into the
+// mantissa of fp16 1024.0 (0x6400) gives exactly 1024 + u, so (1024 + u) - 1032
+// = q exactly and one fp16 multiply by the group scale gives fp16(s q),
+// correctly rounded.
 __device__ __forceinline__ half8_t dequant_dword(uint32_t w, half2_t s2) {
   constexpr uint32_t kMagic = 0x64006400u;
   const half2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
@@ -31,6 +32,30 @@ __device__ __forceinline__ half8_t dequant_dword(uint32_t w, half2_t s2) {
   v.z = __builtin_bit_cast(uint32_t, h2);
   v.w = __builtin_bit_cast(uint32_t, h3);
   return __builtin_bit_cast(half8_t, v);
+}
+
+// D = (a & m) | o in one VALU op; m and o must already sit in VGPRs (a VOP3
+// instruction on this target takes neither two SGPRs nor a literal).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(m), "v"(o));
+  return d;
+}
+
+// The 8 codes of one dword as exact fp16 q = u - 8 (no scale), using the
+// masks 0x000F000F and 0x64006400 held in VGPRs.
+__device__ __forceinline__ half8_t widen_q(uint32_t w, uint32_t vmask, uint32_t vmagic) {
+  const half2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  u32x4_t v;
+  v.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, and_or(w, vmask, vmagic)) - bias);
+  v.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, and_or(w >> 4, vmask, vmagic)) - bias);
+  v.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, and_or(w >> 8, vmask, vmagic)) - bias);
+  v.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, and_or(w >> 12, vmask, vmagic)) - bias);
+  return __builtin_bit_cast(half8_t, v);
+}
+
+__device__ __forceinline__ float h_to_f(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
 __device__ __forceinline__ half2_t splat_half(uint32_t bits16) {
@@ -53,7 +78,7 @@ __device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Residual stream entry: column mod 4096 | row mod 16 | fp16 correction.
+// Residual stream entry: column mod 4096 | row mod 16 | fp16 residual value sr*qr.
 __device__ __forceinline__ uint32_t ent_col(uint32_t e) { return e & 0xFFFu; }
 __device__ __forceinline__ uint32_t ent_row(uint32_t e) { return (e >> 12) & 15u; }
 __device__ __forceinline__ uint32_t ent_delta(uint32_t e) { return e >> 16; }
@@ -61,6 +86,21 @@ __device__ __forceinline__ uint32_t ent_delta(uint32_t e) { return e >> 16; }
 // fp32 -> fp16 bits, round to nearest even.
 __device__ __forceinline__ uint16_t f32_to_h(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Store 4 consecutive outputs (as fp16) of which the first `valid` exist; one
+// 8-byte store when all 4 exist and the row is 8-byte aligned.
+__device__ __forceinline__ void store4(uint16_t* y, float4_t s, int valid, bool aligned) {
+  if (valid >= 4 && aligned) {
+    const uint32_t lo = (uint32_t)f32_to_h(s.x) | ((uint32_t)f32_to_h(s.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_h(s.z) | ((uint32_t)f32_to_h(s.w) << 16);
+    *reinterpret_cast<uint2*>(y) = make_uint2(lo, hi);
+  } else {
+    if (valid > 0) y[0] = f32_to_h(s.x);
+    if (valid > 1) y[1] = f32_to_h(s.y);
+    if (valid > 2) y[2] = f32_to_h(s.z);
+    if (valid > 3) y[3] = f32_to_h(s.w);
+  }
 }
 
 }  // namespace mq

@@ -68,13 +68,20 @@ __device__ __forceinline__ uint64_t lane_scale_units(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------- 1. base
+// The wave computes the codes of one 16 x 128 tile (lane l: row l % 16,
+// columns 32 (l / 16) .. +32), then rewrites them through LDS into the kernel
+// layout, where lane l = r + 16 g holds in dword t the columns 32 t + 8 g + c,
+// c = 0..7, at nibble (c / 2) + 4 (c % 2): a dword is then exactly the A
+// operand of one 16x16x32 MFMA step over 32 consecutive columns.
 __global__ __launch_bounds__(kWave) void k_pack_base(const uint16_t* __restrict__ W, int N, int K, int G,
                                                      int Kt, int64_t sstride, uint8_t* __restrict__ tiles,
                                                      uint16_t* __restrict__ scales, SelState* st) {
+  __shared__ uint8_t ucode[kRowsPerBlock][kTileCols];
   const int tile = blockIdx.x;
   const int rb = tile / Kt, kt = tile - (tile / Kt) * Kt;
   const int lane = threadIdx.x;
   const LaneTile t = lane_tile(rb, kt, lane, N, K);
+  const int r = lane & 15, kq = lane >> 4;
   uint32_t w[16];
   uint32_t amax = 0;
   bool finite = true;
@@ -91,22 +98,29 @@ __global__ __launch_bounds__(kWave) void k_pack_base(const uint16_t* __restrict_
   if (G >= 128) amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
   if (!finite) atomicOr(&st->flags, kFlagNonFinite);
 
-  uint4 out = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+  uint8_t* myrow = &ucode[r][32 * kq];
   if (t.valid && finite) {
     uint64_t S;
     const uint32_t sbits = fp16_div7((uint64_t)fp16_units(amax), &S);
-    // 7 s must stay finite in fp16: the fused kernels form s*q in fp16
+    // 7 s must stay finite in fp16: the prefill kernel forms s*q in fp16
     if (7u * S > (2047ull << 29)) atomicOr(&st->flags, kFlagScaleOverflow);
-    uint32_t d[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      const int q = quant7(fp16_units(half_at(w, c)), S);
-      d[c >> 3] |= (uint32_t)(q + 8) << (4 * nib_pos(c & 7));
-    }
-    out = make_uint4(d[0], d[1], d[2], d[3]);
+    for (int c = 0; c < 32; ++c) myrow[c] = (uint8_t)(quant7(fp16_units(half_at(w, c)), S) + 8);
     if ((t.c0 % G) == 0) scales[(int64_t)t.row * sstride + t.c0 / G] = (uint16_t)sbits;
+  } else {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) myrow[c] = 8u;   // padding: q = 0
   }
-  reinterpret_cast<uint4*>(tiles)[(int64_t)tile * kWave + lane] = out;
+  __syncthreads();
+  uint32_t d[4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v |= (uint32_t)ucode[r][32 * s4 + 8 * kq + c] << (4 * nib_pos(c));
+    d[s4] = v;
+  }
+  reinterpret_cast<uint4*>(tiles)[(int64_t)tile * kWave + lane] = make_uint4(d[0], d[1], d[2], d[3]);
 }
 
 // Base errors e = w - s q (units) and their order keys for one lane's 32 entries.
@@ -458,15 +472,11 @@ __global__ __launch_bounds__(kWave) void k_row_emit(const uint16_t* __restrict__
         const int qr = quant7_scaled(e[c], sm, sQ);
         col[pc] = (uint16_t)j;
         atomicOr(&rcodes32[pc >> 3], (uint32_t)(qr + 8) << (4 * (pc & 7)));
-        // Correction the fused kernels add to their fp16 base weight fp16(s q):
-        // delta = fp16(s q + sr qr - fp16(s q)), from exact integer parts.
-        const int64_t sq = fp16_units(half_at(w, c)) - e[c];           // s q in units
-        uint64_t hq;
-        fp16_round_units((uint64_t)(sq < 0 ? -sq : sq), &hq);
-        const int64_t d1 = (sq < 0 ? -sq : sq) - (int64_t)hq;           // |s q| - fp16(|s q|)
-        const double dres = ldexp((double)((int64_t)sm * qr), sQ);      // sr qr in units
-        const double d = ldexp((sq < 0 ? -(double)d1 : (double)d1) + dres, -24);
-        const _Float16 dh = (_Float16)(float)d;
+        // Correction the fused kernels add to the base weight s q: the
+        // residual value sr qr = m qr 2^(Q-24) in fp16 (|m qr| < 2^27, so the
+        // float is within 2^-24 relative; the fp16 rounding dominates).
+        const float dres = ldexpf((float)((int64_t)sm * qr), sQ - 24);
+        const _Float16 dh = (_Float16)dres;
         entries[ps] = ((uint32_t)__builtin_bit_cast(uint16_t, dh) << 16) | ((uint32_t)r << 12) |
                       ((uint32_t)j & (kColWindow - 1));
         ++pc;
@@ -477,7 +487,8 @@ __global__ __launch_bounds__(kWave) void k_row_emit(const uint16_t* __restrict__
   }
 }
 
-// Canonical base codes [N][K/2] from the tile layout: one thread per 32 columns.
+// Canonical base codes [N][K/2] from the tile layout: one thread per 32
+// columns, which sit in dword (c0 % 128) / 32 of the row's four lanes.
 __global__ __launch_bounds__(256) void k_export_codes(const uint8_t* __restrict__ tiles, int N, int K, int Kt,
                                                       uint8_t* __restrict__ codes) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (row, 32-column chunk)
@@ -485,15 +496,18 @@ __global__ __launch_bounds__(256) void k_export_codes(const uint8_t* __restrict_
   if (idx >= (int64_t)N * chunks) return;
   const int row = (int)(idx / chunks), ch = (int)(idx - (idx / chunks) * chunks);
   const int c0 = ch * 32;
-  const int rb = row / kRowsPerBlock, kt = c0 / kTileCols, kq = (c0 % kTileCols) / 32;
-  const int lane = (row % kRowsPerBlock) + 16 * kq;
-  const uint4 v = reinterpret_cast<const uint4*>(tiles)[((int64_t)rb * Kt + kt) * kWave + lane];
-  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  const int rb = row / kRowsPerBlock, kt = c0 / kTileCols, seg = (c0 % kTileCols) / 32;
+  const uint32_t* tw = reinterpret_cast<const uint32_t*>(tiles) + ((int64_t)rb * Kt + kt) * (kWave * 4);
   uint32_t o[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int c = 0; c < 32; ++c) {
-    const uint32_t u = (d[c >> 3] >> (4 * nib_pos(c & 7))) & 0xFu;
-    o[c >> 3] |= u << (4 * (c & 7));       // canonical: column 2b low nibble, 2b+1 high
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t dw = tw[(row % kRowsPerBlock + 16 * g) * 4 + seg];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t u = (dw >> (4 * nib_pos(c))) & 0xFu;
+      const int cc = 8 * g + c;               // column within the 32-column chunk
+      o[cc >> 3] |= u << (4 * (cc & 7));      // canonical: column 2b low nibble, 2b+1 high
+    }
   }
   reinterpret_cast<uint4*>(codes + (int64_t)row * (K / 2) + c0 / 2)[0] = make_uint4(o[0], o[1], o[2], o[3]);
 }

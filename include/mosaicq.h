@@ -130,15 +130,15 @@ mq_status mq_export_canonical(const mq_packed* p, void* codes_u8, void* scales_f
  * tests of the packer; any destination may be NULL). With Nb = ceil(N/16) row
  * blocks and Kt = ceil(K/128) column tiles:
  *   tiles_u8      [Nb, Kt, 64, 16]  1 KiB per (row block, tile): lane l owns
- *                 row 16*rb + (l % 16) and columns 128*kt + 32*(l / 16) + [0, 32);
- *                 in each of its 4 dwords, column offset c (0..7) sits in nibble
- *                 (c / 2) + 4 * (c % 2); padding holds code 8 (q = 0)
+ *                 row 16*rb + (l % 16); its dword t (0..3) holds the 8 columns
+ *                 128*kt + 32*t + 8*(l / 16) + c, c = 0..7, with column offset c
+ *                 in nibble (c / 2) + 4 * (c % 2); padding holds code 8 (q = 0)
  *   tile_ptr_u32  [Nb * Kt + 1]     start of each (row block, tile) segment in
  *                 the residual stream
  *   entries_u32   [nnz]             residual stream sorted by (row block, tile,
  *                 row, column): bits 0-11 column mod 4096, bits 12-15 row mod 16,
- *                 bits 16-31 the fp16 correction fp16(W~ - fp16(s q)) that the
- *                 kernels add to the dequantised base weight
+ *                 bits 16-31 the residual value sr*qr rounded to fp16, which the
+ *                 kernels add to the base weight s*q
  */
 mq_status mq_export_tiled(const mq_packed* p, void* tiles_u8, void* tile_ptr_u32,
                           void* entries_u32, void* hip_stream);

@@ -103,16 +103,17 @@ def test_tiled_layout_round_trips_to_canonical(mq):
         rb, r = divmod(i, 16)
         for j in range(0, K, 7):
             kt, rem = divmod(j, 128)
-            kq, c = divmod(rem, 32)
-            d, u = divmod(c, 8)
-            nib = int((words[rb, kt, r + 16 * kq, d] >> (4 * ((u >> 1) + 4 * (u & 1)))) & 0xF)
+            t4, rem32 = divmod(rem, 32)          # dword t4 holds columns 32 t4 + 8 g + c
+            g, c = divmod(rem32, 8)
+            nib = int((words[rb, kt, r + 16 * g, t4] >> (4 * ((c >> 1) + 4 * (c & 1)))) & 0xF)
             assert nib - 8 == q[i, j]
     # stream: same entries as the CSR, grouped by (row block, tile)
     tp = t["tile_ptr"].astype(np.int64)
     ent = t["entries"].view(np.uint32)
     assert tp[0] == 0 and tp[-1] == p.nnz
-    Wt = oracle.dequant(ref)
-    s = ref["s"].astype(np.float64)
+    sel_pos = {int(v): n for n, v in enumerate(ref["sel"].tolist())}
+    sr = ref["sr"].astype(np.float64)
+    qr = ref["qr"].astype(np.float64)
     seen = set()
     for rb in range(Nb):
         for kt in range(Kt):
@@ -124,10 +125,10 @@ def test_tiled_layout_round_trips_to_canonical(mq):
                 j = (kt * 128 // 4096) * 4096 + jl
                 assert j // 128 == kt
                 keys.append((i, j))
-                base = np.float16(s[i, j // G] * q[i, j])
-                delta = np.array([dbits], np.uint16).view(np.float16)[0]
-                # base + delta reproduces W~ to fp16 precision
-                assert abs(float(base) + float(delta) - Wt[i, j]) <= 2 ** -10 * abs(Wt[i, j]) + 2 ** -24
+                # the stored value is the residual sr * qr rounded to fp16
+                val = sr[i] * qr[sel_pos[i * K + j]]
+                delta = float(np.array([dbits], np.uint16).view(np.float16)[0])
+                assert delta == float(np.float16(val)) or abs(delta - val) <= 2 ** -11 * abs(val) + 2 ** -24
                 seen.add(i * K + j)
             assert keys == sorted(keys)
     assert seen == set(ref["sel"].tolist())
