@@ -97,7 +97,10 @@ MQ_API mq_status mq_pack(const void* W_dev_fp16, int64_t N, int64_t K, int32_t g
   const size_t sz_rcodes = (size_t)round_up((nnz + 1) / 2 + 1, 4);
   const size_t sz_rscale = (size_t)N * sizeof(float);
   const size_t sz_tptr = (n_tiles + 1) * sizeof(uint32_t);
-  const size_t sz_ent = (size_t)std::max<int64_t>(nnz, 1) * sizeof(uint32_t);
+  // the stream pads each row block to a multiple of 32 entries and is
+  // followed by zero entries so kernels may read whole chunks past its end
+  p->stream_cap = nnz + (int64_t)(mq::kChunk - 1) * p->Nb;
+  const size_t sz_ent = (size_t)(p->stream_cap + mq::kEntryPad) * sizeof(uint32_t);
   struct {
     void** dst;
     size_t n;
@@ -230,8 +233,8 @@ MQ_API mq_status mq_export_tiled(const mq_packed* p, void* tiles_u8, void* tile_
   if (tiles_u8) e = hipMemcpyAsync(tiles_u8, p->tiles, n_tiles * mq::kTileBytes, hipMemcpyDefault, s);
   if (e == hipSuccess && tile_ptr_u32)
     e = hipMemcpyAsync(tile_ptr_u32, p->tile_ptr, (n_tiles + 1) * 4, hipMemcpyDefault, s);
-  if (e == hipSuccess && entries_u32 && p->nnz > 0)
-    e = hipMemcpyAsync(entries_u32, p->entries, (size_t)p->nnz * 4, hipMemcpyDefault, s);
+  if (e == hipSuccess && entries_u32 && p->nstream > 0)
+    e = hipMemcpyAsync(entries_u32, p->entries, (size_t)p->nstream * 4, hipMemcpyDefault, s);
   return from_hip(e);
 }
 

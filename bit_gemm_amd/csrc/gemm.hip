@@ -96,6 +96,7 @@ __device__ __forceinline__ void patch_stage(_Float16* Ws, const uint32_t* __rest
     const uint32_t p0 = tile_ptr[(int64_t)rb * Kt + kt], p1 = tile_ptr[(int64_t)rb * Kt + kt + 1];
     for (uint32_t e = p0 + lane; e < p1; e += 64) {
       const uint32_t v = entries[e];
+      if (v == 0u) continue;   // zero padding (a real entry that encodes to 0 changes nothing)
       const int row = rb * kRowsPerBlock + (int)ent_row(v);
       const int kk = (int)(ent_col(v) & (kTileCols - 1));
       const float s = h_to_f(scales[(int64_t)row * sstride + ((kt * kTileCols + kk) >> gshift)]);

@@ -23,6 +23,7 @@ namespace mq {
 namespace {
 
 constexpr int kWaves = 8;
+constexpr size_t kXldsMaxBytes = 64 * 1024;   // X is staged in LDS when M * K * 2 fits
 constexpr int kTpb = 4;   // code tiles per batch of one wave
 
 // clamp(v) helper for token rows: rows >= M read row 0, their outputs are never stored
@@ -41,10 +42,10 @@ struct TileScales {
 
 template <int NS>
 __device__ __forceinline__ void load_scales(TileScales<NS>& S, const uint16_t* __restrict__ scales,
-                                            const int64_t (&srow)[4], const bool (&rowok)[4], int kt) {
+                                            const int (&srow)[4], const bool (&rowok)[4], int kt) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t si = srow[i] + (int64_t)kt * NS;
+    const int si = srow[i] + kt * NS;
     if (NS == 1) {
       S.lo[i] = scales[si];
     } else if (NS == 2) {
@@ -98,66 +99,437 @@ __device__ __forceinline__ void tile_mma(float4_t (&acc)[MB], const uint4 code, 
   }
 }
 
-// GSH = log2(128 / G). XLDS: X staged whole in LDS (M * K * 2 bytes), else X
-// fragments come from global memory. MW: K > 4096 (several column windows).
-// TPW > 0: every wave owns exactly TPW tiles (Kt == 8 TPW, K % 128 == 0) and
-// loads them all up front; TPW == 0: any shape, one tile per iteration.
-template <int MB, int GSH, bool XLDS, bool MW, int TPW>
-__global__ __launch_bounds__(64 * kWaves) void k_gemv(const uint4* __restrict__ tiles,
-                                                      const uint16_t* __restrict__ scales, int64_t sstride,
-                                                      const uint32_t* __restrict__ tile_ptr,
-                                                      const uint32_t* __restrict__ entries,
-                                                      const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
-                                                      int M, int N, int K, int Kt) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [M][K] when XLDS
-  __shared__ float4_t red[kWaves][MB][64];
-  constexpr int NS = 1 << GSH;
-  const int rb = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = lane & 15, g = lane >> 4;
-  const int kt0 = TPW ? wave * TPW : (Kt * wave) / kWaves;
-  const int kt1 = TPW ? kt0 + TPW : (Kt * (wave + 1)) / kWaves;
-  const int64_t tbase = (int64_t)rb * Kt;
-  int mrow[MB];
-  token_rows<MB>(M, r, mrow);
-
-  // ---- residual entries of this wave's first two chunks (issued first)
-  const uint32_t E0 = tile_ptr[tbase], E1 = tile_ptr[tbase + Kt];
-  uint32_t ent[2][8];
+// One residual chunk of 32 entries (8 per lane): an MFMA whose A is one-hot
+// by output row and carries the fp16 residual values, B the X columns the
+// entries name. `first` is the stream index of the chunk's first entry
+// (window bookkeeping when K > 4096); rtp = tile_ptr of the row block.
+template <int MB, bool XLDS, bool MW>
+__device__ __forceinline__ void res_chunk(float4_t (&acc)[MB], const uint4 v0, const uint4 v1, uint32_t first,
+                                          const uint32_t* __restrict__ rtp, int nwin,
+                                          const uint16_t* __restrict__ X, const uint16_t* xs, const int (&mrow)[MB],
+                                          int K, int r, int g) {
+  const uint32_t e[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  int col[8];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint32_t idx = E0 + 32u * (uint32_t)(wave + kWaves * c) + 8u * g + u;
-      ent[c][u] = (idx < E1) ? entries[idx] : 0u;   // entry 0: zero value
+  for (int u = 0; u < 8; ++u) {
+    int wb = 0;
+    if (MW) {   // column window of the entry: count window starts at or below it
+      const uint32_t idx = first + 8 * g + u;
+      for (int w = 1; w < nwin; ++w) wb += (idx >= rtp[32 * w]) ? kColWindow : 0;
     }
+    col[u] = wb + (int)ent_col(e[u]);
+  }
+  u32x4_t av;
+#pragma unroll
+  for (int u = 0; u < 8; u += 2) {
+    const uint32_t lo = (ent_row(e[u]) == (uint32_t)r) ? ent_delta(e[u]) : 0u;
+    const uint32_t hi = (ent_row(e[u + 1]) == (uint32_t)r) ? ent_delta(e[u + 1]) : 0u;
+    av[u >> 1] = lo | (hi << 16);
+  }
+  const half8_t a = __builtin_bit_cast(half8_t, av);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    u32x4_t bv;
+#pragma unroll
+    for (int u = 0; u < 8; u += 2) {
+      uint32_t lo, hi;
+      if (XLDS) {
+        lo = xs[mrow[mb] * K + col[u]];
+        hi = xs[mrow[mb] * K + col[u + 1]];
+      } else {
+        lo = X[mrow[mb] * K + col[u]];
+        hi = X[mrow[mb] * K + col[u + 1]];
+      }
+      bv[u >> 1] = lo | (hi << 16);
+    }
+    acc[mb] = mfma16(a, __builtin_bit_cast(half8_t, bv), acc[mb]);
+  }
+}
 
-  int64_t srow[4];
+// Scales of rows 4g..4g+3 for TPW consecutive tiles when G = 128: one vector
+// load per row (TPW fp16 values, 8- or 16-byte aligned).
+template <int TPW>
+__device__ __forceinline__ void load_scales_run(uint32_t (&w)[4][TPW / 2], const uint16_t* __restrict__ scales,
+                                                const int (&srow)[4], const bool (&rowok)[4], int kt0) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t* p = scales + srow[i] + kt0;
+    if (TPW == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      w[i][0] = rowok[i] ? v.x : 0u;
+      w[i][1] = rowok[i] ? v.y : 0u;
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      w[i][0] = rowok[i] ? v.x : 0u;
+      w[i][1] = rowok[i] ? v.y : 0u;
+      w[i][2] = rowok[i] ? v.z : 0u;
+      w[i][3] = rowok[i] ? v.w : 0u;
+    }
+  }
+}
+
+// Fast decode kernel for K = 4096 and up to 4 tokens (XR = M rounded up to a
+// power of two). One workgroup of 8 waves per 16-row block, 4 code tiles
+// per wave. Memory counters retire in issue order, so the issue order is
+// the consumption order:
+//   1. the wave's own 512 columns of X (16 B per lane per token row), and
+//      the scales of its tiles;
+//   2. code tiles 0 and 1;
+//   3. the row block's residual offsets (scalar loads: waiting for them
+//      overlaps the tiles in flight), then the wave's first two residual
+//      chunks (indices wave and wave + 8);
+//   4. code tiles 2 and 3.
+// The X slices are written to LDS and published by a barrier that waits
+// for LDS traffic only, while the code tiles are still in flight. Tiles 0
+// and 1 are computed first, then the residual chunks (their X columns come
+// from LDS), then tiles 2 and 3, so the residual work overlaps the second
+// half of the stream. Partial 16 x 1 tiles are summed in LDS in a fixed
+// order.
+template <int GSH, int XR>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 6 : 1, 8))) void k_gemv_x(
+    const uint4* __restrict__ tiles, const uint16_t* __restrict__ scales, int sstride,
+    const uint32_t* __restrict__ tile_ptr, const uint32_t* __restrict__ entries, const uint16_t* __restrict__ X,
+    uint16_t* __restrict__ Y, int M, int N, int zero_off) {
+  constexpr int KS = 8, TPW = 4, K = 4096, Kt = 32, NS = 1 << GSH;
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][4096]
+  __shared__ float4_t red[KS][64];
+  const int rb = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int kt0 = wave * TPW, c0 = kt0 * kTileCols, tbase = rb * Kt;
+  int mrow[1];
+  token_rows<1>(M, r, mrow);
+
+  // 1. X slice (rows >= M repeat row 0, never stored) and scales (raw: the
+  // rows past N are zeroed at use, after the loads have been issued)
+  const uint16_t* xsrc = X + c0 + 8 * lane;
+  uint4 x0, x1, x2, x3;
+  x0 = *reinterpret_cast<const uint4*>(xsrc);
+  if constexpr (XR > 1) x1 = *reinterpret_cast<const uint4*>(xsrc + (1 < M ? K : 0));
+  if constexpr (XR > 2) {
+    x2 = *reinterpret_cast<const uint4*>(xsrc + (2 < M ? 2 * K : 0));
+    x3 = *reinterpret_cast<const uint4*>(xsrc + (3 < M ? 3 * K : 0));
+  }
+  int srow[4];
   bool rowok[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = rb * kRowsPerBlock + 4 * g + i;
     rowok[i] = row < N;
-    srow[i] = (int64_t)min(row, N - 1) * sstride;
+    srow[i] = min(row, N - 1) * sstride;
   }
-
-  // ---- all code tiles of the wave (fast path) issued before anything waits
-  constexpr int NT = TPW ? TPW : 1;
-  uint4 code[NT];
-  TileScales<NS> S[NT];
-  if (TPW) {
+  // NS = 1: the 4 tiles' scales of a row are one 8-byte load; else per tile
+  uint2 sraw[4][NS == 1 ? 1 : TPW];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      code[t] = tiles[(tbase + kt0 + t) * 64 + lane];
-      load_scales<NS>(S[t], scales, srow, rowok, kt0 + t);
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (NS == 1) {
+      sraw[i][0] = *reinterpret_cast<const uint2*>(scales + srow[i] + kt0);
+    } else {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const uint16_t* sp = scales + srow[i] + (kt0 + t) * NS;
+        if constexpr (NS == 2) sraw[i][t] = make_uint2(*reinterpret_cast<const uint32_t*>(sp), 0u);
+        else sraw[i][t] = *reinterpret_cast<const uint2*>(sp);
+      }
     }
   }
-  if (XLDS) {
+
+  // 2. code tiles 0 and 1
+  const uint4* tp = tiles + (tbase + kt0) * 64 + lane;
+  uint4 code[TPW];
+  code[0] = tp[0];
+  code[1] = tp[64];
+  __builtin_amdgcn_sched_barrier(0);   // keep the issue order (no instruction crosses)
+
+  // 3. residual chunks wave and wave + 8: two aligned 16-byte loads per lane
+  // each (row-block segments are whole 32-entry chunks); an index past the
+  // row block reads the zero entries after the stream
+  const uint32_t E0 = tile_ptr[tbase], E1 = tile_ptr[tbase + Kt];
+  const uint32_t nchunks = (E1 - E0) / (uint32_t)kChunk;
+  uint4 ent[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t c = (uint32_t)(wave + j * KS);
+    const uint32_t* ep = (c < nchunks) ? entries + E0 + kChunk * c : entries + zero_off;
+    const uint4* e4 = reinterpret_cast<const uint4*>(ep + 8 * g);
+    ent[j][0] = e4[0];
+    ent[j][1] = e4[1];
+  }
+
+  // 4. code tiles 2 and 3
+  __builtin_amdgcn_sched_barrier(0);
+  code[2] = tp[128];
+  code[3] = tp[192];
+
+  // X slices into LDS, published with a wait on LDS traffic only
+  uint16_t* xdst = xs + c0 + 8 * lane;
+  *reinterpret_cast<uint4*>(xdst) = x0;
+  if constexpr (XR > 1) *reinterpret_cast<uint4*>(xdst + K) = x1;
+  if constexpr (XR > 2) {
+    *reinterpret_cast<uint4*>(xdst + 2 * K) = x2;
+    *reinterpret_cast<uint4*>(xdst + 3 * K) = x3;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  uint32_t vmask = 0x000F000Fu, vmagic = 0x64006400u;
+  asm volatile("" : "+v"(vmask), "+v"(vmagic));   // keep both constants in VGPRs for v_and_or_b32
+  float4_t acc[1] = {float4_t{0.f, 0.f, 0.f, 0.f}};
+  auto tile = [&](int t) __attribute__((always_inline)) {
+    TileScales<NS> S;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (NS == 1) {
+        const uint32_t w = (t < 2) ? sraw[i][0].x : sraw[i][0].y;
+        S.lo[i] = rowok[i] ? (w >> (16 * (t & 1))) & 0xFFFFu : 0u;
+      } else {
+        S.lo[i] = rowok[i] ? sraw[i][t].x : 0u;
+        if constexpr (NS == 4) S.hi[i] = rowok[i] ? sraw[i][t].y : 0u;
+      }
+    }
+    tile_mma<1, NS, true, false>(acc, code[t], S, X, xs, mrow, K, kt0 + t, g, vmask, vmagic);
+  };
+  tile(0);
+  tile(1);
+  // residual chunks of this wave; a chunk past the row block is skipped (the
+  // empty use keeps its load ahead of the tiles instead of inside the branch)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t c = (uint32_t)(wave + j * KS);
+    if (c < nchunks)
+      res_chunk<1, true, false>(acc, ent[j][0], ent[j][1], E0 + kChunk * c, tile_ptr + tbase, 1, X, xs, mrow, K, r, g);
+    else
+      asm volatile("" ::"v"(ent[j][0].x), "v"(ent[j][1].x));
+  }
+  tile(2);
+  tile(3);
+  for (uint32_t c = (uint32_t)(wave + 2 * KS); c < nchunks; c += KS) {
+    const uint4* e4 = reinterpret_cast<const uint4*>(entries + E0 + kChunk * c + 8 * g);
+    res_chunk<1, true, false>(acc, e4[0], e4[1], E0 + kChunk * c, tile_ptr + tbase, 1, X, xs, mrow, K, r, g);
+  }
+
+  red[wave][lane] = acc[0];
+  __syncthreads();
+  if (wave == 0) {
+    float4_t sum = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < KS; ++w) sum += red[w][lane];
+    const int n0 = rb * kRowsPerBlock + 4 * g;
+    if (r < M) store4(Y + (int64_t)r * N + n0, sum, N - n0, (N & 3) == 0);
+  }
+}
+
+// Decode kernel for K = 4096 and 5..16 tokens. X ([XR][4096] fp16, up to
+// 128 KiB) fills most of the LDS, so one workgroup per CU holds it and works
+// through R consecutive row blocks with it: X is copied in once (each wave
+// its 512-column slice, straight from global memory into LDS) and
+// published, then every wave requests the scales, its 4 code tiles and its
+// first residual chunk of all R row blocks before computing anything; the
+// row blocks are then computed in order (residual chunks gather their X
+// columns from LDS) and the 8 partials of each are summed in LDS in a fixed
+// order.
+template <int GSH, int XR, int R>
+__global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles, const uint16_t* __restrict__ scales,
+                                               int sstride, const uint32_t* __restrict__ tile_ptr,
+                                               const uint32_t* __restrict__ entries, const uint16_t* __restrict__ X,
+                                               uint16_t* __restrict__ Y, int M, int N, int Nb, int zero_off) {
+  constexpr int KS = 8, TPW = 4, K = 4096, Kt = 32, NS = 1 << GSH;
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][4096]
+  __shared__ float4_t red[R][KS][64];
+  const int rb0 = blockIdx.x * R;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int kt0 = wave * TPW, c0 = kt0 * kTileCols;
+  int mrow[1];
+  token_rows<1>(M, r, mrow);
+
+  // residual segment of each row block (scalar loads, they land during the X copy)
+  uint32_t E0[R], nch[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int tbase = min(rb0 + j, Nb - 1) * Kt;
+    E0[j] = tile_ptr[tbase];
+    nch[j] = (tile_ptr[tbase + Kt] - E0[j]) / (uint32_t)kChunk;
+  }
+
+  // X slice of this wave, one 1 KiB copy per token row (rows >= M are never read)
+#pragma unroll
+  for (int m = 0; m < XR; ++m) {
+    if (m < M)
+      __builtin_amdgcn_global_load_lds(X + m * K + c0 + 8 * lane,
+                                       (__attribute__((address_space(3))) void*)(xs + m * K + c0), 16, 0, 0);
+  }
+  __syncthreads();
+
+  // everything the R row blocks need, requested before any of it is used,
+  // row block by row block (scales, code tiles, the wave's first two
+  // residual chunks: indices wave and wave + 8, zero entries past the end)
+  uint4 code[R][TPW];
+  uint2 sraw[R][4][NS == 1 ? 1 : TPW];
+  uint4 ent[R][2][2];
+  bool live[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int rb = min(rb0 + j, Nb - 1);   // a row block past the end repeats the last (never stored)
+    live[j] = rb0 + j < Nb;
+    const int tbase = rb * Kt;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int srow = min(rb * kRowsPerBlock + 4 * g + i, N - 1) * sstride;
+      if constexpr (NS == 1) {
+        sraw[j][i][0] = *reinterpret_cast<const uint2*>(scales + srow + kt0);
+      } else {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          const uint16_t* sp = scales + srow + (kt0 + t) * NS;
+          if constexpr (NS == 2) sraw[j][i][t] = make_uint2(*reinterpret_cast<const uint32_t*>(sp), 0u);
+          else sraw[j][i][t] = *reinterpret_cast<const uint2*>(sp);
+        }
+      }
+    }
+    const uint4* tp = tiles + (tbase + kt0) * 64 + lane;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) code[j][t] = tp[t * 64];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t c = (uint32_t)(wave + h * KS);
+      const uint32_t* ep = (c < nch[j]) ? entries + E0[j] + kChunk * c : entries + zero_off;
+      const uint4* e4 = reinterpret_cast<const uint4*>(ep + 8 * g);
+      ent[j][h][0] = e4[0];
+      ent[j][h][1] = e4[1];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep row block j's requests ahead of row block j + 1's
+  }
+
+  uint32_t vmask = 0x000F000Fu, vmagic = 0x64006400u;
+  asm volatile("" : "+v"(vmask), "+v"(vmagic));   // keep both constants in VGPRs for v_and_or_b32
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int rb = min(rb0 + j, Nb - 1);
+    float4_t acc[1] = {float4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      TileScales<NS> S;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = rb * kRowsPerBlock + 4 * g + i < N;
+        if constexpr (NS == 1) {
+          const uint32_t w = (t < 2) ? sraw[j][i][0].x : sraw[j][i][0].y;
+          S.lo[i] = ok ? (w >> (16 * (t & 1))) & 0xFFFFu : 0u;
+        } else {
+          S.lo[i] = ok ? sraw[j][i][t].x : 0u;
+          if constexpr (NS == 4) S.hi[i] = ok ? sraw[j][i][t].y : 0u;
+        }
+      }
+      tile_mma<1, NS, true, false>(acc, code[j][t], S, X, xs, mrow, K, kt0 + t, g, vmask, vmagic);
+    }
+    const uint32_t* rtp = tile_ptr + rb * Kt;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      res_chunk<1, true, false>(acc, ent[j][h][0], ent[j][h][1], E0[j] + kChunk * (wave + h * KS), rtp, 1, X, xs, mrow,
+                                K, r, g);
+    for (uint32_t c = (uint32_t)(wave + 2 * KS); c < nch[j]; c += KS) {
+      const uint4* e4 = reinterpret_cast<const uint4*>(entries + E0[j] + kChunk * c + 8 * g);
+      res_chunk<1, true, false>(acc, e4[0], e4[1], E0[j] + kChunk * c, rtp, 1, X, xs, mrow, K, r, g);
+    }
+    red[j][wave][lane] = acc[0];
+  }
+  __syncthreads();
+  if (wave < R && live[wave]) {   // wave j sums row block j
+    const int j = wave, rb = rb0 + j;
+    float4_t sum = red[j][0][lane];
+#pragma unroll
+    for (int w = 1; w < KS; ++w) sum += red[j][w][lane];
+    const int n0 = rb * kRowsPerBlock + 4 * g;
+    if (r < M) store4(Y + (int64_t)r * N + n0, sum, N - n0, (N & 3) == 0);
+  }
+}
+
+// General decode kernel. KS waves per row block. GSH = log2(128 / G).
+// XR > 0: X is copied whole into LDS ([M][K] within [XR][K]) and published
+// before the code tiles are requested, else X fragments come from global
+// memory. MW: K > 4096
+// (several column windows). TPW > 0: every wave owns exactly TPW tiles
+// (Kt == KS * TPW, K % 128 == 0) and issues all its loads up front; TPW == 0:
+// any shape, one tile per iteration.
+// Occupancy: all row blocks of a decode layer should be resident at once, so
+// each SIMD must hold 6 waves of 8-wave groups (80 VGPRs).
+template <int KS, int MB, int GSH, int XR, bool MW, int TPW>
+__global__ __launch_bounds__(64 * KS) __attribute__((amdgpu_waves_per_eu(KS == 8 && TPW == 4 && MB == 1 && GSH == 0 ? 6 : 1, 8))) void k_gemv(const uint4* __restrict__ tiles,
+                                                  const uint16_t* __restrict__ scales, int sstride,
+                                                  const uint32_t* __restrict__ tile_ptr,
+                                                  const uint32_t* __restrict__ entries,
+                                                  const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
+                                                  int M, int N, int K, int Kt, int zero_off) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [M][K] when XR > 0
+  constexpr bool XLDS = XR > 0;
+  __shared__ float4_t red[KS][MB][64];
+  constexpr int NS = 1 << GSH;
+  const int rb = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int kt0 = TPW ? wave * TPW : (Kt * wave) / KS;
+  const int kt1 = TPW ? kt0 + TPW : (Kt * (wave + 1)) / KS;
+  const int tbase = rb * Kt;
+  int mrow[MB];
+  token_rows<MB>(M, r, mrow);
+
+  // ---- loads, in the order the tile loop consumes them (memory counters
+  // retire in issue order, so whatever a tile needs is issued before the
+  // code tiles it waits for).
+  int srow[4];
+  bool rowok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = rb * kRowsPerBlock + 4 * g + i;
+    rowok[i] = row < N;
+    srow[i] = min(row, N - 1) * sstride;
+  }
+  constexpr int NT = TPW ? TPW : 1;
+  constexpr bool RUN = TPW > 0 && NS == 1;   // G = 128: one vector load of scales per row
+  uint32_t srun[4][RUN ? TPW / 2 : 1];
+  TileScales<NS> S[NT];
+  if constexpr (RUN) {
+    load_scales_run<TPW>(srun, scales, srow, rowok, kt0);
+  } else if (TPW) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) load_scales<NS>(S[t], scales, srow, rowok, kt0 + t);
+  }
+
+  if (XLDS) {   // whole X, straight from global memory into LDS, then published
     const int n16 = (M * K) >> 3;
     const uint4* src = reinterpret_cast<const uint4*>(X);
-    uint4* dst = reinterpret_cast<uint4*>(xs);
-    for (int i = threadIdx.x; i < n16; i += 64 * kWaves) dst[i] = src[i];
+    for (int ch = wave; ch * 64 < n16; ch += KS) {
+      if (ch * 64 + lane < n16)
+        __builtin_amdgcn_global_load_lds(src + ch * 64 + lane,
+                                         (__attribute__((address_space(3))) void*)(xs + ch * 512), 16, 0, 0);
+    }
     __syncthreads();
+  }
+
+  // ---- code tiles of the wave (fast path): all issued before anything waits
+  uint4 code[NT];
+  if (TPW) {
+    const uint4* tp = tiles + (tbase + kt0) * 64 + lane;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) code[t] = tp[t * 64];
+  }
+
+  // ---- the wave's first two residual chunks (indices wave and wave + KS),
+  // requested ahead of the tile loop. Row-block segments of the stream are
+  // whole 32-entry chunks (zero padded), so a chunk is two aligned 16-byte
+  // loads per lane; a chunk index past the row block reads the zero entries
+  // after the stream. Both are processed unconditionally after the tiles.
+  const uint32_t E0 = tile_ptr[tbase], E1 = tile_ptr[tbase + Kt];
+  const uint32_t nchunks = (E1 - E0) / (uint32_t)kChunk;
+  const int nwin = (Kt + 31) >> 5;
+  uint4 ent[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t c = (uint32_t)(wave + j * KS);
+    const uint32_t* ep = (c < nchunks) ? entries + E0 + kChunk * c : entries + zero_off;
+    const uint4* e4 = reinterpret_cast<const uint4*>(ep + 8 * g);
+    ent[j][0] = e4[0];
+    ent[j][1] = e4[1];
   }
 
   uint32_t vmask = 0x000F000Fu, vmagic = 0x64006400u;
@@ -168,8 +540,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv(const uint4* __restrict__ 
   for (int mb = 0; mb < MB; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
   if (TPW) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (RUN) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[t].lo[i] = (srun[i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
+      }
       tile_mma<MB, NS, XLDS, false>(acc, code[t], S[t], X, xs, mrow, K, kt0 + t, g, vmask, vmagic);
+    }
   } else {
     for (int kt = kt0; kt < kt1; ++kt) {
       const uint4 c1 = tiles[(tbase + kt) * 64 + lane];
@@ -179,59 +556,16 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv(const uint4* __restrict__ 
     }
   }
 
-  // ---- residual: chunks wave, wave + 8, ... of the row block's entries
-  const uint32_t nchunks = (E1 - E0 + 31u) >> 5;
-  const int nwin = (Kt + 31) >> 5;
-  for (uint32_t c = (uint32_t)wave, ci = 0; c < nchunks; c += kWaves, ++ci) {
-    uint32_t e[8];
-    if (ci < 2) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) e[u] = (ci == 0) ? ent[0][u] : ent[1][u];
-    } else {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t idx = E0 + 32u * c + 8u * g + u;
-        e[u] = (idx < E1) ? entries[idx] : 0u;
-      }
-    }
-    int col[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      int wb = 0;
-      if (MW) {
-        const uint32_t idx = E0 + 32u * c + 8u * g + u;
-        for (int w = 1; w < nwin; ++w) wb += (idx >= tile_ptr[tbase + 32 * w]) ? kColWindow : 0;
-      }
-      col[u] = wb + (int)ent_col(e[u]);
-    }
-    u32x4_t av;
-#pragma unroll
-    for (int u = 0; u < 8; u += 2) {
-      const uint32_t lo = (ent_row(e[u]) == (uint32_t)r) ? ent_delta(e[u]) : 0u;
-      const uint32_t hi = (ent_row(e[u + 1]) == (uint32_t)r) ? ent_delta(e[u + 1]) : 0u;
-      av[u >> 1] = lo | (hi << 16);
-    }
-    const half8_t a = __builtin_bit_cast(half8_t, av);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      u32x4_t bv;
-#pragma unroll
-      for (int u = 0; u < 8; u += 2) {
-        uint32_t lo, hi;
-        if (XLDS) {
-          lo = xs[mrow[mb] * K + col[u]];
-          hi = xs[mrow[mb] * K + col[u + 1]];
-        } else {
-          lo = X[(int64_t)mrow[mb] * K + col[u]];
-          hi = X[(int64_t)mrow[mb] * K + col[u + 1]];
-        }
-        bv[u >> 1] = lo | (hi << 16);
-      }
-      acc[mb] = mfma16(a, __builtin_bit_cast(half8_t, bv), acc[mb]);
-    }
+  // ---- residual: chunks wave, wave + KS, ... of the row block's entries
+  res_chunk<MB, XLDS, MW>(acc, ent[0][0], ent[0][1], E0 + kChunk * wave, tile_ptr + tbase, nwin, X, xs, mrow, K, r, g);
+  res_chunk<MB, XLDS, MW>(acc, ent[1][0], ent[1][1], E0 + kChunk * (wave + KS), tile_ptr + tbase, nwin, X, xs, mrow, K,
+                          r, g);
+  for (uint32_t c = (uint32_t)(wave + 2 * KS); c < nchunks; c += KS) {
+    const uint4* e4 = reinterpret_cast<const uint4*>(entries + E0 + kChunk * c + 8 * g);
+    res_chunk<MB, XLDS, MW>(acc, e4[0], e4[1], E0 + kChunk * c, tile_ptr + tbase, nwin, X, xs, mrow, K, r, g);
   }
 
-  // ---- fixed-order sum of the 8 partial tiles, fp16 output
+  // ---- fixed-order sum of the KS partial tiles, fp16 output
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) red[wave][mb][lane] = acc[mb];
   __syncthreads();
@@ -239,52 +573,113 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemv(const uint4* __restrict__ 
     const int mb = wave;
     float4_t s = red[0][mb][lane];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) s += red[w][mb][lane];
+    for (int w = 1; w < KS; ++w) s += red[w][mb][lane];
     const int m = mb * 16 + r;                   // token
     const int n0 = rb * kRowsPerBlock + 4 * g;   // first of 4 output features
     if (m < M) store4(Y + (int64_t)m * N + n0, s, N - n0, (N & 3) == 0);
   }
 }
 
-constexpr size_t kXldsMax = 64 * 1024;
+constexpr size_t kXldsMax = kXldsMaxBytes;
 
-template <int MB, int GSH, bool XL, bool MWV, int TPW>
-hipError_t launch(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s, size_t xbytes) {
-  if (XL) {
-    static bool done = false;   // once per instantiation: allow 64 KiB of dynamic LDS
-    if (!done) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<MB, GSH, XL, MWV, TPW>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXldsMax);
-      if (e != hipSuccess) return e;
-      done = true;
-    }
-  }
-  k_gemv<MB, GSH, XL, MWV, TPW><<<dim3((unsigned)p->Nb), dim3(64 * kWaves), XL ? xbytes : 0, s>>>(
-      reinterpret_cast<const uint4*>(p->tiles), p->scales, p->sstride, p->tile_ptr, p->entries, X, Y, M,
-      (int)p->N, (int)p->K, (int)p->Kt);
+// once per kernel instantiation: allow kXldsMax bytes of dynamic LDS
+template <typename F>
+hipError_t allow_lds(F* fn, bool& done) {
+  if (done) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXldsMax);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
+template <int GSH, int XR>
+hipError_t launch_x(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
+  static bool done = false;
+  const hipError_t e = allow_lds(&k_gemv_x<GSH, XR>, done);
+  if (e != hipSuccess) return e;
+  k_gemv_x<GSH, XR><<<dim3((unsigned)p->Nb), dim3(512), (size_t)XR * 4096 * 2, s>>>(
+      reinterpret_cast<const uint4*>(p->tiles), p->scales, (int)p->sstride, p->tile_ptr, p->entries, X, Y, M,
+      (int)p->N, (int)p->stream_cap);
   return hipGetLastError();
 }
 
-template <int MB, int GSH, bool XL, bool MWV>
-hipError_t pick_tpw(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s, size_t xbytes) {
-  const bool exact = (p->K % kTileCols) == 0 && (p->Kt % kWaves) == 0;
-  const int64_t tpw = p->Kt / kWaves;
-  if (exact && tpw == 4) return launch<MB, GSH, XL, MWV, 4>(p, X, M, Y, s, xbytes);
-  if (exact && tpw == 8) return launch<MB, GSH, XL, MWV, 8>(p, X, M, Y, s, xbytes);
-  if (exact && tpw == 2) return launch<MB, GSH, XL, MWV, 2>(p, X, M, Y, s, xbytes);
-  if (exact && tpw == 1) return launch<MB, GSH, XL, MWV, 1>(p, X, M, Y, s, xbytes);
-  return launch<MB, GSH, XL, MWV, 0>(p, X, M, Y, s, xbytes);
+constexpr size_t kLdsMaxBytes = 160 * 1024;   // LDS of one CU
+
+template <int GSH, int XR, int R>
+hipError_t launch_r(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
+  static bool done = false;
+  if (!done) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_r<GSH, XR, R>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)(kLdsMaxBytes - R * 8 * 64 * sizeof(float4_t)));
+    if (e != hipSuccess) return e;
+    done = true;
+  }
+  const unsigned grid = (unsigned)((p->Nb + R - 1) / R);
+  k_gemv_r<GSH, XR, R><<<dim3(grid), dim3(512), (size_t)XR * 4096 * 2, s>>>(
+      reinterpret_cast<const uint4*>(p->tiles), p->scales, (int)p->sstride, p->tile_ptr, p->entries, X, Y, M,
+      (int)p->N, (int)p->Nb, (int)p->stream_cap);
+  return hipGetLastError();
+}
+
+// row blocks per workgroup so that one wave of workgroups covers the layer
+template <int GSH, int XR>
+hipError_t launch_r_any(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
+  if (p->Nb <= 256) return launch_r<GSH, XR, 1>(p, X, M, Y, s);
+  if (p->Nb <= 512) return launch_r<GSH, XR, 2>(p, X, M, Y, s);
+  return launch_r<GSH, XR, 3>(p, X, M, Y, s);
+}
+
+// XL: X copied whole into LDS ([M][K], at most kXldsMax bytes)
+template <int KS, int MB, int GSH, int XL, bool MWV, int TPW>
+hipError_t launch(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
+  if (XL) {
+    static bool done = false;
+    const hipError_t e = allow_lds(&k_gemv<KS, MB, GSH, XL, MWV, TPW>, done);
+    if (e != hipSuccess) return e;
+  }
+  k_gemv<KS, MB, GSH, XL, MWV, TPW><<<dim3((unsigned)p->Nb), dim3(64 * KS), XL ? (size_t)M * p->K * 2 : 0, s>>>(
+      reinterpret_cast<const uint4*>(p->tiles), p->scales, (int)p->sstride, p->tile_ptr, p->entries, X, Y, M,
+      (int)p->N, (int)p->K, (int)p->Kt, (int)p->stream_cap);
+  return hipGetLastError();
+}
+
+// Waves per row block and tiles per wave: the fast path needs Kt = KS * TPW;
+// 8 waves x 4 tiles when Kt = 32 (K = 4096), 4 x 4 for K = 2048, 8 x 8 for
+// K = 8192 (one token block only: more would not fit the registers), else
+// the generic one-tile loop over 8 waves.
+template <int MB, int GSH, int XL, bool MWV>
+hipError_t pick_shape(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
+  const bool k128 = (p->K % kTileCols) == 0;
+  if constexpr (!MWV) {
+    if (k128 && p->Kt == 32) return launch<kWaves, MB, GSH, XL, false, 4>(p, X, M, Y, s);
+    if (k128 && p->Kt == 16) return launch<4, MB, GSH, XL, false, 4>(p, X, M, Y, s);
+  } else if constexpr (MB == 1) {
+    if (k128 && p->Kt == 64) return launch<kWaves, MB, GSH, XL, true, 8>(p, X, M, Y, s);
+  }
+  return launch<kWaves, MB, GSH, XL, MWV, 0>(p, X, M, Y, s);
+}
+
+template <int MB, int GSH, int XL>
+hipError_t run_x(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
+  return p->Kt > 32 ? pick_shape<MB, GSH, XL, true>(p, X, M, Y, s) : pick_shape<MB, GSH, XL, false>(p, X, M, Y, s);
 }
 
 template <int MB, int GSH>
 hipError_t run(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
-  const size_t xbytes = (size_t)M * p->K * 2;
-  const bool xlds = MB == 1 && xbytes <= kXldsMax;
-  const bool mw = p->Kt > 32;
-  if (xlds) return mw ? pick_tpw<MB, GSH, true, true>(p, X, M, Y, s, xbytes)
-                      : pick_tpw<MB, GSH, true, false>(p, X, M, Y, s, xbytes);
-  return mw ? pick_tpw<MB, GSH, false, true>(p, X, M, Y, s, xbytes)
-            : pick_tpw<MB, GSH, false, false>(p, X, M, Y, s, xbytes);
+  if constexpr (MB == 1) {
+    if (p->K == 4096 && M <= 4) {   // fast kernel: X slices in LDS, residual amid the tiles
+      if (M == 1) return launch_x<GSH, 1>(p, X, M, Y, s);
+      if (M == 2) return launch_x<GSH, 2>(p, X, M, Y, s);
+      return launch_x<GSH, 4>(p, X, M, Y, s);
+    }
+    if (p->K == 4096) {   // 5..16 tokens: X whole in LDS, several row blocks per workgroup
+      if (M <= 8) return launch_r_any<GSH, 8>(p, X, M, Y, s);
+      return launch_r_any<GSH, 16>(p, X, M, Y, s);
+    }
+    if ((size_t)M * p->K * 2 <= kXldsMax) return run_x<MB, GSH, 1>(p, X, M, Y, s);
+  }
+  return run_x<MB, GSH, 0>(p, X, M, Y, s);
 }
 
 template <int MB>

@@ -15,6 +15,8 @@ constexpr int kRowsPerBlock = 16;   // rows of one code tile (one MFMA row block
 constexpr int kTileCols = 128;      // input columns of one code tile
 constexpr int kTileBytes = 1024;    // 16 rows x 128 columns x 4 bits
 constexpr int kColWindow = 4096;    // residual entries store column mod 4096
+constexpr int kEntryPad = 1024;     // zero entries after the residual stream (read-ahead slack)
+constexpr int kChunk = 32;          // residual entries per MFMA chunk; row-block segments are padded to it
 
 struct Packed;  // layout of mq_packed (the opaque handle)
 
@@ -54,7 +56,9 @@ struct mq_packed {
   uint8_t* rcodes;      // [(nnz+1)/2 rounded up to 4]
   float* rscale;        // [N]
   uint32_t* tile_ptr;   // [Nb*Kt + 1]
-  uint32_t* entries;    // [nnz]
+  uint32_t* entries;    // [nstream + kEntryPad]: residual stream, row blocks padded to 32 entries
+  int64_t nstream;      // entries in the stream incl. the per-row-block zero padding
+  int64_t stream_cap;   // allocated stream length (excluding the trailing zero pad)
   size_t bytes;
 };
 

@@ -350,6 +350,7 @@ __global__ __launch_bounds__(kWave) void k_row_select(const uint16_t* __restrict
   const uint64_t ebase = (row < N) ? eq_base[row] : 0u;
   uint64_t run_tie = 0;      // ties of this row in earlier tiles
   uint64_t maxkey = 0;
+  uint32_t rb_total = 0;     // stream entries of the row block (lane 0)
   for (int kt = 0; kt < Kt; ++kt) {
     const LaneTile t = lane_tile(rb, kt, lane, N, K);
     uint64_t key[32];
@@ -376,7 +377,11 @@ __global__ __launch_bounds__(kWave) void k_row_select(const uint16_t* __restrict
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o);
     if (lane == 0) tile_cnt[(int64_t)rb * Kt + kt] = v;
+    rb_total += v;
   }
+  // pad the row block's stream segment to whole 32-entry chunks (zero entries)
+  if (lane == 0 && (rb_total % kChunk) != 0)
+    tile_cnt[(int64_t)rb * Kt + Kt - 1] += kChunk - rb_total % kChunk;
   // max over the row's four lanes
   maxkey = max(maxkey, (uint64_t)__shfl_xor((unsigned long long)maxkey, 16));
   maxkey = max(maxkey, (uint64_t)__shfl_xor((unsigned long long)maxkey, 32));
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(kWave) void k_row_emit(const uint16_t* __restrict__
                                                     const uint32_t* __restrict__ tile_ptr,
                                                     uint16_t* __restrict__ col, uint32_t* __restrict__ rcodes32,
                                                     uint32_t* __restrict__ entries, int64_t nnz,
-                                                    SelState* flags) {
+                                                    int64_t stream_cap, SelState* flags) {
   const int rb = blockIdx.x, lane = threadIdx.x;
   const int r = lane & 15;
   const uint64_t T = st->prefix, krem = st->krem;
@@ -465,7 +470,7 @@ __global__ __launch_bounds__(kWave) void k_row_emit(const uint16_t* __restrict__
       for (int c = 0; c < 32; ++c) {
         if (!((sel >> c) & 1u)) continue;
         const int j = t.c0 + c;
-        if (pc >= nnz || (int64_t)ps >= nnz) {   // counts disagree: never write out of bounds
+        if (pc >= nnz || (int64_t)ps >= stream_cap) {   // counts disagree: never write out of bounds
           atomicOr(&flags->flags, kFlagCountMismatch);
           break;
         }
@@ -543,6 +548,7 @@ hipError_t pack_on_device(const uint16_t* W, mq_packed* p, hipStream_t stream, u
   MQ_TRY(hipMemsetAsync(p->rscale, 0, (size_t)N * sizeof(float), stream));
   MQ_TRY(hipMemsetAsync(p->row_ptr, 0, (size_t)(N + 1) * sizeof(int32_t), stream));
   MQ_TRY(hipMemsetAsync(p->tile_ptr, 0, (size_t)(ntiles + 1) * sizeof(uint32_t), stream));
+  MQ_TRY(hipMemsetAsync(p->entries, 0, (size_t)(p->stream_cap + kEntryPad) * sizeof(uint32_t), stream));
 
   k_pack_base<<<dim3((unsigned)ntiles), dim3(kWave), 0, stream>>>(W, N, K, G, Kt, p->sstride, p->tiles,
                                                                  p->scales, st);
@@ -584,13 +590,17 @@ hipError_t pack_on_device(const uint16_t* W, mq_packed* p, hipStream_t stream, u
     k_row_emit<<<dim3(Nb), dim3(kWave), 0, stream>>>(W, p->scales, N, K, G, Kt, p->sstride, st, eb, p->row_ptr,
                                                      p->rscale, crt, p->tile_ptr, p->col,
                                                      reinterpret_cast<uint32_t*>(p->rcodes), p->entries, p->nnz,
-                                                     st);
+                                                     p->stream_cap, st);
     MQ_TRY(hipGetLastError());
   }
   SelState fin;
+  uint32_t nstream = 0;
   MQ_TRY(hipMemcpyAsync(&fin, st, sizeof(fin), hipMemcpyDeviceToHost, stream));
+  MQ_TRY(hipMemcpyAsync(&nstream, p->tile_ptr + ntiles, sizeof(nstream), hipMemcpyDeviceToHost, stream));
   MQ_TRY(hipStreamSynchronize(stream));
   *flags_out = fin.flags;
+  p->nstream = nstream;
+  if ((int64_t)nstream > p->stream_cap) *flags_out |= kFlagCountMismatch;
   return hipSuccess;
 }
 

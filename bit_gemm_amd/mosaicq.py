@@ -186,14 +186,15 @@ def mq_export_tiled(packed: Packed, stream=None) -> dict:
     dev = torch.device("cuda", torch.cuda.current_device())
     Nb = -(-packed.N // 16)
     Kt = -(-packed.K // 128)
-    out = {
-        "tiles": torch.empty((Nb, Kt, 64, 16), dtype=torch.uint8, device=dev),
-        "tile_ptr": torch.empty(Nb * Kt + 1, dtype=torch.int32, device=dev),
-        "entries": torch.empty(max(packed.nnz, 1), dtype=torch.int32, device=dev),
-    }
-    _check(lib.mq_export_tiled(packed.handle, *[ctypes.c_void_p(out[k].data_ptr()) for k in
-                                                ("tiles", "tile_ptr", "entries")], _stream_handle(stream)),
+    tiles = torch.empty((Nb, Kt, 64, 16), dtype=torch.uint8, device=dev)
+    tile_ptr = torch.empty(Nb * Kt + 1, dtype=torch.int32, device=dev)
+    s = _stream_handle(stream)
+    _check(lib.mq_export_tiled(packed.handle, ctypes.c_void_p(tiles.data_ptr()),
+                               ctypes.c_void_p(tile_ptr.data_ptr()), None, s), "mq_export_tiled")
+    torch.cuda.synchronize()
+    nstream = int(tile_ptr[-1].item())
+    entries = torch.empty(max(nstream, 1), dtype=torch.int32, device=dev)
+    _check(lib.mq_export_tiled(packed.handle, None, None, ctypes.c_void_p(entries.data_ptr()), s),
            "mq_export_tiled")
     torch.cuda.synchronize()
-    out["entries"] = out["entries"][:packed.nnz]
-    return out
+    return {"tiles": tiles, "tile_ptr": tile_ptr, "entries": entries[:nstream]}

@@ -134,11 +134,12 @@ mq_status mq_export_canonical(const mq_packed* p, void* codes_u8, void* scales_f
  *                 128*kt + 32*t + 8*(l / 16) + c, c = 0..7, with column offset c
  *                 in nibble (c / 2) + 4 * (c % 2); padding holds code 8 (q = 0)
  *   tile_ptr_u32  [Nb * Kt + 1]     start of each (row block, tile) segment in
- *                 the residual stream
- *   entries_u32   [nnz]             residual stream sorted by (row block, tile,
+ *                 the residual stream; tile_ptr[Nb * Kt] is the stream length
+ *   entries_u32   [tile_ptr[Nb*Kt]] residual stream sorted by (row block, tile,
  *                 row, column): bits 0-11 column mod 4096, bits 12-15 row mod 16,
  *                 bits 16-31 the residual value sr*qr rounded to fp16, which the
- *                 kernels add to the base weight s*q
+ *                 kernels add to the base weight s*q. Each row block's segment
+ *                 ends with zero entries up to a multiple of 32.
  */
 mq_status mq_export_tiled(const mq_packed* p, void* tiles_u8, void* tile_ptr_u32,
                           void* entries_u32, void* hip_stream);

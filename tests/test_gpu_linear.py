@@ -64,6 +64,27 @@ def test_one_hot_rows_reproduce_the_dequantised_weights(mq):
             assert np.all(np.abs(Y - ref) <= 2 ** -10 * np.abs(ref) + 2 ** -24), (j0, kern)
 
 
+# K = 4096 decode shapes: the up-to-4-token kernel (X slices in LDS) and the
+# several-row-blocks-per-workgroup kernel (1, 2 or 3 row blocks, the last
+# workgroup partly past the end), ragged N, no residual, and residual
+# densities whose chunks overflow the two prefetched per wave
+K4096 = [(40, 128, 0.3), (16, 128, 0.0), (4100, 64, 0.01), (8210, 32, 0.002), (1000, 128, 0.02)]
+
+
+@pytest.mark.parametrize("N,G,rho", K4096)
+def test_linear_k4096_decode_paths(mq, N, G, rho):
+    K = 4096
+    W = _layer(N, K, seed=N + G)
+    p = mq.mq_pack(to_dev(W), G, rho)
+    Wt = oracle.dequant(oracle.pack(W, G, rho))
+    for M in (1, 2, 3, 4, 5, 8, 9, 16):
+        X = _x(M, K, seed=100 + M)
+        for kern in (mq.KERNEL_GEMV, mq.KERNEL_GEMM):
+            print(f"[linear parity] K=4096 N={N} G={G} rho={rho} M={M} kernel={kern}", flush=True)
+            Y = mq.mq_linear_with(to_dev(X), p, kern).cpu().numpy()
+            check_linear(Y, X, Wt, f"K=4096 N={N} G={G} rho={rho} M={M} kernel={kern}")
+
+
 @pytest.mark.parametrize("name", ["tiny-1024x1024", "decode-11008x4096"])
 def test_linear_workload_layers(mq, name):
     wl = synth.WORKLOADS[name]
