@@ -8,15 +8,23 @@ before the timed region (packing is timed separately), inputs are resident
 in HBM, and every launch reads a different packed copy so the 256 MB
 Infinity Cache cannot serve the weights.
 
+Timing: the warm-up steps and the timed steps are each captured once as a
+HIP graph and replayed between device synchronisations, so the figures are
+GPU time and not the Python launch rate (a decode launch is shorter than one
+ctypes call through torch).
+
 Printed: one JSON line with the decode GB/s (algorithmic bytes of the
-canonical packed format + X + Y over kernel time), its fraction of the 8 TB/s
-HBM roofline, the prefill TFLOP/s on the 70B-shaped MLP (28672x8192, M = 512
-and 2048) against the 2.5 PFLOP/s dense fp16 MFMA peak, and the CPU oracle
-timed on a bounded sample as a baseline.
+canonical packed format + X + Y over kernel time), the roofline of the
+dominant decode kernel against the 8 TB/s HBM peak (with the HBM bytes that
+rocprofv3 counted for it, when those counters were taken on the current
+kernel sources), the prefill TFLOP/s on the 70B-shaped MLP (28672x8192,
+M = 512 and 2048) against the 2.5 PFLOP/s dense fp16 MFMA peak, and the CPU
+oracle timed on a bounded sample as a baseline.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -39,8 +47,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
-                    help="run one leg only (used for profiling runs)")
+    ap.add_argument("--only", choices=["decode", "prefill", "copy"], default=None,
+                    help="run one leg only (profiling runs); 'copy' runs the plain device copy that "
+                         "calibrates the HBM byte counters")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the warm single-copy decode leg (keeps per-kernel profiles all-cold)")
     return ap.parse_args()
 
 
@@ -59,6 +70,66 @@ def time_events(fn, n):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b)   # ms
+
+
+def capture(torch, fn, n):
+    """A HIP graph holding fn(0) .. fn(n-1) (fn launches on the current stream)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):      # first calls outside capture (one-time kernel attributes)
+        for i in range(2):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(torch, fn, warmup, steps):
+    """Replay a graph of `warmup` calls untimed, then time one replay of a
+    graph of exactly `steps` calls between device synchronisations (ms)."""
+    if warmup > 0:
+        capture(torch, fn, warmup).replay()
+    g = capture(torch, fn, steps)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
+def source_digest():
+    """sha256 of the decode kernel sources (counters are only valid for these)."""
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "kernel_common.h", "mq_internal.h"):
+        with open(os.path.join(ROOT, "bit_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic(kernel_tag):
+    """HBM bytes per launch that rocprofv3 counted for `kernel_tag`, from the
+    committed counter summary, or None when the summary is missing or was
+    taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "decode_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != source_digest():
+        return None
+    v = vals.get(f"hbm_bytes_per_launch[{kernel_tag}]")
+    return float(v) if v else None
 
 
 def bench_decode(args, mq, synth, torch):
@@ -89,21 +160,19 @@ def bench_decode(args, mq, synth, torch):
         for M in Ms:
             mq.mq_linear_with(Xs[M], p, mq.KERNEL_GEMV, Ys[M])
 
-    time_events(step, args.warmup)
-    ms = time_events(step, args.steps)
+    ms = time_graphs(torch, step, args.warmup, args.steps)
     bytes_step = sum(decode_bytes(first, M) for M in Ms)
     per_m = {}
-    for M in Ms:
+    for M in Ms:   # each M runs its own kernel: average launch duration of each
         def one(i, M=M):
             mq.mq_linear_with(Xs[M], copies[i % ncopy], mq.KERNEL_GEMV, Ys[M])
-        time_events(one, args.warmup)
-        mms = time_events(one, args.steps) / args.steps
-        per_m[str(M)] = {"us": round(mms * 1e3, 3), "GBps": round(decode_bytes(first, M) / mms / 1e6, 1)}
+        mms = time_graphs(torch, one, args.warmup, args.steps) / args.steps
+        per_m[str(M)] = {"us": round(mms * 1e3, 3), "GBps": round(decode_bytes(first, M) / mms / 1e6, 1),
+                         "bytes": decode_bytes(first, M)}
     # warm, single copy (weights can stay in the Infinity Cache): context only
     def warm(i):
         mq.mq_linear_with(Xs[1], first, mq.KERNEL_GEMV, Ys[1])
-    time_events(warm, args.warmup)
-    warm_ms = time_events(warm, args.steps) / args.steps
+    warm_ms = float("nan") if args.no_warm else time_graphs(torch, warm, args.warmup, args.steps) / args.steps
     return {
         "layer": layer, "first": first, "ms_per_step": ms / args.steps, "bytes_step": bytes_step,
         "launches_per_step": len(Ms), "per_m": per_m, "pack_ms": pack_ms, "pack_wall_ms": pack_wall_ms,
@@ -181,25 +250,40 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
 
+    if args.only == "copy":
+        # a plain device copy of known size: reference for the HBM byte counters
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}), flush=True)
+        return
     if args.only == "prefill":
         print(json.dumps({"prefill": bench_prefill(args, mq, synth, torch)}), flush=True)
         return
     d = bench_decode(args, mq, synth, torch)
     value = d["bytes_step"] / (d["ms_per_step"] * 1e-3) / 1e9
-    per_launch_bytes = d["bytes_step"] / d["launches_per_step"]
-    per_launch_ms = d["ms_per_step"] / d["launches_per_step"]
-    achieved = per_launch_bytes / (per_launch_ms * 1e-3) / 1e9
+    # dominant kernel: the decode launch with the longest average duration
+    mdom = max(d["per_m"], key=lambda m: d["per_m"][m]["us"])
+    dom = d["per_m"][mdom]
+    achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
+    tag = ("k_gemv_x" if int(mdom) <= 4 else "k_gemv_r") + f"@M={mdom}"
+    traffic = counted_traffic(tag)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(d["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": "decode-11008x4096", "N": 11008, "K": 4096, "group": 128, "rho": 0.005,
-                   "nnz": d["nnz"], "M": [1, 4, 16], "kernel": "k_gemv", "packed_copies": d["copies"]},
+                   "nnz": d["nnz"], "M": [1, 4, 16], "packed_copies": d["copies"],
+                   "timing": "hip graph replay"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": tag,
+                     "algorithmic_bytes_per_launch": dom["bytes"], "avg_launch_us": dom["us"]},
         "decode_per_M": d["per_m"],
-        "decode_warm_single_copy_us_M1": round(d["warm_us_m1"], 3),
+        "decode_warm_single_copy_us_M1": None if args.no_warm else round(d["warm_us_m1"], 3),
         "pack": {"workload": "decode-11008x4096", "gpu_ms": round(d["pack_ms"], 3),
                  "wall_ms_first_call": round(d["pack_wall_ms"], 3)},
     }
