@@ -23,6 +23,10 @@ namespace mq {
 namespace {
 
 constexpr int kWaves = 8;
+// X rows in LDS are kXPad halfs (16 B) longer than K: with a row stride that
+// is a multiple of the 128-byte bank period, the 16 lanes of an MFMA B
+// fragment (16 token rows, same columns) would hit the same banks.
+constexpr int kXPad = 8;
 constexpr size_t kXldsMaxBytes = 64 * 1024;   // X is staged in LDS when M * K * 2 fits
 constexpr int kTpb = 4;   // code tiles per batch of one wave
 
@@ -64,7 +68,7 @@ __device__ __forceinline__ void load_scales(TileScales<NS>& S, const uint16_t* _
 template <int MB, int NS, bool XLDS, bool PAD>
 __device__ __forceinline__ void tile_mma(float4_t (&acc)[MB], const uint4 code, const TileScales<NS>& S,
                                          const uint16_t* __restrict__ X, const uint16_t* xs, const int (&mrow)[MB],
-                                         int K, int kt, int g, uint32_t vmask, uint32_t vmagic) {
+                                         int K, int ldx, int kt, int g, uint32_t vmask, uint32_t vmagic) {
   constexpr int SPG = 4 / NS;   // MFMA k-steps per scale group
   half8_t a[4];
   a[0] = widen_q(code.x, vmask, vmagic);
@@ -80,7 +84,7 @@ __device__ __forceinline__ void tile_mma(float4_t (&acc)[MB], const uint4 code, 
       if (PAD && seg >= K)   // padded 32-column segment (uniform branch)
         bx[s4] = as_half8(make_uint4(0u, 0u, 0u, 0u));
       else if (XLDS)
-        bx[s4] = *reinterpret_cast<const half8_t*>(xs + mrow[mb] * K + seg + 8 * g);
+        bx[s4] = *reinterpret_cast<const half8_t*>(xs + mrow[mb] * ldx + seg + 8 * g);
       else
         bx[s4] = as_half8(*reinterpret_cast<const uint4*>(X + (int64_t)mrow[mb] * K + seg + 8 * g));
     }
@@ -107,7 +111,7 @@ template <int MB, bool XLDS, bool MW>
 __device__ __forceinline__ void res_chunk(float4_t (&acc)[MB], const uint4 v0, const uint4 v1, uint32_t first,
                                           const uint32_t* __restrict__ rtp, int nwin,
                                           const uint16_t* __restrict__ X, const uint16_t* xs, const int (&mrow)[MB],
-                                          int K, int r, int g) {
+                                          int K, int ldx, int r, int g) {
   const uint32_t e[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
   int col[8];
 #pragma unroll
@@ -134,8 +138,8 @@ __device__ __forceinline__ void res_chunk(float4_t (&acc)[MB], const uint4 v0, c
     for (int u = 0; u < 8; u += 2) {
       uint32_t lo, hi;
       if (XLDS) {
-        lo = xs[mrow[mb] * K + col[u]];
-        hi = xs[mrow[mb] * K + col[u + 1]];
+        lo = xs[mrow[mb] * ldx + col[u]];
+        hi = xs[mrow[mb] * ldx + col[u + 1]];
       } else {
         lo = X[mrow[mb] * K + col[u]];
         hi = X[mrow[mb] * K + col[u + 1]];
@@ -190,8 +194,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
     const uint4* __restrict__ tiles, const uint16_t* __restrict__ scales, int sstride,
     const uint32_t* __restrict__ tile_ptr, const uint32_t* __restrict__ entries, const uint16_t* __restrict__ X,
     uint16_t* __restrict__ Y, int M, int N, int zero_off) {
-  constexpr int KS = 8, TPW = 4, K = 4096, Kt = 32, NS = 1 << GSH;
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][4096]
+  constexpr int KS = 8, TPW = 4, K = 4096, Kt = 32, NS = 1 << GSH, LDX = K + kXPad;
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][LDX]
   __shared__ float4_t red[KS][64];
   const int rb = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -264,10 +268,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
   // X slices into LDS, published with a wait on LDS traffic only
   uint16_t* xdst = xs + c0 + 8 * lane;
   *reinterpret_cast<uint4*>(xdst) = x0;
-  if constexpr (XR > 1) *reinterpret_cast<uint4*>(xdst + K) = x1;
+  if constexpr (XR > 1) *reinterpret_cast<uint4*>(xdst + LDX) = x1;
   if constexpr (XR > 2) {
-    *reinterpret_cast<uint4*>(xdst + 2 * K) = x2;
-    *reinterpret_cast<uint4*>(xdst + 3 * K) = x3;
+    *reinterpret_cast<uint4*>(xdst + 2 * LDX) = x2;
+    *reinterpret_cast<uint4*>(xdst + 3 * LDX) = x3;
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
         if constexpr (NS == 4) S.hi[i] = rowok[i] ? sraw[i][t].y : 0u;
       }
     }
-    tile_mma<1, NS, true, false>(acc, code[t], S, X, xs, mrow, K, kt0 + t, g, vmask, vmagic);
+    tile_mma<1, NS, true, false>(acc, code[t], S, X, xs, mrow, K, LDX, kt0 + t, g, vmask, vmagic);
   };
   tile(0);
   tile(1);
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
   for (int j = 0; j < 2; ++j) {
     const uint32_t c = (uint32_t)(wave + j * KS);
     if (c < nchunks)
-      res_chunk<1, true, false>(acc, ent[j][0], ent[j][1], E0 + kChunk * c, tile_ptr + tbase, 1, X, xs, mrow, K, r, g);
+      res_chunk<1, true, false>(acc, ent[j][0], ent[j][1], E0 + kChunk * c, tile_ptr + tbase, 1, X, xs, mrow, K, LDX, r, g);
     else
       asm volatile("" ::"v"(ent[j][0].x), "v"(ent[j][1].x));
   }
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
   tile(3);
   for (uint32_t c = (uint32_t)(wave + 2 * KS); c < nchunks; c += KS) {
     const uint4* e4 = reinterpret_cast<const uint4*>(entries + E0 + kChunk * c + 8 * g);
-    res_chunk<1, true, false>(acc, e4[0], e4[1], E0 + kChunk * c, tile_ptr + tbase, 1, X, xs, mrow, K, r, g);
+    res_chunk<1, true, false>(acc, e4[0], e4[1], E0 + kChunk * c, tile_ptr + tbase, 1, X, xs, mrow, K, LDX, r, g);
   }
 
   red[wave][lane] = acc[0];
@@ -332,8 +336,8 @@ __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles,
                                                int sstride, const uint32_t* __restrict__ tile_ptr,
                                                const uint32_t* __restrict__ entries, const uint16_t* __restrict__ X,
                                                uint16_t* __restrict__ Y, int M, int N, int Nb, int zero_off) {
-  constexpr int KS = 8, TPW = 4, K = 4096, Kt = 32, NS = 1 << GSH;
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][4096]
+  constexpr int KS = 8, TPW = 4, K = 4096, Kt = 32, NS = 1 << GSH, LDX = K + kXPad;
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][LDX]
   __shared__ float4_t red[R][KS][64];
   const int rb0 = blockIdx.x * R;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -356,7 +360,7 @@ __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles,
   for (int m = 0; m < XR; ++m) {
     if (m < M)
       __builtin_amdgcn_global_load_lds(X + m * K + c0 + 8 * lane,
-                                       (__attribute__((address_space(3))) void*)(xs + m * K + c0), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(xs + m * LDX + c0), 16, 0, 0);
   }
   __syncthreads();
 
@@ -420,16 +424,16 @@ __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles,
           if constexpr (NS == 4) S.hi[i] = ok ? sraw[j][i][t].y : 0u;
         }
       }
-      tile_mma<1, NS, true, false>(acc, code[j][t], S, X, xs, mrow, K, kt0 + t, g, vmask, vmagic);
+      tile_mma<1, NS, true, false>(acc, code[j][t], S, X, xs, mrow, K, LDX, kt0 + t, g, vmask, vmagic);
     }
     const uint32_t* rtp = tile_ptr + rb * Kt;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       res_chunk<1, true, false>(acc, ent[j][h][0], ent[j][h][1], E0[j] + kChunk * (wave + h * KS), rtp, 1, X, xs, mrow,
-                                K, r, g);
+                                K, LDX, r, g);
     for (uint32_t c = (uint32_t)(wave + 2 * KS); c < nch[j]; c += KS) {
       const uint4* e4 = reinterpret_cast<const uint4*>(entries + E0[j] + kChunk * c + 8 * g);
-      res_chunk<1, true, false>(acc, e4[0], e4[1], E0[j] + kChunk * c, rtp, 1, X, xs, mrow, K, r, g);
+      res_chunk<1, true, false>(acc, e4[0], e4[1], E0[j] + kChunk * c, rtp, 1, X, xs, mrow, K, LDX, r, g);
     }
     red[j][wave][lane] = acc[0];
   }
@@ -460,8 +464,9 @@ __global__ __launch_bounds__(64 * KS) __attribute__((amdgpu_waves_per_eu(KS == 8
                                                   const uint32_t* __restrict__ entries,
                                                   const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
                                                   int M, int N, int K, int Kt, int zero_off) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [M][K] when XR > 0
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [M][LDX] when XR > 0
   constexpr bool XLDS = XR > 0;
+  const int LDX = K + kXPad;
   __shared__ float4_t red[KS][MB][64];
   constexpr int NS = 1 << GSH;
   const int rb = blockIdx.x;
@@ -495,13 +500,13 @@ __global__ __launch_bounds__(64 * KS) __attribute__((amdgpu_waves_per_eu(KS == 8
     for (int t = 0; t < NT; ++t) load_scales<NS>(S[t], scales, srow, rowok, kt0 + t);
   }
 
-  if (XLDS) {   // whole X, straight from global memory into LDS, then published
-    const int n16 = (M * K) >> 3;
-    const uint4* src = reinterpret_cast<const uint4*>(X);
-    for (int ch = wave; ch * 64 < n16; ch += KS) {
-      if (ch * 64 + lane < n16)
-        __builtin_amdgcn_global_load_lds(src + ch * 64 + lane,
-                                         (__attribute__((address_space(3))) void*)(xs + ch * 512), 16, 0, 0);
+  if (XLDS) {   // whole X, straight from global memory into LDS (1 KiB per copy, by row), then published
+    const int nck = (K + 511) >> 9;
+    for (int idx = wave; idx < M * nck; idx += KS) {
+      const int m = idx / nck, c = (idx - m * nck) * 512;
+      if (c + 8 * lane < K)
+        __builtin_amdgcn_global_load_lds(X + (int64_t)m * K + c + 8 * lane,
+                                         (__attribute__((address_space(3))) void*)(xs + m * LDX + c), 16, 0, 0);
     }
     __syncthreads();
   }
@@ -545,24 +550,24 @@ __global__ __launch_bounds__(64 * KS) __attribute__((amdgpu_waves_per_eu(KS == 8
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[t].lo[i] = (srun[i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
       }
-      tile_mma<MB, NS, XLDS, false>(acc, code[t], S[t], X, xs, mrow, K, kt0 + t, g, vmask, vmagic);
+      tile_mma<MB, NS, XLDS, false>(acc, code[t], S[t], X, xs, mrow, K, LDX, kt0 + t, g, vmask, vmagic);
     }
   } else {
     for (int kt = kt0; kt < kt1; ++kt) {
       const uint4 c1 = tiles[(tbase + kt) * 64 + lane];
       TileScales<NS> s1;
       load_scales<NS>(s1, scales, srow, rowok, kt);
-      tile_mma<MB, NS, XLDS, true>(acc, c1, s1, X, xs, mrow, K, kt, g, vmask, vmagic);
+      tile_mma<MB, NS, XLDS, true>(acc, c1, s1, X, xs, mrow, K, LDX, kt, g, vmask, vmagic);
     }
   }
 
   // ---- residual: chunks wave, wave + KS, ... of the row block's entries
-  res_chunk<MB, XLDS, MW>(acc, ent[0][0], ent[0][1], E0 + kChunk * wave, tile_ptr + tbase, nwin, X, xs, mrow, K, r, g);
+  res_chunk<MB, XLDS, MW>(acc, ent[0][0], ent[0][1], E0 + kChunk * wave, tile_ptr + tbase, nwin, X, xs, mrow, K, LDX, r, g);
   res_chunk<MB, XLDS, MW>(acc, ent[1][0], ent[1][1], E0 + kChunk * (wave + KS), tile_ptr + tbase, nwin, X, xs, mrow, K,
-                          r, g);
+                          LDX, r, g);
   for (uint32_t c = (uint32_t)(wave + 2 * KS); c < nchunks; c += KS) {
     const uint4* e4 = reinterpret_cast<const uint4*>(entries + E0 + kChunk * c + 8 * g);
-    res_chunk<MB, XLDS, MW>(acc, e4[0], e4[1], E0 + kChunk * c, tile_ptr + tbase, nwin, X, xs, mrow, K, r, g);
+    res_chunk<MB, XLDS, MW>(acc, e4[0], e4[1], E0 + kChunk * c, tile_ptr + tbase, nwin, X, xs, mrow, K, LDX, r, g);
   }
 
   // ---- fixed-order sum of the KS partial tiles, fp16 output
@@ -597,7 +602,7 @@ hipError_t launch_x(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, h
   static bool done = false;
   const hipError_t e = allow_lds(&k_gemv_x<GSH, XR>, done);
   if (e != hipSuccess) return e;
-  k_gemv_x<GSH, XR><<<dim3((unsigned)p->Nb), dim3(512), (size_t)XR * 4096 * 2, s>>>(
+  k_gemv_x<GSH, XR><<<dim3((unsigned)p->Nb), dim3(512), (size_t)XR * (4096 + kXPad) * 2, s>>>(
       reinterpret_cast<const uint4*>(p->tiles), p->scales, (int)p->sstride, p->tile_ptr, p->entries, X, Y, M,
       (int)p->N, (int)p->stream_cap);
   return hipGetLastError();
@@ -616,7 +621,7 @@ hipError_t launch_r(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, h
     done = true;
   }
   const unsigned grid = (unsigned)((p->Nb + R - 1) / R);
-  k_gemv_r<GSH, XR, R><<<dim3(grid), dim3(512), (size_t)XR * 4096 * 2, s>>>(
+  k_gemv_r<GSH, XR, R><<<dim3(grid), dim3(512), (size_t)XR * (4096 + kXPad) * 2, s>>>(
       reinterpret_cast<const uint4*>(p->tiles), p->scales, (int)p->sstride, p->tile_ptr, p->entries, X, Y, M,
       (int)p->N, (int)p->Nb, (int)p->stream_cap);
   return hipGetLastError();
@@ -630,7 +635,7 @@ hipError_t launch_r_any(const mq_packed* p, const uint16_t* X, int M, uint16_t* 
   return launch_r<GSH, XR, 3>(p, X, M, Y, s);
 }
 
-// XL: X copied whole into LDS ([M][K], at most kXldsMax bytes)
+// XL: X copied whole into LDS ([M][K + kXPad], at most kXldsMax bytes)
 template <int KS, int MB, int GSH, int XL, bool MWV, int TPW>
 hipError_t launch(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
   if (XL) {
@@ -638,7 +643,8 @@ hipError_t launch(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hip
     const hipError_t e = allow_lds(&k_gemv<KS, MB, GSH, XL, MWV, TPW>, done);
     if (e != hipSuccess) return e;
   }
-  k_gemv<KS, MB, GSH, XL, MWV, TPW><<<dim3((unsigned)p->Nb), dim3(64 * KS), XL ? (size_t)M * p->K * 2 : 0, s>>>(
+  k_gemv<KS, MB, GSH, XL, MWV, TPW><<<dim3((unsigned)p->Nb), dim3(64 * KS), XL ? (size_t)M * (p->K + kXPad) * 2 : 0,
+                                      s>>>(
       reinterpret_cast<const uint4*>(p->tiles), p->scales, (int)p->sstride, p->tile_ptr, p->entries, X, Y, M,
       (int)p->N, (int)p->K, (int)p->Kt, (int)p->stream_cap);
   return hipGetLastError();
@@ -677,7 +683,7 @@ hipError_t run(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStr
       if (M <= 8) return launch_r_any<GSH, 8>(p, X, M, Y, s);
       return launch_r_any<GSH, 16>(p, X, M, Y, s);
     }
-    if ((size_t)M * p->K * 2 <= kXldsMax) return run_x<MB, GSH, 1>(p, X, M, Y, s);
+    if ((size_t)M * (p->K + kXPad) * 2 <= kXldsMax) return run_x<MB, GSH, 1>(p, X, M, Y, s);
   }
   return run_x<MB, GSH, 0>(p, X, M, Y, s);
 }
