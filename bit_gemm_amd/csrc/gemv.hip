@@ -68,13 +68,14 @@ __device__ __forceinline__ void load_scales(TileScales<NS>& S, const uint16_t* _
 template <int MB, int NS, bool XLDS, bool PAD>
 __device__ __forceinline__ void tile_mma(float4_t (&acc)[MB], const uint4 code, const TileScales<NS>& S,
                                          const uint16_t* __restrict__ X, const uint16_t* xs, const int (&mrow)[MB],
-                                         int K, int ldx, int kt, int g, uint32_t vmask, uint32_t vmagic) {
+                                         int K, int ldx, int kt, int g, uint32_t vmask, uint32_t vmask4,
+                                         uint32_t vmagic) {
   constexpr int SPG = 4 / NS;   // MFMA k-steps per scale group
   half8_t a[4];
-  a[0] = widen_q(code.x, vmask, vmagic);
-  a[1] = widen_q(code.y, vmask, vmagic);
-  a[2] = widen_q(code.z, vmask, vmagic);
-  a[3] = widen_q(code.w, vmask, vmagic);
+  a[0] = widen_q(code.x, vmask, vmask4, vmagic);
+  a[1] = widen_q(code.y, vmask, vmask4, vmagic);
+  a[2] = widen_q(code.z, vmask, vmask4, vmagic);
+  a[3] = widen_q(code.w, vmask, vmask4, vmagic);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     half8_t bx[4];
@@ -275,8 +276,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  uint32_t vmask = 0x000F000Fu, vmagic = 0x64006400u;
-  asm volatile("" : "+v"(vmask), "+v"(vmagic));   // keep both constants in VGPRs for v_and_or_b32
+  uint32_t vmask = 0x000F000Fu, vmask4 = 0x00F000F0u, vmagic = 0x64006400u;
+  asm volatile("" : "+v"(vmask), "+v"(vmask4), "+v"(vmagic));   // keep the constants in VGPRs for v_and_or_b32
   float4_t acc[1] = {float4_t{0.f, 0.f, 0.f, 0.f}};
   auto tile = [&](int t) __attribute__((always_inline)) {
     TileScales<NS> S;
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
         if constexpr (NS == 4) S.hi[i] = rowok[i] ? sraw[i][t].y : 0u;
       }
     }
-    tile_mma<1, NS, true, false>(acc, code[t], S, X, xs, mrow, K, LDX, kt0 + t, g, vmask, vmagic);
+    tile_mma<1, NS, true, false>(acc, code[t], S, X, xs, mrow, K, LDX, kt0 + t, g, vmask, vmask4, vmagic);
   };
   tile(0);
   tile(1);
@@ -324,13 +325,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
 
 // Decode kernel for K = 4096 and 5..16 tokens. X ([XR][4096] fp16, up to
 // 128 KiB) fills most of the LDS, so one workgroup per CU holds it and works
-// through R consecutive row blocks with it: X is copied in once (each wave
-// its 512-column slice, straight from global memory into LDS) and
-// published, then every wave requests the scales, its 4 code tiles and its
-// first residual chunk of all R row blocks before computing anything; the
-// row blocks are then computed in order (residual chunks gather their X
-// columns from LDS) and the 8 partials of each are summed in LDS in a fixed
-// order.
+// through R consecutive row blocks with it. X is copied in first (each wave
+// its 512-column slice, straight from global memory into LDS) and published;
+// then every wave requests the scales, its 4 code tiles and its first two
+// residual chunks of all R row blocks before computing anything. The row
+// blocks are computed in order (residual chunks gather their X columns from
+// LDS) and the 8 partials of each are summed in LDS in a fixed order.
 template <int GSH, int XR, int R>
 __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles, const uint16_t* __restrict__ scales,
                                                int sstride, const uint32_t* __restrict__ tile_ptr,
@@ -355,7 +355,10 @@ __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles,
     nch[j] = (tile_ptr[tbase + Kt] - E0[j]) / (uint32_t)kChunk;
   }
 
-  // X slice of this wave, one 1 KiB copy per token row (rows >= M are never read)
+  // X slice of this wave, one 1 KiB copy per token row straight from global
+  // memory into LDS (rows >= M are never read), published before any code
+  // tile is requested: X requests issued alongside the code stream queue
+  // behind it in the memory system and would land only at its end.
 #pragma unroll
   for (int m = 0; m < XR; ++m) {
     if (m < M)
@@ -404,8 +407,9 @@ __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles,
     __builtin_amdgcn_sched_barrier(0);   // keep row block j's requests ahead of row block j + 1's
   }
 
-  uint32_t vmask = 0x000F000Fu, vmagic = 0x64006400u;
-  asm volatile("" : "+v"(vmask), "+v"(vmagic));   // keep both constants in VGPRs for v_and_or_b32
+
+  uint32_t vmask = 0x000F000Fu, vmask4 = 0x00F000F0u, vmagic = 0x64006400u;
+  asm volatile("" : "+v"(vmask), "+v"(vmask4), "+v"(vmagic));   // keep the constants in VGPRs for v_and_or_b32
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const int rb = min(rb0 + j, Nb - 1);
@@ -424,13 +428,17 @@ __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles,
           if constexpr (NS == 4) S.hi[i] = ok ? sraw[j][i][t].y : 0u;
         }
       }
-      tile_mma<1, NS, true, false>(acc, code[j][t], S, X, xs, mrow, K, LDX, kt0 + t, g, vmask, vmagic);
+      tile_mma<1, NS, true, false>(acc, code[j][t], S, X, xs, mrow, K, LDX, kt0 + t, g, vmask, vmask4, vmagic);
     }
     const uint32_t* rtp = tile_ptr + rb * Kt;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      res_chunk<1, true, false>(acc, ent[j][h][0], ent[j][h][1], E0[j] + kChunk * (wave + h * KS), rtp, 1, X, xs, mrow,
-                                K, LDX, r, g);
+    for (int h = 0; h < 2; ++h) {   // a chunk past the row block is skipped; the empty use keeps its load in place
+      if ((uint32_t)(wave + h * KS) < nch[j])
+        res_chunk<1, true, false>(acc, ent[j][h][0], ent[j][h][1], E0[j] + kChunk * (wave + h * KS), rtp, 1, X, xs,
+                                  mrow, K, LDX, r, g);
+      else
+        asm volatile("" ::"v"(ent[j][h][0].x), "v"(ent[j][h][1].x));
+    }
     for (uint32_t c = (uint32_t)(wave + 2 * KS); c < nch[j]; c += KS) {
       const uint4* e4 = reinterpret_cast<const uint4*>(entries + E0[j] + kChunk * c + 8 * g);
       res_chunk<1, true, false>(acc, e4[0], e4[1], E0[j] + kChunk * c, rtp, 1, X, xs, mrow, K, LDX, r, g);
@@ -537,8 +545,8 @@ __global__ __launch_bounds__(64 * KS) __attribute__((amdgpu_waves_per_eu(KS == 8
     ent[j][1] = e4[1];
   }
 
-  uint32_t vmask = 0x000F000Fu, vmagic = 0x64006400u;
-  asm volatile("" : "+v"(vmask), "+v"(vmagic));   // keep both constants in VGPRs for v_and_or_b32
+  uint32_t vmask = 0x000F000Fu, vmask4 = 0x00F000F0u, vmagic = 0x64006400u;
+  asm volatile("" : "+v"(vmask), "+v"(vmask4), "+v"(vmagic));   // keep the constants in VGPRs for v_and_or_b32
 
   float4_t acc[MB];
 #pragma unroll
@@ -550,14 +558,14 @@ __global__ __launch_bounds__(64 * KS) __attribute__((amdgpu_waves_per_eu(KS == 8
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[t].lo[i] = (srun[i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
       }
-      tile_mma<MB, NS, XLDS, false>(acc, code[t], S[t], X, xs, mrow, K, LDX, kt0 + t, g, vmask, vmagic);
+      tile_mma<MB, NS, XLDS, false>(acc, code[t], S[t], X, xs, mrow, K, LDX, kt0 + t, g, vmask, vmask4, vmagic);
     }
   } else {
     for (int kt = kt0; kt < kt1; ++kt) {
       const uint4 c1 = tiles[(tbase + kt) * 64 + lane];
       TileScales<NS> s1;
       load_scales<NS>(s1, scales, srow, rowok, kt);
-      tile_mma<MB, NS, XLDS, true>(acc, c1, s1, X, xs, mrow, K, LDX, kt, g, vmask, vmagic);
+      tile_mma<MB, NS, XLDS, true>(acc, c1, s1, X, xs, mrow, K, LDX, kt, g, vmask, vmask4, vmagic);
     }
   }
 
@@ -628,11 +636,14 @@ hipError_t launch_r(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, h
 }
 
 // row blocks per workgroup so that one wave of workgroups covers the layer
+// (G = 32 keeps 4 scales per tile and row: at most 2 row blocks fit the registers)
 template <int GSH, int XR>
 hipError_t launch_r_any(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
   if (p->Nb <= 256) return launch_r<GSH, XR, 1>(p, X, M, Y, s);
-  if (p->Nb <= 512) return launch_r<GSH, XR, 2>(p, X, M, Y, s);
-  return launch_r<GSH, XR, 3>(p, X, M, Y, s);
+  if constexpr (GSH < 2) {
+    if (p->Nb > 512) return launch_r<GSH, XR, 3>(p, X, M, Y, s);
+  }
+  return launch_r<GSH, XR, 2>(p, X, M, Y, s);
 }
 
 // XL: X copied whole into LDS ([M][K + kXPad], at most kXldsMax bytes)
