@@ -21,6 +21,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmosaicq.so")
 HOSTCHECK = os.path.join(HERE, "libmq_hostcheck.so")
 SOURCES = ["api.cpp", "pack.hip", "gemv.hip", "gemm.hip"]
+# per-source code generation options (none at present)
+EXTRA: dict = {}
 ARCH = os.environ.get("MQ_OFFLOAD_ARCH", "gfx950")
 
 
@@ -54,7 +56,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([cc, "-x", "hip", *_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, "-x", "hip", *_flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
         list(ex.map(_run, cmds))
     tmp = LIB + ".tmp"
