@@ -85,15 +85,23 @@ __device__ __forceinline__ uint32_t dword_scale(uint2 sraw, int t) {
 }
 
 // X stage [BM tokens][BK columns]: 8 x 16 B per thread, 8 consecutive chunks of a
-// row per 8 lanes; clamped addresses, zeros past M or K (branch-free).
-__device__ __forceinline__ void load_x(uint4 (&x)[8], const uint16_t* __restrict__ X, int M, int K, int m0, int col0,
-                                       int tid) {
+// row per 8 lanes; thread tid reads rows tid / 8 + 32 i, chunk tid % 8, so its
+// 8 row pointers are fixed (xrow, computed once; rows past M read row M - 1,
+// which only feeds outputs that are never stored). Every load is
+// unconditional (a guarded load would become a branch); when K is not a
+// multiple of 128 the chunks past K are zeroed with a mask kept opaque to the
+// compiler (a select would be turned back into a branch).
+template <bool KTAIL>
+__device__ __forceinline__ void load_x(uint4 (&x)[8], const uint16_t* const (&xrow)[8], int K, int col0, int tid) {
+  // without a K tail (K % 128 == 0) only the look-ahead past the last stage
+  // leaves [0, K): it re-reads the last stage (never consumed)
+  const int col = (KTAIL ? col0 : min(col0, K - BK)) + 8 * (tid & 7);
+  uint32_t keep = col < K ? ~0u : 0u;
+  if (KTAIL) asm volatile("" : "+v"(keep));
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int idx = tid + kThreads * i;
-    const int row = m0 + (idx >> 3), col = col0 + 8 * (idx & 7);
-    const uint4 v = *reinterpret_cast<const uint4*>(X + (int64_t)min(row, M - 1) * K + min(col, K - 8));
-    x[i] = (row < M && col < K) ? v : make_uint4(0u, 0u, 0u, 0u);
+    const uint4 v = *reinterpret_cast<const uint4*>(xrow[i] + (KTAIL ? min(col, K - 8) : col));
+    x[i] = KTAIL ? make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep) : v;
   }
 }
 
@@ -113,7 +121,7 @@ __device__ __forceinline__ void store_x(const uint4 (&x)[8], _Float16* Xs, int t
 // without an entry write to a dummy word (no branches).
 template <int GSH>
 __device__ __forceinline__ void write_w(const TileRegs& T, _Float16* Ws, uint32_t* ssc, _Float16* dummy, int lrb0,
-                                        int h, int lane) {
+                                        int h, int lane, uint32_t vmask, uint32_t vmask4, uint32_t vmagic) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int j = 0; j < kRbPerWave; ++j) {
@@ -121,8 +129,8 @@ __device__ __forceinline__ void write_w(const TileRegs& T, _Float16* Ws, uint32_
     const uint32_t d0 = h ? T.code[j].z : T.code[j].x;
     const uint32_t d1 = h ? T.code[j].w : T.code[j].y;
     const uint32_t s0 = dword_scale<GSH>(T.sraw[j], 2 * h), s1 = dword_scale<GSH>(T.sraw[j], 2 * h + 1);
-    *reinterpret_cast<half8_t*>(dst) = dequant_dword(d0, splat_half(s0));
-    *reinterpret_cast<half8_t*>(dst + 32) = dequant_dword(d1, splat_half(s1));
+    *reinterpret_cast<half8_t*>(dst) = dequant_dword(d0, splat_half(s0), vmask, vmask4, vmagic);
+    *reinterpret_cast<half8_t*>(dst + 32) = dequant_dword(d1, splat_half(s1), vmask, vmask4, vmagic);
     ssc[(lrb0 + j) * kRowsPerBlock + r] = s0 | (s1 << 16);   // same value from the 4 lanes of a row
   }
 #pragma unroll
@@ -134,7 +142,8 @@ __device__ __forceinline__ void write_w(const TileRegs& T, _Float16* Ws, uint32_
     const uint32_t sb = ssc[row];
     const float s = h_to_f(((c & 63) < 32 ? sb : sb >> 16) & 0xFFFFu);
     _Float16* w = ok ? Ws + row * LDW + (c & 63) : dummy;
-    const float q = (s != 0.f) ? rintf((float)*w * __builtin_amdgcn_rcpf(s)) : 0.f;
+    // s = 0 means fp16(s q) = 0, and then q = rint(0 * 1e30) = 0 as well: no select
+    const float q = rintf((float)*w * __builtin_amdgcn_rcpf(fmaxf(s, 1e-30f)));
     *w = (_Float16)fmaf(s, q, h_to_f(ent_delta(v)));
   }
 }
@@ -197,7 +206,7 @@ __device__ __forceinline__ int xcd_tile(int b, int T) {
   return x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
 }
 
-template <int GSH>
+template <int GSH, bool KTAIL>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ tiles,
                                                       const uint16_t* __restrict__ scales, int64_t sstride,
                                                       const uint32_t* __restrict__ tile_ptr,
@@ -217,6 +226,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ 
   const int wn = wave & 1, wm = wave >> 1;   // 2 x 2 waves of 128 x 128
   const int lrb0 = kRbPerWave * wave;        // local row blocks widened by this wave
   const int rbw = rb0 + lrb0;
+  const uint16_t* xrow[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xrow[i] = X + (int64_t)min(m0 + (tid >> 3) + 32 * i, M - 1) * K;
+  uint32_t vmask = 0x000F000Fu, vmask4 = 0x00F000F0u, vmagic = 0x64006400u;
+  asm volatile("" : "+v"(vmask), "+v"(vmask4), "+v"(vmagic));   // keep the constants in VGPRs for v_and_or_b32
 
   float16_t acc[4][4];
 #pragma unroll
@@ -229,29 +243,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ 
   TileRegs t0, t1;
   uint4 xr[8];
   load_tile<GSH>(t0, tiles, scales, sstride, tile_ptr, entries, Kt, Nb, rbw, 0, lane);
-  load_x(xr, X, M, K, m0, 0, tid);
-  write_w<GSH>(t0, buf0, ssc, dummy, lrb0, 0, lane);
+  load_x<KTAIL>(xr, xrow, K, 0, tid);
+  write_w<GSH>(t0, buf0, ssc, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
   if (t0.cnt[0] > 64 || t0.cnt[1] > 64 || t0.cnt[2] > 64 || t0.cnt[3] > 64)
     patch_rest<GSH>(t0, buf0, ssc, lrb0, 0, lane, entries);
   store_x(xr, buf0 + BN * LDW, tid);
-  load_x(xr, X, M, K, m0, BK, tid);
+  load_x<KTAIL>(xr, xrow, K, BK, tid);
   load_tile<GSH>(t1, tiles, scales, sstride, tile_ptr, entries, Kt, Nb, rbw, 1, lane);
   __syncthreads();
 
   for (int kt = 0; kt < Kt; ++kt) {
     // stage 2 kt (buffer 0) runs; stage 2 kt + 1 (half 1 of tile kt) is prepared in buffer 1
     mfma_stage(acc, buf0, buf0 + BN * LDW, wn, wm, lane);
-    write_w<GSH>(t0, buf1, ssc + BN, dummy, lrb0, 1, lane);
+    write_w<GSH>(t0, buf1, ssc + BN, dummy, lrb0, 1, lane, vmask, vmask4, vmagic);
     store_x(xr, buf1 + BN * LDW, tid);
-    load_x(xr, X, M, K, m0, (2 * kt + 2) * BK, tid);
+    load_x<KTAIL>(xr, xrow, K, (2 * kt + 2) * BK, tid);
     if (t0.cnt[0] > 64 || t0.cnt[1] > 64 || t0.cnt[2] > 64 || t0.cnt[3] > 64)
       patch_rest<GSH>(t0, buf1, ssc + BN, lrb0, 1, lane, entries);
     __syncthreads();
     // stage 2 kt + 1 (buffer 1) runs; stage 2 kt + 2 (half 0 of tile kt + 1) is prepared in buffer 0
     mfma_stage(acc, buf1, buf1 + BN * LDW, wn, wm, lane);
-    write_w<GSH>(t1, buf0, ssc, dummy, lrb0, 0, lane);
+    write_w<GSH>(t1, buf0, ssc, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
     store_x(xr, buf0 + BN * LDW, tid);
-    load_x(xr, X, M, K, m0, (2 * kt + 3) * BK, tid);
+    load_x<KTAIL>(xr, xrow, K, (2 * kt + 3) * BK, tid);
     if (t1.cnt[0] > 64 || t1.cnt[1] > 64 || t1.cnt[2] > 64 || t1.cnt[3] > 64)
       patch_rest<GSH>(t1, buf0, ssc, lrb0, 0, lane, entries);
     t0 = t1;
@@ -280,11 +294,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ 
   }
 }
 
-template <int GSH>
+template <int GSH, bool KTAIL>
 hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<GSH>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<GSH, KTAIL>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -292,7 +306,7 @@ hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y,
   const int NT = (int)((p->Nb + (BN / kRowsPerBlock) - 1) / (BN / kRowsPerBlock));
   const int MT = (int)((M + BM - 1) / BM);
   const int T = NT * MT;
-  k_gemm<GSH><<<dim3((unsigned)T), dim3(kThreads), kLdsBytes, s>>>(
+  k_gemm<GSH, KTAIL><<<dim3((unsigned)T), dim3(kThreads), kLdsBytes, s>>>(
       reinterpret_cast<const uint4*>(p->tiles), p->scales, p->sstride, p->tile_ptr, p->entries, X, Y, (int)M,
       (int)p->N, (int)p->K, (int)p->Kt, (int)p->Nb, NT, T);
   return hipGetLastError();
@@ -300,10 +314,15 @@ hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y,
 
 }  // namespace
 
+template <bool KTAIL>
+hipError_t launch_k(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
+  if (p->G == 128) return launch<0, KTAIL>(p, X, M, Y, s);
+  if (p->G == 64) return launch<1, KTAIL>(p, X, M, Y, s);
+  return launch<2, KTAIL>(p, X, M, Y, s);
+}
+
 hipError_t launch_gemm(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
-  if (p->G == 128) return launch<0>(p, X, M, Y, s);
-  if (p->G == 64) return launch<1>(p, X, M, Y, s);
-  return launch<2>(p, X, M, Y, s);
+  return (p->K % kTileCols) != 0 ? launch_k<true>(p, X, M, Y, s) : launch_k<false>(p, X, M, Y, s);
 }
 
 }  // namespace mq

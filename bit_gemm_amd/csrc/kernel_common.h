@@ -10,30 +10,6 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// One dword of the tile layout holds 8 codes u = q + 8 of 8 consecutive
-// columns, column c in nibble (c / 2) + 4 (c % 2). OR-ing a nibble into the
-// mantissa of fp16 1024.0 (0x6400) gives exactly 1024 + u, so (1024 + u) - 1032
-// = q exactly and one fp16 multiply by the group scale gives fp16(s q),
-// correctly rounded.
-__device__ __forceinline__ half8_t dequant_dword(uint32_t w, half2_t s2) {
-  constexpr uint32_t kMagic = 0x64006400u;
-  const half2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const uint32_t p0 = (w & 0x000F000Fu) | kMagic;
-  const uint32_t p1 = ((w >> 4) & 0x000F000Fu) | kMagic;
-  const uint32_t p2 = ((w >> 8) & 0x000F000Fu) | kMagic;
-  const uint32_t p3 = ((w >> 12) & 0x000F000Fu) | kMagic;
-  const half2_t h0 = (__builtin_bit_cast(half2_t, p0) - bias) * s2;
-  const half2_t h1 = (__builtin_bit_cast(half2_t, p1) - bias) * s2;
-  const half2_t h2 = (__builtin_bit_cast(half2_t, p2) - bias) * s2;
-  const half2_t h3 = (__builtin_bit_cast(half2_t, p3) - bias) * s2;
-  u32x4_t v;
-  v.x = __builtin_bit_cast(uint32_t, h0);
-  v.y = __builtin_bit_cast(uint32_t, h1);
-  v.z = __builtin_bit_cast(uint32_t, h2);
-  v.w = __builtin_bit_cast(uint32_t, h3);
-  return __builtin_bit_cast(half8_t, v);
-}
-
 // D = (a & m) | o in one VALU op; m and o must already sit in VGPRs (a VOP3
 // instruction on this target takes neither two SGPRs nor a literal).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
@@ -61,6 +37,22 @@ __device__ __forceinline__ half8_t widen_q(uint32_t w, uint32_t vmask, uint32_t 
   v.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, and_or(w8, vmask, vmagic)) - bias);
   v.w = __builtin_bit_cast(uint32_t,
                            __builtin_elementwise_fma(__builtin_bit_cast(half2_t, and_or(w8, vmask4, vmagic)), k16, k72));
+  return __builtin_bit_cast(half8_t, v);
+}
+
+// The 8 codes of one dword as fp16(s q): exact q as in widen_q, then one
+// packed multiply by the group scale (a single rounding of s q).
+__device__ __forceinline__ half8_t dequant_dword(uint32_t w, half2_t s2, uint32_t vmask, uint32_t vmask4,
+                                                 uint32_t vmagic) {
+  // (vector elements are copied to scalars first: a bit_cast of an element
+  // lvalue such as v.y reads element 0 with this compiler)
+  const u32x4_t q = __builtin_bit_cast(u32x4_t, widen_q(w, vmask, vmask4, vmagic));
+  const uint32_t q0 = q.x, q1 = q.y, q2 = q.z, q3 = q.w;
+  u32x4_t v;
+  v.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, q0) * s2);
+  v.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, q1) * s2);
+  v.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, q2) * s2);
+  v.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, q3) * s2);
   return __builtin_bit_cast(half8_t, v);
 }
 
