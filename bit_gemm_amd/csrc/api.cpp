@@ -34,7 +34,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 void release(mq_packed* p) {
-  void* bufs[] = {p->tiles, p->scales, p->row_ptr, p->col, p->rcodes, p->rscale, p->tile_ptr, p->entries};
+  void* bufs[] = {p->tiles, p->scales, p->row_ptr, p->col, p->rcodes, p->rscale, p->tile_ptr, p->entries, p->wpatch};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   p->magic = 0;
@@ -106,7 +106,7 @@ MQ_API mq_status mq_pack(const void* W_dev_fp16, int64_t N, int64_t K, int32_t g
     size_t n;
   } allocs[] = {{(void**)&p->tiles, sz_tiles},   {(void**)&p->scales, sz_scales}, {(void**)&p->row_ptr, sz_rowptr},
                 {(void**)&p->col, sz_col},       {(void**)&p->rcodes, sz_rcodes}, {(void**)&p->rscale, sz_rscale},
-                {(void**)&p->tile_ptr, sz_tptr}, {(void**)&p->entries, sz_ent}};
+                {(void**)&p->tile_ptr, sz_tptr}, {(void**)&p->entries, sz_ent},  {(void**)&p->wpatch, sz_ent}};
   size_t total = 0;
   for (auto& a : allocs) {
     e = hipMalloc(a.dst, a.n);

@@ -31,77 +31,91 @@ constexpr int BM = 256;               // tokens per workgroup
 constexpr int BK = 64;                // K columns per LDS stage
 constexpr int LDW = BK + 8;           // LDS row (halves): 144 B, so 8 consecutive rows hit distinct banks
 constexpr int kThreads = 256;
+constexpr int kBufferFlags = 0x00020000;   // buffer descriptor word 3: 32-bit data format, raw (unswizzled) addressing
 constexpr int kRbPerWave = 4;         // row blocks widened and patched by each wave
 constexpr size_t kStageHalves = (size_t)(BN + BM) * LDW;
-constexpr size_t kScaleOff = 2 * kStageHalves * sizeof(_Float16);             // [2][BN] u32 stage scales
-constexpr size_t kDummyOff = kScaleOff + 2 * BN * sizeof(uint32_t);            // patch target of idle lanes
-constexpr size_t kLdsBytes = kDummyOff + 16;
+constexpr size_t kDummyOff = 2 * kStageHalves * sizeof(_Float16);   // [64] halves: patch targets of idle lanes
+constexpr size_t kLdsBytes = kDummyOff + 64 * sizeof(_Float16);
 
-// Registers holding one code tile (two stages) of the wave's 4 row blocks.
-struct TileRegs {
-  uint4 code[kRbPerWave];
-  uint2 sraw[kRbPerWave];        // fp16 scales of the lane's row: 1, 2 or 4 groups of the tile
-  uint32_t ent[kRbPerWave];      // residual entry p0 + lane of the tile's segment (0 = none)
+// Residual segment bounds of one code tile for the wave's 4 row blocks
+// (wave-uniform, so they live in scalar registers). They are fetched a full
+// iteration before the entry loads that use them as addresses.
+struct TilePtrs {
   uint32_t p0[kRbPerWave], cnt[kRbPerWave];
 };
 
-// Branch-free: a row block past the layer or a tile past K reads clamped
-// indices and yields codes of q = 0, scale 0 and no entries. Entry loads stay
-// in bounds because 1024 zero entries follow the stream.
-template <int GSH>
-__device__ __forceinline__ void load_tile(TileRegs& T, const uint4* __restrict__ tiles,
-                                          const uint16_t* __restrict__ scales, int64_t sstride,
-                                          const uint32_t* __restrict__ tile_ptr,
-                                          const uint32_t* __restrict__ entries, int Kt, int Nb, int rbw, int kt,
-                                          int lane) {
-  const int r = lane & 15;
+__device__ __forceinline__ void load_ptrs(TilePtrs& P, const uint32_t* __restrict__ tile_ptr, int Kt, int Nb, int rbw,
+                                          int kt) {
 #pragma unroll
   for (int j = 0; j < kRbPerWave; ++j) {
     const bool ok = rbw + j < Nb && kt < Kt;
-    const int rb = min(rbw + j, Nb - 1), ktc = min(kt, Kt - 1);
-    const int64_t t = (int64_t)rb * Kt + ktc;
-    const uint4 c = tiles[t * 64 + lane];
-    const uint16_t* sp = scales + (int64_t)(rb * kRowsPerBlock + r) * sstride + (ktc << GSH);
-    uint2 sr;
-    if constexpr (GSH == 0) sr = make_uint2(*sp, 0u);
-    else if constexpr (GSH == 1) sr = make_uint2(*reinterpret_cast<const uint32_t*>(sp), 0u);
-    else sr = *reinterpret_cast<const uint2*>(sp);
+    const int64_t t = (int64_t)min(rbw + j, Nb - 1) * Kt + min(kt, Kt - 1);
     const uint32_t p0 = tile_ptr[t], p1 = tile_ptr[t + 1];
-    const uint32_t e = entries[p0 + lane];
-    T.code[j] = ok ? c : make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-    T.sraw[j] = ok ? sr : make_uint2(0u, 0u);
-    T.p0[j] = p0;
-    T.cnt[j] = ok ? p1 - p0 : 0u;
-    T.ent[j] = (uint32_t)lane < T.cnt[j] ? e : 0u;
+    P.p0[j] = p0;
+    P.cnt[j] = ok ? p1 - p0 : 0u;
   }
 }
 
-// fp16 bits of the scale of dword t (0..3) of the tile.
+// Registers holding one half (64 columns, one LDS stage) of a code tile for
+// the wave's 4 row blocks. Each half set is refilled in place right after
+// its last use, two stages ahead of the next one, so the loop never copies
+// registers that are still being loaded (a copy would wait for the load).
+// Nothing is selected at load time either: row blocks past the layer and
+// tiles past K are masked where the values are used, through `live` (scale
+// forced to 0) and P.cnt (no entries).
+struct HalfRegs {
+  uint2 code[kRbPerWave];        // dwords 2h, 2h + 1 of the lane's 16-byte slice of the tile
+  uint32_t sraw[kRbPerWave];     // fp16 scale bits of the lane's row: one, or two (G = 32: dword 0 low, 1 high)
+  uint32_t ent[kRbPerWave];      // patched-weight entry p0 + lane of the tile's segment (valid when lane < cnt)
+  TilePtrs P;
+  uint32_t live;                 // bit j: row block j exists and the tile is inside K
+};
+
+// Branch- and wait-free: clamped indices keep every load in bounds (1024 zero
+// entries follow the stream, so p0 + lane is always readable).
 template <int GSH>
-__device__ __forceinline__ uint32_t dword_scale(uint2 sraw, int t) {
-  if constexpr (GSH == 0) return sraw.x & 0xFFFFu;
-  else if constexpr (GSH == 1) return (sraw.x >> (16 * (t >> 1))) & 0xFFFFu;
-  else return ((t < 2 ? sraw.x : sraw.y) >> (16 * (t & 1))) & 0xFFFFu;
+__device__ __forceinline__ void load_half(HalfRegs& H, const TilePtrs& P, const uint4* __restrict__ tiles,
+                                          const uint16_t* __restrict__ scales, int64_t sstride,
+                                          const uint32_t* __restrict__ wpatch, int Kt, int Nb, int rbw, int kt, int h,
+                                          int lane) {
+  const int r = lane & 15;
+  uint32_t live = 0;
+#pragma unroll
+  for (int j = 0; j < kRbPerWave; ++j) {
+    live |= (rbw + j < Nb && kt < Kt) ? 1u << j : 0u;
+    const int rb = min(rbw + j, Nb - 1), ktc = min(kt, Kt - 1);
+    const int64_t t = (int64_t)rb * Kt + ktc;
+    H.code[j] = reinterpret_cast<const uint2*>(tiles)[(t * 64 + lane) * 2 + h];
+    const uint16_t* srow = scales + (int64_t)(rb * kRowsPerBlock + r) * sstride;
+    if constexpr (GSH == 0) H.sraw[j] = srow[ktc];
+    else if constexpr (GSH == 1) H.sraw[j] = srow[2 * ktc + h];
+    else H.sraw[j] = *reinterpret_cast<const uint32_t*>(srow + 4 * ktc + 2 * h);
+    H.ent[j] = wpatch[P.p0[j] + lane];
+  }
+  H.P = P;
+  H.live = live;
 }
 
 // X stage [BM tokens][BK columns]: 8 x 16 B per thread, 8 consecutive chunks of a
-// row per 8 lanes; thread tid reads rows tid / 8 + 32 i, chunk tid % 8, so its
-// 8 row pointers are fixed (xrow, computed once; rows past M read row M - 1,
-// which only feeds outputs that are never stored). Every load is
-// unconditional (a guarded load would become a branch); when K is not a
-// multiple of 128 the chunks past K are zeroed with a mask kept opaque to the
-// compiler (a select would be turned back into a branch).
+// row per 8 lanes; thread tid reads rows tid / 8 + 32 i, chunk tid % 8. The
+// loads go through a buffer resource over the workgroup's rows of X (base row
+// m0, `nrec` = valid rows x K x 2 bytes): rows past M read as zero by the
+// hardware's range check, so one offset register serves all 8 rows and no
+// load needs a guard (a guarded load would become a branch). Columns past K
+// (a K tail, or the look-ahead past the last stage) read the next row or
+// zero; with a K tail they are masked to zero with a mask kept opaque to the
+// compiler (a select would be turned back into a branch), otherwise they
+// land in a stage that is never consumed.
 template <bool KTAIL>
-__device__ __forceinline__ void load_x(uint4 (&x)[8], const uint16_t* const (&xrow)[8], int K, int col0, int tid) {
-  // without a K tail (K % 128 == 0) only the look-ahead past the last stage
-  // leaves [0, K): it re-reads the last stage (never consumed)
-  const int col = (KTAIL ? col0 : min(col0, K - BK)) + 8 * (tid & 7);
-  uint32_t keep = col < K ? ~0u : 0u;
+__device__ __forceinline__ void load_x(uint4 (&x)[8], __amdgpu_buffer_rsrc_t xrs, uint32_t xoff, int K, int col0,
+                                       int tid) {
+  uint32_t keep = col0 + 8 * (tid & 7) < K ? ~0u : 0u;
   if (KTAIL) asm volatile("" : "+v"(keep));
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint4 v = *reinterpret_cast<const uint4*>(xrow[i] + (KTAIL ? min(col, K - 8) : col));
-    x[i] = KTAIL ? make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep) : v;
+    const uint32_t off = xoff + (uint32_t)(32 * i * K + col0) * 2u;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+    x[i] = KTAIL ? make_uint4(v[0] & keep, v[1] & keep, v[2] & keep, v[3] & keep) : make_uint4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -113,56 +127,44 @@ __device__ __forceinline__ void store_x(const uint4 (&x)[8], _Float16* Xs, int t
   }
 }
 
-// Widen half h of the tile (dwords 2h, 2h+1) of the wave's row blocks to
-// fp16(s q) in the stage buffer, record each row's stage scales, then patch
-// the first 64 residual entries of each tile segment that fall in this half:
-// fp16(s q + sr qr), with q recovered exactly from the fp16(s q) just written
-// (|q| <= 7, so any reciprocal within a few ulp gives the right rint). Lanes
-// without an entry write to a dummy word (no branches).
+// Widen half h of the tile (dwords 2h, 2h + 1) of the wave's row blocks to
+// fp16(s q) in the stage buffer, then overwrite the positions of the first
+// 64 residual entries of each tile segment that fall in this half with their
+// patched weights. A wave's LDS writes execute in order, so a patch lands
+// after the widened value it replaces; no other wave writes these rows.
+// Lanes without an entry write to their own dummy slot (no branches).
 template <int GSH>
-__device__ __forceinline__ void write_w(const TileRegs& T, _Float16* Ws, uint32_t* ssc, _Float16* dummy, int lrb0,
-                                        int h, int lane, uint32_t vmask, uint32_t vmask4, uint32_t vmagic) {
+__device__ __forceinline__ void write_w(const HalfRegs& H, _Float16* Ws, _Float16* dummy, int lrb0, int h, int lane,
+                                        uint32_t vmask, uint32_t vmask4, uint32_t vmagic) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int j = 0; j < kRbPerWave; ++j) {
     _Float16* dst = Ws + ((lrb0 + j) * kRowsPerBlock + r) * LDW + 8 * g;
-    const uint32_t d0 = h ? T.code[j].z : T.code[j].x;
-    const uint32_t d1 = h ? T.code[j].w : T.code[j].y;
-    const uint32_t s0 = dword_scale<GSH>(T.sraw[j], 2 * h), s1 = dword_scale<GSH>(T.sraw[j], 2 * h + 1);
-    *reinterpret_cast<half8_t*>(dst) = dequant_dword(d0, splat_half(s0), vmask, vmask4, vmagic);
-    *reinterpret_cast<half8_t*>(dst + 32) = dequant_dword(d1, splat_half(s1), vmask, vmask4, vmagic);
-    ssc[(lrb0 + j) * kRowsPerBlock + r] = s0 | (s1 << 16);   // same value from the 4 lanes of a row
+    const bool live = (H.live >> j) & 1u;
+    const uint32_t s0 = live ? (GSH == 2 ? H.sraw[j] & 0xFFFFu : H.sraw[j]) : 0u;
+    const uint32_t s1 = live ? (GSH == 2 ? H.sraw[j] >> 16 : H.sraw[j]) : 0u;
+    *reinterpret_cast<half8_t*>(dst) = dequant_dword(H.code[j].x, splat_half(s0), vmask, vmask4, vmagic);
+    *reinterpret_cast<half8_t*>(dst + 32) = dequant_dword(H.code[j].y, splat_half(s1), vmask, vmask4, vmagic);
   }
 #pragma unroll
   for (int j = 0; j < kRbPerWave; ++j) {
-    const uint32_t v = T.ent[j];
-    const int c = (int)(ent_col(v) & (kTileCols - 1));
-    const bool ok = v != 0u && (c >> 6) == h;
+    const uint32_t v = H.ent[j];
+    const bool ok = (uint32_t)lane < H.P.cnt[j] && (v & kPatchValid) != 0u && ((v >> 6) & 1u) == (uint32_t)h;
     const int row = (lrb0 + j) * kRowsPerBlock + (int)ent_row(v);
-    const uint32_t sb = ssc[row];
-    const float s = h_to_f(((c & 63) < 32 ? sb : sb >> 16) & 0xFFFFu);
-    _Float16* w = ok ? Ws + row * LDW + (c & 63) : dummy;
-    // s = 0 means fp16(s q) = 0, and then q = rint(0 * 1e30) = 0 as well: no select
-    const float q = rintf((float)*w * __builtin_amdgcn_rcpf(fmaxf(s, 1e-30f)));
-    *w = (_Float16)fmaf(s, q, h_to_f(ent_delta(v)));
+    _Float16* w = ok ? Ws + row * LDW + (v & 63u) : dummy + lane;
+    *reinterpret_cast<uint16_t*>(w) = (uint16_t)(v >> 16);
   }
 }
 
 // Entries 64.. of tile segments longer than 64 (dense residual tiles): rare.
-template <int GSH>
-__device__ __forceinline__ void patch_rest(const TileRegs& T, _Float16* Ws, const uint32_t* ssc, int lrb0, int h,
-                                        int lane, const uint32_t* __restrict__ entries) {
+__device__ __forceinline__ void patch_rest(const HalfRegs& H, _Float16* Ws, int lrb0, int h, int lane,
+                                           const uint32_t* __restrict__ wpatch) {
   for (int j = 0; j < kRbPerWave; ++j) {
-    for (uint32_t e = T.p0[j] + 64 + lane; e < T.p0[j] + T.cnt[j]; e += 64) {
-      const uint32_t v = entries[e];
-      const int c = (int)(ent_col(v) & (kTileCols - 1));
-      if (v == 0u || (c >> 6) != h) continue;
+    for (uint32_t e = H.P.p0[j] + 64 + lane; e < H.P.p0[j] + H.P.cnt[j]; e += 64) {
+      const uint32_t v = wpatch[e];
+      if ((v & kPatchValid) == 0u || ((v >> 6) & 1u) != (uint32_t)h) continue;
       const int row = (lrb0 + j) * kRowsPerBlock + (int)ent_row(v);
-      const uint32_t sb = ssc[row];
-      const float s = h_to_f(((c & 63) < 32 ? sb : sb >> 16) & 0xFFFFu);
-      _Float16* w = Ws + row * LDW + (c & 63);
-      const float q = (s != 0.f) ? rintf((float)*w * __builtin_amdgcn_rcpf(s)) : 0.f;
-      *w = (_Float16)fmaf(s, q, h_to_f(ent_delta(v)));
+      *reinterpret_cast<uint16_t*>(Ws + row * LDW + (v & 63u)) = (uint16_t)(v >> 16);
     }
   }
 }
@@ -210,11 +212,10 @@ template <int GSH, bool KTAIL>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ tiles,
                                                       const uint16_t* __restrict__ scales, int64_t sstride,
                                                       const uint32_t* __restrict__ tile_ptr,
-                                                      const uint32_t* __restrict__ entries,
+                                                      const uint32_t* __restrict__ wpatch,
                                                       const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
                                                       int M, int N, int K, int Kt, int Nb, int NT, int T) {
   extern __shared__ __attribute__((aligned(16))) _Float16 lds[];
-  uint32_t* const ssc = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(lds) + kScaleOff);
   _Float16* const dummy = reinterpret_cast<_Float16*>(reinterpret_cast<char*>(lds) + kDummyOff);
   _Float16* const buf0 = lds;
   _Float16* const buf1 = lds + kStageHalves;
@@ -226,9 +227,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ 
   const int wn = wave & 1, wm = wave >> 1;   // 2 x 2 waves of 128 x 128
   const int lrb0 = kRbPerWave * wave;        // local row blocks widened by this wave
   const int rbw = rb0 + lrb0;
-  const uint16_t* xrow[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) xrow[i] = X + (int64_t)min(m0 + (tid >> 3) + 32 * i, M - 1) * K;
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(X + (int64_t)m0 * K), 0, (int)(min(BM, M - m0) * K * 2), kBufferFlags);
+  const uint32_t xoff = (uint32_t)((tid >> 3) * K + 8 * (tid & 7)) * 2u;
   uint32_t vmask = 0x000F000Fu, vmask4 = 0x00F000F0u, vmagic = 0x64006400u;
   asm volatile("" : "+v"(vmask), "+v"(vmask4), "+v"(vmagic));   // keep the constants in VGPRs for v_and_or_b32
 
@@ -240,36 +241,46 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  TileRegs t0, t1;
+  // Stage s = 2 kt + h is half h of tile kt. H0 / H1 hold the next even /
+  // odd stage to prepare; pa / pb the segment bounds of the next refill of
+  // H1 / H0.
+  HalfRegs H0, H1;
+  TilePtrs pa, pb;
   uint4 xr[8];
-  load_tile<GSH>(t0, tiles, scales, sstride, tile_ptr, entries, Kt, Nb, rbw, 0, lane);
-  load_x<KTAIL>(xr, xrow, K, 0, tid);
-  write_w<GSH>(t0, buf0, ssc, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
-  if (t0.cnt[0] > 64 || t0.cnt[1] > 64 || t0.cnt[2] > 64 || t0.cnt[3] > 64)
-    patch_rest<GSH>(t0, buf0, ssc, lrb0, 0, lane, entries);
+  load_ptrs(pa, tile_ptr, Kt, Nb, rbw, 0);
+  load_half<GSH>(H0, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, 0, 0, lane);
+  load_half<GSH>(H1, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, 0, 1, lane);
+  load_x<KTAIL>(xr, xrs, xoff, K, 0, tid);
+  write_w<GSH>(H0, buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
+  if (H0.P.cnt[0] > 64 || H0.P.cnt[1] > 64 || H0.P.cnt[2] > 64 || H0.P.cnt[3] > 64)
+    patch_rest(H0, buf0, lrb0, 0, lane, wpatch);
   store_x(xr, buf0 + BN * LDW, tid);
-  load_x<KTAIL>(xr, xrow, K, BK, tid);
-  load_tile<GSH>(t1, tiles, scales, sstride, tile_ptr, entries, Kt, Nb, rbw, 1, lane);
+  load_x<KTAIL>(xr, xrs, xoff, K, BK, tid);
+  load_ptrs(pa, tile_ptr, Kt, Nb, rbw, 1);
+  load_half<GSH>(H0, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, 1, 0, lane);
+  load_ptrs(pb, tile_ptr, Kt, Nb, rbw, 2);
   __syncthreads();
 
   for (int kt = 0; kt < Kt; ++kt) {
-    // stage 2 kt (buffer 0) runs; stage 2 kt + 1 (half 1 of tile kt) is prepared in buffer 1
+    // stage 2 kt (buffer 0) runs; stage 2 kt + 1 (H1: half 1 of tile kt) is prepared in buffer 1
     mfma_stage(acc, buf0, buf0 + BN * LDW, wn, wm, lane);
-    write_w<GSH>(t0, buf1, ssc + BN, dummy, lrb0, 1, lane, vmask, vmask4, vmagic);
+    write_w<GSH>(H1, buf1, dummy, lrb0, 1, lane, vmask, vmask4, vmagic);
+    if (H1.P.cnt[0] > 64 || H1.P.cnt[1] > 64 || H1.P.cnt[2] > 64 || H1.P.cnt[3] > 64)
+      patch_rest(H1, buf1, lrb0, 1, lane, wpatch);
     store_x(xr, buf1 + BN * LDW, tid);
-    load_x<KTAIL>(xr, xrow, K, (2 * kt + 2) * BK, tid);
-    if (t0.cnt[0] > 64 || t0.cnt[1] > 64 || t0.cnt[2] > 64 || t0.cnt[3] > 64)
-      patch_rest<GSH>(t0, buf1, ssc + BN, lrb0, 1, lane, entries);
+    load_x<KTAIL>(xr, xrs, xoff, K, (2 * kt + 2) * BK, tid);
+    load_half<GSH>(H1, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt + 1, 1, lane);
+    load_ptrs(pa, tile_ptr, Kt, Nb, rbw, kt + 2);
     __syncthreads();
-    // stage 2 kt + 1 (buffer 1) runs; stage 2 kt + 2 (half 0 of tile kt + 1) is prepared in buffer 0
+    // stage 2 kt + 1 (buffer 1) runs; stage 2 kt + 2 (H0: half 0 of tile kt + 1) is prepared in buffer 0
     mfma_stage(acc, buf1, buf1 + BN * LDW, wn, wm, lane);
-    write_w<GSH>(t1, buf0, ssc, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
+    write_w<GSH>(H0, buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
+    if (H0.P.cnt[0] > 64 || H0.P.cnt[1] > 64 || H0.P.cnt[2] > 64 || H0.P.cnt[3] > 64)
+      patch_rest(H0, buf0, lrb0, 0, lane, wpatch);
     store_x(xr, buf0 + BN * LDW, tid);
-    load_x<KTAIL>(xr, xrow, K, (2 * kt + 3) * BK, tid);
-    if (t1.cnt[0] > 64 || t1.cnt[1] > 64 || t1.cnt[2] > 64 || t1.cnt[3] > 64)
-      patch_rest<GSH>(t1, buf0, ssc, lrb0, 0, lane, entries);
-    t0 = t1;
-    load_tile<GSH>(t1, tiles, scales, sstride, tile_ptr, entries, Kt, Nb, rbw, kt + 2, lane);
+    load_x<KTAIL>(xr, xrs, xoff, K, (2 * kt + 3) * BK, tid);
+    load_half<GSH>(H0, pb, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt + 2, 0, lane);
+    load_ptrs(pb, tile_ptr, Kt, Nb, rbw, kt + 3);
     __syncthreads();
   }
 
@@ -307,7 +318,7 @@ hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y,
   const int MT = (int)((M + BM - 1) / BM);
   const int T = NT * MT;
   k_gemm<GSH, KTAIL><<<dim3((unsigned)T), dim3(kThreads), kLdsBytes, s>>>(
-      reinterpret_cast<const uint4*>(p->tiles), p->scales, p->sstride, p->tile_ptr, p->entries, X, Y, (int)M,
+      reinterpret_cast<const uint4*>(p->tiles), p->scales, p->sstride, p->tile_ptr, p->wpatch, X, Y, (int)M,
       (int)p->N, (int)p->K, (int)p->Kt, (int)p->Nb, NT, T);
   return hipGetLastError();
 }

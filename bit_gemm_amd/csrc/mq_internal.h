@@ -17,6 +17,7 @@ constexpr int kTileBytes = 1024;    // 16 rows x 128 columns x 4 bits
 constexpr int kColWindow = 4096;    // residual entries store column mod 4096
 constexpr int kEntryPad = 1024;     // zero entries after the residual stream (read-ahead slack)
 constexpr int kChunk = 32;          // residual entries per MFMA chunk; row-block segments are padded to it
+constexpr uint32_t kPatchValid = 0x800u;   // bit 11 of a patched-weight entry (stream padding is 0)
 
 struct Packed;  // layout of mq_packed (the opaque handle)
 
@@ -57,6 +58,7 @@ struct mq_packed {
   float* rscale;        // [N]
   uint32_t* tile_ptr;   // [Nb*Kt + 1]
   uint32_t* entries;    // [nstream + kEntryPad]: residual stream, row blocks padded to 32 entries
+  uint32_t* wpatch;     // [nstream + kEntryPad]: the same entries carrying the patched weight fp16(s q + sr qr)
   int64_t nstream;      // entries in the stream incl. the per-row-block zero padding
   int64_t stream_cap;   // allocated stream length (excluding the trailing zero pad)
   size_t bytes;

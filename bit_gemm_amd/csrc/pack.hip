@@ -422,8 +422,10 @@ __global__ __launch_bounds__(kWave) void k_row_emit(const uint16_t* __restrict__
                                                     const float* __restrict__ rscale,
                                                     const uint32_t* __restrict__ cnt_rt,
                                                     const uint32_t* __restrict__ tile_ptr,
+                                                    const uint8_t* __restrict__ tiles,
                                                     uint16_t* __restrict__ col, uint32_t* __restrict__ rcodes32,
-                                                    uint32_t* __restrict__ entries, int64_t nnz,
+                                                    uint32_t* __restrict__ entries, uint32_t* __restrict__ wpatch,
+                                                    int64_t nnz,
                                                     int64_t stream_cap, SelState* flags) {
   const int rb = blockIdx.x, lane = threadIdx.x;
   const int r = lane & 15;
@@ -467,6 +469,9 @@ __global__ __launch_bounds__(kWave) void k_row_emit(const uint16_t* __restrict__
     if (sel) {
       int64_t pc = csr + sel_ex;
       uint32_t ps = tile_ptr[(int64_t)rb * Kt + kt] + row_off + sel_ex;
+      // the lane's base scale and the tile's codes, for the patched weight
+      const float sbase = (float)__builtin_bit_cast(_Float16, scales[(int64_t)row * sstride + t.c0 / G]);
+      const uint32_t* tw = reinterpret_cast<const uint32_t*>(tiles) + ((int64_t)rb * Kt + kt) * (kWave * 4);
       for (int c = 0; c < 32; ++c) {
         if (!((sel >> c) & 1u)) continue;
         const int j = t.c0 + c;
@@ -484,6 +489,15 @@ __global__ __launch_bounds__(kWave) void k_row_emit(const uint16_t* __restrict__
         const _Float16 dh = (_Float16)dres;
         entries[ps] = ((uint32_t)__builtin_bit_cast(uint16_t, dh) << 16) | ((uint32_t)r << 12) |
                       ((uint32_t)j & (kColWindow - 1));
+        // Patched weight for kernels that overwrite the dequantized base
+        // weight in place: fp16(s q + fp16(sr qr)), one fused multiply-add
+        // and one rounding. Column c of the lane's 32 sits in dword lane / 16
+        // of lane r + 16 (c / 8) of the tile, at nibble nib_pos(c % 8).
+        const uint32_t dw = tw[(r + 16 * (c >> 3)) * 4 + (lane >> 4)];
+        const int q = (int)((dw >> (4 * nib_pos(c & 7))) & 0xFu) - 8;
+        const _Float16 wv = (_Float16)fmaf(sbase, (float)q, (float)dh);
+        wpatch[ps] = ((uint32_t)__builtin_bit_cast(uint16_t, wv) << 16) | ((uint32_t)r << 12) | kPatchValid |
+                     ((uint32_t)j & (kTileCols - 1));
         ++pc;
         ++ps;
       }
@@ -549,6 +563,7 @@ hipError_t pack_on_device(const uint16_t* W, mq_packed* p, hipStream_t stream, u
   MQ_TRY(hipMemsetAsync(p->row_ptr, 0, (size_t)(N + 1) * sizeof(int32_t), stream));
   MQ_TRY(hipMemsetAsync(p->tile_ptr, 0, (size_t)(ntiles + 1) * sizeof(uint32_t), stream));
   MQ_TRY(hipMemsetAsync(p->entries, 0, (size_t)(p->stream_cap + kEntryPad) * sizeof(uint32_t), stream));
+  MQ_TRY(hipMemsetAsync(p->wpatch, 0, (size_t)(p->stream_cap + kEntryPad) * sizeof(uint32_t), stream));
 
   k_pack_base<<<dim3((unsigned)ntiles), dim3(kWave), 0, stream>>>(W, N, K, G, Kt, p->sstride, p->tiles,
                                                                  p->scales, st);
@@ -588,8 +603,9 @@ hipError_t pack_on_device(const uint16_t* W, mq_packed* p, hipStream_t stream, u
     k_scan_tiles<<<dim3(1), dim3(1024), 0, stream>>>(tcnt, ntiles, p->tile_ptr);
     MQ_TRY(hipGetLastError());
     k_row_emit<<<dim3(Nb), dim3(kWave), 0, stream>>>(W, p->scales, N, K, G, Kt, p->sstride, st, eb, p->row_ptr,
-                                                     p->rscale, crt, p->tile_ptr, p->col,
-                                                     reinterpret_cast<uint32_t*>(p->rcodes), p->entries, p->nnz,
+                                                     p->rscale, crt, p->tile_ptr, p->tiles, p->col,
+                                                     reinterpret_cast<uint32_t*>(p->rcodes), p->entries, p->wpatch,
+                                                     p->nnz,
                                                      p->stream_cap, st);
     MQ_TRY(hipGetLastError());
   }
