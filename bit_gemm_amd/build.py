@@ -21,8 +21,10 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmosaicq.so")
 HOSTCHECK = os.path.join(HERE, "libmq_hostcheck.so")
 SOURCES = ["api.cpp", "pack.hip", "gemv.hip", "gemm.hip"]
-# per-source code generation options (none at present)
-EXTRA: dict = {}
+# per-source code generation options: the prefill GEMM's stage body is one
+# long basic block; the ILP-oriented machine scheduler interleaves its
+# widening arithmetic with the MFMAs instead of clustering it after them
+EXTRA: dict = {"gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 ARCH = os.environ.get("MQ_OFFLOAD_ARCH", "gfx950")
 
 

@@ -132,7 +132,11 @@ __device__ __forceinline__ void store_x(const uint4 (&x)[8], _Float16* Xs, int t
 // 64 residual entries of each tile segment that fall in this half with their
 // patched weights. A wave's LDS writes execute in order, so a patch lands
 // after the widened value it replaces; no other wave writes these rows.
-// Lanes without an entry write to their own dummy slot (no branches).
+// Lanes without an entry write to their own dummy slot. The target offset is
+// blended with a mask hidden behind an empty asm: written as a select, it
+// becomes an exec-masked branch, and branches split the stage into separate
+// scheduling regions, which keeps the widening from interleaving with the
+// MFMAs.
 template <int GSH>
 __device__ __forceinline__ void write_w(const HalfRegs& H, _Float16* Ws, _Float16* dummy, int lrb0, int h, int lane,
                                         uint32_t vmask, uint32_t vmask4, uint32_t vmagic) {
@@ -149,18 +153,20 @@ __device__ __forceinline__ void write_w(const HalfRegs& H, _Float16* Ws, _Float1
 #pragma unroll
   for (int j = 0; j < kRbPerWave; ++j) {
     const uint32_t v = H.ent[j];
-    const bool ok = (uint32_t)lane < H.P.cnt[j] && (v & kPatchValid) != 0u && ((v >> 6) & 1u) == (uint32_t)h;
-    const int row = (lrb0 + j) * kRowsPerBlock + (int)ent_row(v);
-    _Float16* w = ok ? Ws + row * LDW + (v & 63u) : dummy + lane;
-    *reinterpret_cast<uint16_t*>(w) = (uint16_t)(v >> 16);
+    uint32_t okm = 0u - (((uint32_t)lane < H.P.cnt[j]) & ((v & kPatchValid) != 0u) & (((v >> 6) & 1u) == (uint32_t)h));
+    asm("" : "+v"(okm));
+    // both offsets are positive: the dummy slots follow the two stage buffers
+    const uint32_t real = (uint32_t)(((lrb0 + j) * kRowsPerBlock + (int)ent_row(v)) * LDW) + (v & 63u);
+    const uint32_t idle = (uint32_t)(dummy - Ws) + (uint32_t)lane;
+    reinterpret_cast<uint16_t*>(Ws)[idle ^ ((real ^ idle) & okm)] = (uint16_t)(v >> 16);
   }
 }
 
 // Entries 64.. of tile segments longer than 64 (dense residual tiles): rare.
-__device__ __forceinline__ void patch_rest(const HalfRegs& H, _Float16* Ws, int lrb0, int h, int lane,
+__device__ __forceinline__ void patch_rest(const TilePtrs& P, _Float16* Ws, int lrb0, int h, int lane,
                                            const uint32_t* __restrict__ wpatch) {
   for (int j = 0; j < kRbPerWave; ++j) {
-    for (uint32_t e = H.P.p0[j] + 64 + lane; e < H.P.p0[j] + H.P.cnt[j]; e += 64) {
+    for (uint32_t e = P.p0[j] + 64 + lane; e < P.p0[j] + P.cnt[j]; e += 64) {
       const uint32_t v = wpatch[e];
       if ((v & kPatchValid) == 0u || ((v >> 6) & 1u) != (uint32_t)h) continue;
       const int row = (lrb0 + j) * kRowsPerBlock + (int)ent_row(v);
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ 
   load_x<KTAIL>(xr, xrs, xoff, K, 0, tid);
   write_w<GSH>(H0, buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
   if (H0.P.cnt[0] > 64 || H0.P.cnt[1] > 64 || H0.P.cnt[2] > 64 || H0.P.cnt[3] > 64)
-    patch_rest(H0, buf0, lrb0, 0, lane, wpatch);
+    patch_rest(H0.P, buf0, lrb0, 0, lane, wpatch);
   store_x(xr, buf0 + BN * LDW, tid);
   load_x<KTAIL>(xr, xrs, xoff, K, BK, tid);
   load_ptrs(pa, tile_ptr, Kt, Nb, rbw, 1);
@@ -265,22 +271,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ 
     // stage 2 kt (buffer 0) runs; stage 2 kt + 1 (H1: half 1 of tile kt) is prepared in buffer 1
     mfma_stage(acc, buf0, buf0 + BN * LDW, wn, wm, lane);
     write_w<GSH>(H1, buf1, dummy, lrb0, 1, lane, vmask, vmask4, vmagic);
-    if (H1.P.cnt[0] > 64 || H1.P.cnt[1] > 64 || H1.P.cnt[2] > 64 || H1.P.cnt[3] > 64)
-      patch_rest(H1, buf1, lrb0, 1, lane, wpatch);
     store_x(xr, buf1 + BN * LDW, tid);
     load_x<KTAIL>(xr, xrs, xoff, K, (2 * kt + 2) * BK, tid);
+    const TilePtrs p1 = H1.P;
     load_half<GSH>(H1, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt + 1, 1, lane);
     load_ptrs(pa, tile_ptr, Kt, Nb, rbw, kt + 2);
+    if (p1.cnt[0] > 64 || p1.cnt[1] > 64 || p1.cnt[2] > 64 || p1.cnt[3] > 64) patch_rest(p1, buf1, lrb0, 1, lane, wpatch);
     __syncthreads();
     // stage 2 kt + 1 (buffer 1) runs; stage 2 kt + 2 (H0: half 0 of tile kt + 1) is prepared in buffer 0
     mfma_stage(acc, buf1, buf1 + BN * LDW, wn, wm, lane);
     write_w<GSH>(H0, buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
-    if (H0.P.cnt[0] > 64 || H0.P.cnt[1] > 64 || H0.P.cnt[2] > 64 || H0.P.cnt[3] > 64)
-      patch_rest(H0, buf0, lrb0, 0, lane, wpatch);
     store_x(xr, buf0 + BN * LDW, tid);
     load_x<KTAIL>(xr, xrs, xoff, K, (2 * kt + 3) * BK, tid);
+    const TilePtrs p0 = H0.P;
     load_half<GSH>(H0, pb, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt + 2, 0, lane);
     load_ptrs(pb, tile_ptr, Kt, Nb, rbw, kt + 3);
+    if (p0.cnt[0] > 64 || p0.cnt[1] > 64 || p0.cnt[2] > 64 || p0.cnt[3] > 64) patch_rest(p0, buf0, lrb0, 0, lane, wpatch);
     __syncthreads();
   }
 
