@@ -206,6 +206,23 @@ def bench_prefill(args, mq, synth, torch):
         out["M"][str(M)] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tflops, 1),
                             "frac_mfma_peak": round(tflops / FP16_PEAK_TFLOPS, 4)}
     p.free()
+    # Context only: a dense fp16 GEMM of the same shape through torch.matmul
+    # (the vendor BLAS), random weights. It shows what the matrix cores give a
+    # plain fp16 product of this shape on this chip; it is not part of the path.
+    dense = {}
+    Wd = torch.randn(layer.N, layer.K, dtype=torch.float16, device="cuda") * 0.02
+    for M in wl.batch:
+        Xd = torch.randn(M, layer.K, dtype=torch.float16, device="cuda")
+        Yd = torch.empty((M, layer.N), dtype=torch.float16, device="cuda")
+
+        def mm(i):
+            torch.matmul(Xd, Wd.t(), out=Yd)
+        time_events(mm, 3)
+        n = max(3, min(args.steps, 20))
+        ms = time_events(mm, n) / n
+        dense[str(M)] = round(2.0 * M * layer.N * layer.K / (ms * 1e-3) / 1e12, 1)
+    del Wd
+    out["dense_fp16_matmul_TFLOPs"] = dense
     return out
 
 
