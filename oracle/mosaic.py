@@ -132,15 +132,24 @@ def select_topk(e: np.ndarray, k: int) -> np.ndarray:
     """O5 [MQ-M2 top-K; MQ-Abs]: the k entries that come first in the order
     (|e| descending, row-major index ascending).
 
-    A stable sort on -|e| keeps equal keys in index order, so its first k
-    positions are exactly that set. Returns the selected row-major indices,
+    Written as the equivalent threshold form: T is the k-th largest |e|;
+    every entry with |e| > T is taken, then the entries with |e| == T in
+    ascending index order until k are chosen. (A full sort of all N*K keys
+    gives the same set and is what the brute-force pin compares against; the
+    threshold form needs only a partition, which keeps layers of 10^8
+    weights within seconds.) Returns the selected row-major indices,
     ascending (int64).
     """
     flat = np.abs(e).ravel()
+    n = flat.size
     if k <= 0:
         return np.zeros(0, dtype=np.int64)
-    order = np.argsort(-flat, kind="stable")
-    return np.sort(order[:k]).astype(np.int64)
+    if k >= n:
+        return np.arange(n, dtype=np.int64)
+    T = np.partition(flat, n - k)[n - k]          # the k-th largest |e|
+    above = np.flatnonzero(flat > T)
+    ties = np.flatnonzero(flat == T)[: k - above.size]
+    return np.sort(np.concatenate([above, ties])).astype(np.int64)
 
 
 # --------------------------------------------------- O6/O7: residual encode
