@@ -104,6 +104,25 @@ def time_graphs(torch, fn, warmup, steps):
     return a.elapsed_time(b)
 
 
+def replay_spread(torch, fn, warmup, steps, reps=9):
+    """Per-launch time (ms) from `reps` timed replays of one graph of `steps`
+    calls: (median, p10, p90) over the replays."""
+    import numpy as np
+    if warmup > 0:
+        capture(torch, fn, warmup).replay()
+    g = capture(torch, fn, steps)
+    out = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / steps)
+    return float(np.median(out)), float(np.percentile(out, 10)), float(np.percentile(out, 90))
+
+
 def source_digest():
     """sha256 of the decode kernel sources (counters are only valid for these)."""
     h = hashlib.sha256()
@@ -163,12 +182,28 @@ def bench_decode(args, mq, synth, torch):
     ms = time_graphs(torch, step, args.warmup, args.steps)
     bytes_step = sum(decode_bytes(first, M) for M in Ms)
     per_m = {}
-    for M in Ms:   # each M runs its own kernel: average launch duration of each
+    for M in Ms:   # each M runs its own kernel: launch duration of each (median of 9 replays)
         def one(i, M=M):
             mq.mq_linear_with(Xs[M], copies[i % ncopy], mq.KERNEL_GEMV, Ys[M])
-        mms = time_graphs(torch, one, args.warmup, args.steps) / args.steps
-        per_m[str(M)] = {"us": round(mms * 1e3, 3), "GBps": round(decode_bytes(first, M) / mms / 1e6, 1),
-                         "bytes": decode_bytes(first, M)}
+        mms, p10, p90 = replay_spread(torch, one, args.warmup, args.steps)
+        per_m[str(M)] = {"us": round(mms * 1e3, 3), "p10_us": round(p10 * 1e3, 3), "p90_us": round(p90 * 1e3, 3),
+                         "GBps": round(decode_bytes(first, M) / mms / 1e6, 1), "bytes": decode_bytes(first, M)}
+    # the same layer packed without residual (rho = 0), rotated the same way:
+    # t(rho) / t(0) is what the residual costs the fused kernel
+    Wd = torch.from_numpy(layer.W()).cuda()
+    plain = [mq.mq_pack(Wd, layer.group, 0.0)]
+    nplain = max(2, math.ceil(2 * MALL_BYTES / plain[0].device_bytes))
+    while len(plain) < nplain:
+        plain.append(mq.mq_pack(Wd, layer.group, 0.0))
+    del Wd
+    overhead = {}
+    for M in Ms:
+        def one0(i, M=M):
+            mq.mq_linear_with(Xs[M], plain[i % nplain], mq.KERNEL_GEMV, Ys[M])
+        m0 = replay_spread(torch, one0, args.warmup, args.steps)[0]
+        overhead[str(M)] = round(per_m[str(M)]["us"] / (m0 * 1e3), 3)
+    for p in plain:
+        p.free()
     # warm, single copy (weights can stay in the Infinity Cache): context only
     def warm(i):
         mq.mq_linear_with(Xs[1], first, mq.KERNEL_GEMV, Ys[1])
@@ -176,7 +211,7 @@ def bench_decode(args, mq, synth, torch):
     return {
         "layer": layer, "first": first, "ms_per_step": ms / args.steps, "bytes_step": bytes_step,
         "launches_per_step": len(Ms), "per_m": per_m, "pack_ms": pack_ms, "pack_wall_ms": pack_wall_ms,
-        "copies": ncopy, "warm_us_m1": warm_ms * 1e3, "nnz": first.nnz,
+        "copies": ncopy, "warm_us_m1": warm_ms * 1e3, "nnz": first.nnz, "overhead": overhead,
     }
 
 
@@ -206,6 +241,22 @@ def bench_prefill(args, mq, synth, torch):
         out["M"][str(M)] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tflops, 1),
                             "frac_mfma_peak": round(tflops / FP16_PEAK_TFLOPS, 4)}
     p.free()
+    # the same layer without residual (rho = 0): t(rho) / t(0)
+    W = torch.from_numpy(layer.W()).cuda()
+    p0 = mq.mq_pack(W, layer.group, 0.0)
+    del W
+    out["residual_overhead_t_rho_over_t0"] = {}
+    for M in wl.batch:
+        X = torch.from_numpy(layer.X(M)).cuda()
+        Y = torch.empty((M, layer.N), dtype=torch.float16, device="cuda")
+
+        def run0(i):
+            mq.mq_linear_with(X, p0, mq.KERNEL_GEMM, Y)
+        time_events(run0, 3)
+        n = max(3, min(args.steps, 50))
+        ms0 = time_events(run0, n) / n
+        out["residual_overhead_t_rho_over_t0"][str(M)] = round(out["M"][str(M)]["us"] / (ms0 * 1e3), 3)
+    p0.free()
     # Context only: a dense fp16 GEMM of the same shape through torch.matmul
     # (the vendor BLAS), random weights. It shows what the matrix cores give a
     # plain fp16 product of this shape on this chip; it is not part of the path.
@@ -226,10 +277,12 @@ def bench_prefill(args, mq, synth, torch):
     return out
 
 
-def cpu_baseline(layer, Ms):
-    """The oracle, as it stands, on the same decode layer: dequantisation plus
-    the float64 linear for M = 1, 4, 16 (packing by the oracle is done first
-    and reported apart). Bounded: about 10-30 s on a few host cores."""
+def cpu_baseline(layer, Ms, min_seconds=10.0, max_steps=60):
+    """The oracle, as it stands, on the same decode layer: one step is its
+    dequantisation plus the float64 linear for M = 1, 4, 16 (packing by the
+    oracle is done first and reported apart). Steps repeat until about
+    `min_seconds` of CPU work (at most `max_steps`), so the sample is long
+    enough to time and the default run still ends within minutes."""
     import numpy as np
     import oracle
     try:
@@ -243,17 +296,22 @@ def cpu_baseline(layer, Ms):
     t_pack = time.perf_counter() - t0
     Xs = {M: layer.X(M) for M in Ms}
     t0 = time.perf_counter()
-    Wt = oracle.dequant(packed)
-    for M in Ms:
-        oracle.linear(Xs[M], Wt)
-    t_lin = time.perf_counter() - t0
+    steps = 0
+    while True:
+        Wt = oracle.dequant(packed)
+        for M in Ms:
+            oracle.linear(Xs[M], Wt)
+        steps += 1
+        t_lin = time.perf_counter() - t0
+        if t_lin >= min_seconds or steps >= max_steps:
+            break
     canon = (layer.N * layer.K // 2 + 2 * layer.N * (layer.K // layer.group) + 4 * (layer.N + 1)
              + 2 * packed["nnz"] + (packed["nnz"] + 1) // 2 + 4 * layer.N)
-    nbytes = sum(canon + 2 * M * layer.K + 2 * M * layer.N for M in Ms)
+    nbytes = steps * sum(canon + 2 * M * layer.K + 2 * M * layer.N for M in Ms)
     return {"value": round(nbytes / t_lin / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle dequant + float64 linear of the full {layer.N}x{layer.K} layer at M={Ms} "
-                      f"(one step); oracle pack of the layer took {t_pack:.1f} s, not included",
-            "seconds": round(t_lin, 3), "pack_seconds": round(t_pack, 2)}
+            "sample": f"{steps} steps of the oracle's dequant + float64 linear of the full {layer.N}x{layer.K} "
+                      f"layer at M={Ms}; the oracle's pack of the layer ({t_pack:.1f} s) is not included",
+            "seconds": round(t_lin, 3), "steps": steps, "pack_seconds": round(t_pack, 2)}
 
 
 def main():
@@ -300,6 +358,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": tag,
                      "algorithmic_bytes_per_launch": dom["bytes"], "avg_launch_us": dom["us"]},
         "decode_per_M": d["per_m"],
+        "decode_residual_overhead_t_rho_over_t0": d["overhead"],
         "decode_warm_single_copy_us_M1": None if args.no_warm else round(d["warm_us_m1"], 3),
         "pack": {"workload": "decode-11008x4096", "gpu_ms": round(d["pack_ms"], 3),
                  "wall_ms_first_call": round(d["pack_wall_ms"], 3)},
