@@ -102,7 +102,8 @@ mq_status mq_linear_with(const void* X_dev_fp16, int64_t M, const mq_packed* p,
 
 /*
  * mq_packed_info -- sizes of a packed layer; any output pointer may be NULL.
- *   bytes = device bytes the handle owns.
+ *   bytes = device bytes the handle owns (codes, scales, the canonical
+ *   residual, and the two tile-ordered residual streams the kernels read).
  */
 mq_status mq_packed_info(const mq_packed* p, int64_t* N, int64_t* K, int32_t* G,
                          int64_t* nnz, size_t* bytes);
@@ -138,8 +139,11 @@ mq_status mq_export_canonical(const mq_packed* p, void* codes_u8, void* scales_f
  *   entries_u32   [tile_ptr[Nb*Kt]] residual stream sorted by (row block, tile,
  *                 row, column): bits 0-11 column mod 4096, bits 12-15 row mod 16,
  *                 bits 16-31 the residual value sr*qr rounded to fp16, which the
- *                 kernels add to the base weight s*q. Each row block's segment
- *                 ends with zero entries up to a multiple of 32.
+ *                 decode kernels add to the base weight s*q. Each row block's
+ *                 segment ends with zero entries up to a multiple of 32. (The
+ *                 prefill kernel reads a parallel copy of this stream, not
+ *                 exported, whose entries hold the patched weight
+ *                 fp16(s*q + that value) instead.)
  */
 mq_status mq_export_tiled(const mq_packed* p, void* tiles_u8, void* tile_ptr_u32,
                           void* entries_u32, void* hip_stream);
