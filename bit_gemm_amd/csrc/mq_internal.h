@@ -81,6 +81,10 @@ hipError_t launch_gemv(const mq_packed* p, const uint16_t* X, int64_t M, uint16_
 // Prefill kernel (gemm.hip): any M >= 1.
 hipError_t launch_gemm(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
 
+// Separate residual kernel (residual.hip): Y <- fp16(Y + X R^T) from the
+// canonical CSR, for the unfused comparison.
+hipError_t launch_residual(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
+
 constexpr int64_t kGemvMaxM = 64;
 
 }  // namespace mq

@@ -101,6 +101,34 @@ mq_status mq_linear_with(const void* X_dev_fp16, int64_t M, const mq_packed* p,
                          void* Y_dev_fp16, void* hip_stream, int32_t kernel);
 
 /*
+ * mq_residual_add -- Y <- Y + X R^T with a separate kernel, R the sparse
+ * residual of p (R_ij = sr_i * qr_ij on the selected entries, read from the
+ * canonical CSR), accumulated in fp32 and rounded to fp16 into Y.
+ *
+ * This is the unfused two-kernel alternative the pages compare against
+ * (MosaicQuant explainer, Methodology section 3: a separate residual kernel
+ * must load the activations again and merge partial outputs). mq_linear on a
+ * handle packed with residual_density 0 from the same W, followed by this
+ * call on the handle with the residual, gives the unfused result of the same
+ * layer; mq_linear itself never needs it. Built for the decode regime: a
+ * workgroup stages a chunk of token rows of X in LDS (16 rows at K = 4096,
+ * up to 64 for short K, 1 at K = 65536) and walks a range of CSR rows.
+ *
+ *   X_dev_fp16   [M, K] fp16 activations (device, caller-owned, 16-byte aligned)
+ *   M            number of tokens, M >= 1
+ *   p            handle from mq_pack (read only)
+ *   Y_dev_fp16   [M, N] fp16 (device, caller-owned): read, updated in place;
+ *                rows of W without residual entries leave Y unchanged
+ *   hip_stream   stream to enqueue on; the call returns without synchronising
+ *
+ * Errors: MQ_ERR_BAD_HANDLE, MQ_ERR_INVALID_ARG (NULL pointers, M <= 0,
+ * misaligned X), MQ_ERR_UNSUPPORTED (M * K or M * N >= 2^31), MQ_ERR_DEVICE.
+ * A handle with nnz = 0 enqueues nothing.
+ */
+mq_status mq_residual_add(const void* X_dev_fp16, int64_t M, const mq_packed* p, void* Y_dev_fp16,
+                          void* hip_stream);
+
+/*
  * mq_packed_info -- sizes of a packed layer; any output pointer may be NULL.
  *   bytes = device bytes the handle owns (codes, scales, the canonical
  *   residual, and the two tile-ordered residual streams the kernels read).
