@@ -196,12 +196,25 @@ def bench_decode(args, mq, synth, torch):
     while len(plain) < nplain:
         plain.append(mq.mq_pack(Wd, layer.group, 0.0))
     del Wd
-    overhead = {}
+    overhead, unfused = {}, {}
     for M in Ms:
         def one0(i, M=M):
             mq.mq_linear_with(Xs[M], plain[i % nplain], mq.KERNEL_GEMV, Ys[M])
         m0 = replay_spread(torch, one0, args.warmup, args.steps)[0]
         overhead[str(M)] = round(per_m[str(M)]["us"] / (m0 * 1e3), 3)
+
+        # unfused: the dense kernel on the residual-free copy, then the
+        # separate residual kernel reading X again and merging into Y
+        def two(i, M=M):
+            mq.mq_linear_with(Xs[M], plain[i % nplain], mq.KERNEL_GEMV, Ys[M])
+            mq.mq_residual_add(Xs[M], copies[i % ncopy], Ys[M])
+
+        def res(i, M=M):
+            mq.mq_residual_add(Xs[M], copies[i % ncopy], Ys[M])
+        m2 = replay_spread(torch, two, args.warmup, args.steps)[0]
+        mr = replay_spread(torch, res, args.warmup, args.steps)[0]
+        unfused[str(M)] = {"us": round(m2 * 1e3, 3), "residual_kernel_us": round(mr * 1e3, 3),
+                           "over_fused": round(m2 * 1e3 / per_m[str(M)]["us"], 3)}
     for p in plain:
         p.free()
     # warm, single copy (weights can stay in the Infinity Cache): context only
@@ -212,6 +225,7 @@ def bench_decode(args, mq, synth, torch):
         "layer": layer, "first": first, "ms_per_step": ms / args.steps, "bytes_step": bytes_step,
         "launches_per_step": len(Ms), "per_m": per_m, "pack_ms": pack_ms, "pack_wall_ms": pack_wall_ms,
         "copies": ncopy, "warm_us_m1": warm_ms * 1e3, "nnz": first.nnz, "overhead": overhead,
+        "unfused": unfused,
     }
 
 
@@ -359,6 +373,7 @@ def main():
                      "algorithmic_bytes_per_launch": dom["bytes"], "avg_launch_us": dom["us"]},
         "decode_per_M": d["per_m"],
         "decode_residual_overhead_t_rho_over_t0": d["overhead"],
+        "decode_unfused_two_kernels": d["unfused"],
         "decode_warm_single_copy_us_M1": None if args.no_warm else round(d["warm_us_m1"], 3),
         "pack": {"workload": "decode-11008x4096", "gpu_ms": round(d["pack_ms"], 3),
                  "wall_ms_first_call": round(d["pack_wall_ms"], 3)},
