@@ -17,9 +17,11 @@ Printed: one JSON line with the decode GB/s (algorithmic bytes of the
 canonical packed format + X + Y over kernel time), the roofline of the
 dominant decode kernel against the 8 TB/s HBM peak (with the HBM bytes that
 rocprofv3 counted for it, when those counters were taken on the current
-kernel sources), the prefill TFLOP/s on the 70B-shaped MLP (28672x8192,
-M = 512 and 2048) against the 2.5 PFLOP/s dense fp16 MFMA peak, and the CPU
-oracle timed on a bounded sample as a baseline.
+kernel sources), the residual's cost t(rho) / t(rho = 0), the unfused
+two-kernel comparison (dense kernel on a residual-free copy, then the
+separate residual kernel), the prefill TFLOP/s on the 70B-shaped MLP
+(28672x8192, M = 512 and 2048) against the 2.5 PFLOP/s dense fp16 MFMA
+peak, and the CPU oracle timed on a bounded sample as a baseline.
 """
 from __future__ import annotations
 
