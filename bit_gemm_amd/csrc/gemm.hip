@@ -60,15 +60,15 @@ __device__ __forceinline__ void load_ptrs(TilePtrs& P, const uint32_t* __restric
 // the wave's 4 row blocks. Each half set is refilled in place right after
 // its last use, two stages ahead of the next one, so the loop never copies
 // registers that are still being loaded (a copy would wait for the load).
-// Nothing is selected at load time either: row blocks past the layer and
-// tiles past K are masked where the values are used, through `live` (scale
-// forced to 0) and P.cnt (no entries).
+// Nothing is selected at load time either (a select waits for its load):
+// row blocks past the layer and tiles past K are clamped to the last ones
+// and only feed output rows that are never stored or stages that are never
+// run; rows past N inside a row block have scale 0.
 struct HalfRegs {
   uint2 code[kRbPerWave];        // dwords 2h, 2h + 1 of the lane's 16-byte slice of the tile
   uint32_t sraw[kRbPerWave];     // fp16 scale bits of the lane's row: one, or two (G = 32: dword 0 low, 1 high)
   uint32_t ent[kRbPerWave];      // patched-weight entry p0 + lane of the tile's segment (valid when lane < cnt)
-  TilePtrs P;
-  uint32_t live;                 // bit j: row block j exists and the tile is inside K
+  uint32_t cnt[kRbPerWave];      // entries in the tile's segment (scalar)
 };
 
 // Branch- and wait-free: clamped indices keep every load in bounds (1024 zero
@@ -79,10 +79,8 @@ __device__ __forceinline__ void load_half(HalfRegs& H, const TilePtrs& P, const 
                                           const uint32_t* __restrict__ wpatch, int Kt, int Nb, int rbw, int kt, int h,
                                           int lane) {
   const int r = lane & 15;
-  uint32_t live = 0;
 #pragma unroll
   for (int j = 0; j < kRbPerWave; ++j) {
-    live |= (rbw + j < Nb && kt < Kt) ? 1u << j : 0u;
     const int rb = min(rbw + j, Nb - 1), ktc = min(kt, Kt - 1);
     const int64_t t = (int64_t)rb * Kt + ktc;
     H.code[j] = reinterpret_cast<const uint2*>(tiles)[(t * 64 + lane) * 2 + h];
@@ -91,9 +89,8 @@ __device__ __forceinline__ void load_half(HalfRegs& H, const TilePtrs& P, const 
     else if constexpr (GSH == 1) H.sraw[j] = srow[2 * ktc + h];
     else H.sraw[j] = *reinterpret_cast<const uint32_t*>(srow + 4 * ktc + 2 * h);
     H.ent[j] = wpatch[P.p0[j] + lane];
+    H.cnt[j] = P.cnt[j];
   }
-  H.P = P;
-  H.live = live;
 }
 
 // X stage [BM tokens][BK columns]: 8 x 16 B per thread, 8 consecutive chunks of a
@@ -144,16 +141,15 @@ __device__ __forceinline__ void write_w(const HalfRegs& H, _Float16* Ws, _Float1
 #pragma unroll
   for (int j = 0; j < kRbPerWave; ++j) {
     _Float16* dst = Ws + ((lrb0 + j) * kRowsPerBlock + r) * LDW + 8 * g;
-    const bool live = (H.live >> j) & 1u;
-    const uint32_t s0 = live ? (GSH == 2 ? H.sraw[j] & 0xFFFFu : H.sraw[j]) : 0u;
-    const uint32_t s1 = live ? (GSH == 2 ? H.sraw[j] >> 16 : H.sraw[j]) : 0u;
+    const uint32_t s0 = GSH == 2 ? H.sraw[j] & 0xFFFFu : H.sraw[j];
+    const uint32_t s1 = GSH == 2 ? H.sraw[j] >> 16 : H.sraw[j];
     *reinterpret_cast<half8_t*>(dst) = dequant_dword(H.code[j].x, splat_half(s0), vmask, vmask4, vmagic);
     *reinterpret_cast<half8_t*>(dst + 32) = dequant_dword(H.code[j].y, splat_half(s1), vmask, vmask4, vmagic);
   }
 #pragma unroll
   for (int j = 0; j < kRbPerWave; ++j) {
     const uint32_t v = H.ent[j];
-    uint32_t okm = 0u - (((uint32_t)lane < H.P.cnt[j]) & ((v & kPatchValid) != 0u) & (((v >> 6) & 1u) == (uint32_t)h));
+    uint32_t okm = 0u - (((uint32_t)lane < H.cnt[j]) & ((v & kPatchValid) != 0u) & (((v >> 6) & 1u) == (uint32_t)h));
     asm("" : "+v"(okm));
     // both offsets are positive: the dummy slots follow the two stage buffers
     const uint32_t real = (uint32_t)(((lrb0 + j) * kRowsPerBlock + (int)ent_row(v)) * LDW) + (v & 63u);
@@ -162,9 +158,14 @@ __device__ __forceinline__ void write_w(const HalfRegs& H, _Float16* Ws, _Float1
   }
 }
 
-// Entries 64.. of tile segments longer than 64 (dense residual tiles): rare.
-__device__ __forceinline__ void patch_rest(const TilePtrs& P, _Float16* Ws, int lrb0, int h, int lane,
+// Entries 64.. of tile segments longer than 64 (dense residual tiles): rare,
+// so the segment bounds are read again here instead of being kept in
+// registers for every stage.
+__device__ __forceinline__ void patch_rest(const uint32_t* __restrict__ tile_ptr, int Kt, int Nb, int rbw, int kt,
+                                           _Float16* Ws, int lrb0, int h, int lane,
                                            const uint32_t* __restrict__ wpatch) {
+  TilePtrs P;
+  load_ptrs(P, tile_ptr, Kt, Nb, rbw, kt);
   for (int j = 0; j < kRbPerWave; ++j) {
     for (uint32_t e = P.p0[j] + 64 + lane; e < P.p0[j] + P.cnt[j]; e += 64) {
       const uint32_t v = wpatch[e];
@@ -258,8 +259,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ 
   load_half<GSH>(H1, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, 0, 1, lane);
   load_x<KTAIL>(xr, xrs, xoff, K, 0, tid);
   write_w<GSH>(H0, buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
-  if (H0.P.cnt[0] > 64 || H0.P.cnt[1] > 64 || H0.P.cnt[2] > 64 || H0.P.cnt[3] > 64)
-    patch_rest(H0.P, buf0, lrb0, 0, lane, wpatch);
+  if (H0.cnt[0] > 64 || H0.cnt[1] > 64 || H0.cnt[2] > 64 || H0.cnt[3] > 64)
+    patch_rest(tile_ptr, Kt, Nb, rbw, 0, buf0, lrb0, 0, lane, wpatch);
   store_x(xr, buf0 + BN * LDW, tid);
   load_x<KTAIL>(xr, xrs, xoff, K, BK, tid);
   load_ptrs(pa, tile_ptr, Kt, Nb, rbw, 1);
@@ -273,20 +274,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ 
     write_w<GSH>(H1, buf1, dummy, lrb0, 1, lane, vmask, vmask4, vmagic);
     store_x(xr, buf1 + BN * LDW, tid);
     load_x<KTAIL>(xr, xrs, xoff, K, (2 * kt + 2) * BK, tid);
-    const TilePtrs p1 = H1.P;
+    const bool long1 = H1.cnt[0] > 64 || H1.cnt[1] > 64 || H1.cnt[2] > 64 || H1.cnt[3] > 64;
     load_half<GSH>(H1, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt + 1, 1, lane);
     load_ptrs(pa, tile_ptr, Kt, Nb, rbw, kt + 2);
-    if (p1.cnt[0] > 64 || p1.cnt[1] > 64 || p1.cnt[2] > 64 || p1.cnt[3] > 64) patch_rest(p1, buf1, lrb0, 1, lane, wpatch);
+    if (long1) patch_rest(tile_ptr, Kt, Nb, rbw, kt, buf1, lrb0, 1, lane, wpatch);
     __syncthreads();
     // stage 2 kt + 1 (buffer 1) runs; stage 2 kt + 2 (H0: half 0 of tile kt + 1) is prepared in buffer 0
     mfma_stage(acc, buf1, buf1 + BN * LDW, wn, wm, lane);
     write_w<GSH>(H0, buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
     store_x(xr, buf0 + BN * LDW, tid);
     load_x<KTAIL>(xr, xrs, xoff, K, (2 * kt + 3) * BK, tid);
-    const TilePtrs p0 = H0.P;
+    const bool long0 = H0.cnt[0] > 64 || H0.cnt[1] > 64 || H0.cnt[2] > 64 || H0.cnt[3] > 64;
     load_half<GSH>(H0, pb, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt + 2, 0, lane);
     load_ptrs(pb, tile_ptr, Kt, Nb, rbw, kt + 3);
-    if (p0.cnt[0] > 64 || p0.cnt[1] > 64 || p0.cnt[2] > 64 || p0.cnt[3] > 64) patch_rest(p0, buf0, lrb0, 0, lane, wpatch);
+    if (long0) patch_rest(tile_ptr, Kt, Nb, rbw, kt + 1, buf0, lrb0, 0, lane, wpatch);
     __syncthreads();
   }
 
