@@ -30,24 +30,42 @@ constexpr int BN = 256;               // output features per workgroup (16 row b
 constexpr int BM = 256;               // tokens per workgroup
 constexpr int BK = 64;                // K columns per LDS stage
 constexpr int LDW = BK + 8;           // LDS row (halves): 144 B, so 8 consecutive rows hit distinct banks
-constexpr int kThreads = 256;
 constexpr int kBufferFlags = 0x00020000;   // buffer descriptor word 3: 32-bit data format, raw (unswizzled) addressing
-constexpr int kRbPerWave = 4;         // row blocks widened and patched by each wave
+// Workgroup layout: 2 (feature halves of 128 rows) x NWM (token slices)
+// waves, each owning a 128 x (256 / NWM) block of the output tile. NWM = 2:
+// 4 waves of 128 x 128 (256 accumulators, one wave per SIMD). NWM = 4: 8
+// waves of 128 x 64 (128 accumulators, two waves per SIMD, so one wave's
+// stalls are covered by the other's MFMAs).
+#ifndef MQ_GEMM_NWM
+#define MQ_GEMM_NWM 4
+#endif
+constexpr int kGemmNwm = MQ_GEMM_NWM;   // token slices per workgroup (2 or 4)
+
+template <int NWM>
+struct Cfg {
+  static constexpr int kWaves = 2 * NWM;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRb = 16 / kWaves;            // row blocks widened and patched by each wave
+  static constexpr int kJb = BM / NWM / 32;          // 32-token MFMA blocks per wave
+  static constexpr int kXr = BM * BK / 8 / kThreads; // 16-byte X chunks per thread per stage
+};
 constexpr size_t kStageHalves = (size_t)(BN + BM) * LDW;
 constexpr size_t kDummyOff = 2 * kStageHalves * sizeof(_Float16);   // [64] halves: patch targets of idle lanes
 constexpr size_t kLdsBytes = kDummyOff + 64 * sizeof(_Float16);
 
-// Residual segment bounds of one code tile for the wave's 4 row blocks
+// Residual segment bounds of one code tile for the wave's RB row blocks
 // (wave-uniform, so they live in scalar registers). They are fetched a full
 // iteration before the entry loads that use them as addresses.
+template <int RB>
 struct TilePtrs {
-  uint32_t p0[kRbPerWave], cnt[kRbPerWave];
+  uint32_t p0[RB], cnt[RB];
 };
 
-__device__ __forceinline__ void load_ptrs(TilePtrs& P, const uint32_t* __restrict__ tile_ptr, int Kt, int Nb, int rbw,
-                                          int kt) {
+template <int RB>
+__device__ __forceinline__ void load_ptrs(TilePtrs<RB>& P, const uint32_t* __restrict__ tile_ptr, int Kt, int Nb,
+                                          int rbw, int kt) {
 #pragma unroll
-  for (int j = 0; j < kRbPerWave; ++j) {
+  for (int j = 0; j < RB; ++j) {
     const bool ok = rbw + j < Nb && kt < Kt;
     const int64_t t = (int64_t)min(rbw + j, Nb - 1) * Kt + min(kt, Kt - 1);
     const uint32_t p0 = tile_ptr[t], p1 = tile_ptr[t + 1];
@@ -57,30 +75,39 @@ __device__ __forceinline__ void load_ptrs(TilePtrs& P, const uint32_t* __restric
 }
 
 // Registers holding one half (64 columns, one LDS stage) of a code tile for
-// the wave's 4 row blocks. Each half set is refilled in place right after
+// the wave's RB row blocks. Each half set is refilled in place right after
 // its last use, two stages ahead of the next one, so the loop never copies
 // registers that are still being loaded (a copy would wait for the load).
 // Nothing is selected at load time either (a select waits for its load):
 // row blocks past the layer and tiles past K are clamped to the last ones
 // and only feed output rows that are never stored or stages that are never
 // run; rows past N inside a row block have scale 0.
+template <int RB>
 struct HalfRegs {
-  uint2 code[kRbPerWave];        // dwords 2h, 2h + 1 of the lane's 16-byte slice of the tile
-  uint32_t sraw[kRbPerWave];     // fp16 scale bits of the lane's row: one, or two (G = 32: dword 0 low, 1 high)
-  uint32_t ent[kRbPerWave];      // patched-weight entry p0 + lane of the tile's segment (valid when lane < cnt)
-  uint32_t cnt[kRbPerWave];      // entries in the tile's segment (scalar)
+  uint2 code[RB];        // dwords 2h, 2h + 1 of the lane's 16-byte slice of the tile
+  uint32_t sraw[RB];     // fp16 scale bits of the lane's row: one, or two (G = 32: dword 0 low, 1 high)
+  uint32_t ent[RB];      // patched-weight entry p0 + lane of the tile's segment (valid when lane < cnt)
+  uint32_t cnt[RB];      // entries in the tile's segment (scalar)
 };
+
+template <int RB>
+__device__ __forceinline__ bool has_long_segment(const HalfRegs<RB>& H) {
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < RB; ++j) any = any || H.cnt[j] > 64;
+  return any;
+}
 
 // Branch- and wait-free: clamped indices keep every load in bounds (1024 zero
 // entries follow the stream, so p0 + lane is always readable).
-template <int GSH>
-__device__ __forceinline__ void load_half(HalfRegs& H, const TilePtrs& P, const uint4* __restrict__ tiles,
+template <int GSH, int RB>
+__device__ __forceinline__ void load_half(HalfRegs<RB>& H, const TilePtrs<RB>& P, const uint4* __restrict__ tiles,
                                           const uint16_t* __restrict__ scales, int64_t sstride,
                                           const uint32_t* __restrict__ wpatch, int Kt, int Nb, int rbw, int kt, int h,
                                           int lane) {
   const int r = lane & 15;
 #pragma unroll
-  for (int j = 0; j < kRbPerWave; ++j) {
+  for (int j = 0; j < RB; ++j) {
     const int rb = min(rbw + j, Nb - 1), ktc = min(kt, Kt - 1);
     const int64_t t = (int64_t)rb * Kt + ktc;
     H.code[j] = reinterpret_cast<const uint2*>(tiles)[(t * 64 + lane) * 2 + h];
@@ -93,8 +120,9 @@ __device__ __forceinline__ void load_half(HalfRegs& H, const TilePtrs& P, const 
   }
 }
 
-// X stage [BM tokens][BK columns]: 8 x 16 B per thread, 8 consecutive chunks of a
-// row per 8 lanes; thread tid reads rows tid / 8 + 32 i, chunk tid % 8. The
+// X stage [BM tokens][BK columns]: XR x 16 B per thread, 8 consecutive chunks of
+// a row per 8 lanes; thread tid reads rows tid / 8 + (THREADS / 8) i, chunk
+// tid % 8. The
 // loads go through a buffer resource over the workgroup's rows of X (base row
 // m0, `nrec` = valid rows x K x 2 bytes): rows past M read as zero by the
 // hardware's range check, so one offset register serves all 8 rows and no
@@ -103,23 +131,24 @@ __device__ __forceinline__ void load_half(HalfRegs& H, const TilePtrs& P, const 
 // zero; with a K tail they are masked to zero with a mask kept opaque to the
 // compiler (a select would be turned back into a branch), otherwise they
 // land in a stage that is never consumed.
-template <bool KTAIL>
-__device__ __forceinline__ void load_x(uint4 (&x)[8], __amdgpu_buffer_rsrc_t xrs, uint32_t xoff, int K, int col0,
+template <bool KTAIL, int XR, int THREADS>
+__device__ __forceinline__ void load_x(uint4 (&x)[XR], __amdgpu_buffer_rsrc_t xrs, uint32_t xoff, int K, int col0,
                                        int tid) {
   uint32_t keep = col0 + 8 * (tid & 7) < K ? ~0u : 0u;
   if (KTAIL) asm volatile("" : "+v"(keep));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t off = xoff + (uint32_t)(32 * i * K + col0) * 2u;
+  for (int i = 0; i < XR; ++i) {
+    const uint32_t off = xoff + (uint32_t)((THREADS / 8) * i * K + col0) * 2u;
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
     x[i] = KTAIL ? make_uint4(v[0] & keep, v[1] & keep, v[2] & keep, v[3] & keep) : make_uint4(v[0], v[1], v[2], v[3]);
   }
 }
 
-__device__ __forceinline__ void store_x(const uint4 (&x)[8], _Float16* Xs, int tid) {
+template <int XR, int THREADS>
+__device__ __forceinline__ void store_x(const uint4 (&x)[XR], _Float16* Xs, int tid) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int idx = tid + kThreads * i;
+  for (int i = 0; i < XR; ++i) {
+    const int idx = tid + THREADS * i;
     *reinterpret_cast<uint4*>(Xs + (idx >> 3) * LDW + 8 * (idx & 7)) = x[i];
   }
 }
@@ -134,12 +163,12 @@ __device__ __forceinline__ void store_x(const uint4 (&x)[8], _Float16* Xs, int t
 // becomes an exec-masked branch, and branches split the stage into separate
 // scheduling regions, which keeps the widening from interleaving with the
 // MFMAs.
-template <int GSH>
-__device__ __forceinline__ void write_w(const HalfRegs& H, _Float16* Ws, _Float16* dummy, int lrb0, int h, int lane,
-                                        uint32_t vmask, uint32_t vmask4, uint32_t vmagic) {
+template <int GSH, int RB>
+__device__ __forceinline__ void write_w(const HalfRegs<RB>& H, _Float16* Ws, _Float16* dummy, int lrb0, int h,
+                                        int lane, uint32_t vmask, uint32_t vmask4, uint32_t vmagic) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int j = 0; j < kRbPerWave; ++j) {
+  for (int j = 0; j < RB; ++j) {
     _Float16* dst = Ws + ((lrb0 + j) * kRowsPerBlock + r) * LDW + 8 * g;
     const uint32_t s0 = GSH == 2 ? H.sraw[j] & 0xFFFFu : H.sraw[j];
     const uint32_t s1 = GSH == 2 ? H.sraw[j] >> 16 : H.sraw[j];
@@ -147,7 +176,7 @@ __device__ __forceinline__ void write_w(const HalfRegs& H, _Float16* Ws, _Float1
     *reinterpret_cast<half8_t*>(dst + 32) = dequant_dword(H.code[j].y, splat_half(s1), vmask, vmask4, vmagic);
   }
 #pragma unroll
-  for (int j = 0; j < kRbPerWave; ++j) {
+  for (int j = 0; j < RB; ++j) {
     const uint32_t v = H.ent[j];
     uint32_t okm = 0u - (((uint32_t)lane < H.cnt[j]) & ((v & kPatchValid) != 0u) & (((v >> 6) & 1u) == (uint32_t)h));
     asm("" : "+v"(okm));
@@ -161,12 +190,13 @@ __device__ __forceinline__ void write_w(const HalfRegs& H, _Float16* Ws, _Float1
 // Entries 64.. of tile segments longer than 64 (dense residual tiles): rare,
 // so the segment bounds are read again here instead of being kept in
 // registers for every stage.
+template <int RB>
 __device__ __forceinline__ void patch_rest(const uint32_t* __restrict__ tile_ptr, int Kt, int Nb, int rbw, int kt,
                                            _Float16* Ws, int lrb0, int h, int lane,
                                            const uint32_t* __restrict__ wpatch) {
-  TilePtrs P;
+  TilePtrs<RB> P;
   load_ptrs(P, tile_ptr, Kt, Nb, rbw, kt);
-  for (int j = 0; j < kRbPerWave; ++j) {
+  for (int j = 0; j < RB; ++j) {
     for (uint32_t e = P.p0[j] + 64 + lane; e < P.p0[j] + P.cnt[j]; e += 64) {
       const uint32_t v = wpatch[e];
       if ((v & kPatchValid) == 0u || ((v >> 6) & 1u) != (uint32_t)h) continue;
@@ -176,34 +206,33 @@ __device__ __forceinline__ void patch_rest(const uint32_t* __restrict__ tile_ptr
   }
 }
 
-// One stage of MFMAs: wave (wn, wm) multiplies its 128 weight rows by its 128
-// token columns over the stage's 64 columns (4 k-steps of 16). Lane l feeds
-// row / column l % 32 and k 8 (l / 32) .. +7 of each 32x32x16 step.
-__device__ __forceinline__ void mfma_stage(float16_t (&acc)[4][4], const _Float16* Ws, const _Float16* Xs, int wn,
+// One stage of MFMAs: wave (wn, wm) multiplies its 128 weight rows by its
+// 32 JB token columns over the stage's 64 columns (4 k-steps of 16). Lane l
+// feeds row / column l % 32 and k 8 (l / 32) .. +7 of each 32x32x16 step.
+template <int JB>
+__device__ __forceinline__ void mfma_stage(float16_t (&acc)[4][JB], const _Float16* Ws, const _Float16* Xs, int wn,
                                            int wm, int lane) {
   const int r32 = lane & 31, kh = 8 * (lane >> 5);
   const _Float16* wa = Ws + (128 * wn + r32) * LDW + kh;
-  const _Float16* xb = Xs + (128 * wm + r32) * LDW + kh;
-  half8_t a[2][4], b[2][4];
+  const _Float16* xb = Xs + (32 * JB * wm + r32) * LDW + kh;
+  half8_t a[2][4], b[2][JB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a[0][i] = *reinterpret_cast<const half8_t*>(wa + 32 * i * LDW);
-    b[0][i] = *reinterpret_cast<const half8_t*>(xb + 32 * i * LDW);
-  }
+  for (int i = 0; i < 4; ++i) a[0][i] = *reinterpret_cast<const half8_t*>(wa + 32 * i * LDW);
+#pragma unroll
+  for (int j = 0; j < JB; ++j) b[0][j] = *reinterpret_cast<const half8_t*>(xb + 32 * j * LDW);
 #pragma unroll
   for (int ks = 0; ks < BK / 16; ++ks) {
     const int cb = ks & 1, nb = cb ^ 1;
     if (ks + 1 < BK / 16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[nb][i] = *reinterpret_cast<const half8_t*>(wa + 32 * i * LDW + 16 * (ks + 1));
-        b[nb][i] = *reinterpret_cast<const half8_t*>(xb + 32 * i * LDW + 16 * (ks + 1));
-      }
+      for (int i = 0; i < 4; ++i) a[nb][i] = *reinterpret_cast<const half8_t*>(wa + 32 * i * LDW + 16 * (ks + 1));
+#pragma unroll
+      for (int j = 0; j < JB; ++j) b[nb][j] = *reinterpret_cast<const half8_t*>(xb + 32 * j * LDW + 16 * (ks + 1));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cb][i], b[cb][j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < JB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cb][i], b[cb][j], acc[i][j], 0, 0, 0);
   }
 }
 
@@ -215,8 +244,8 @@ __device__ __forceinline__ int xcd_tile(int b, int T) {
   return x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
 }
 
-template <int GSH, bool KTAIL>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ tiles,
+template <int GSH, bool KTAIL, int NWM>
+__global__ __launch_bounds__(Cfg<NWM>::kThreads, 1) void k_gemm(const uint4* __restrict__ tiles,
                                                       const uint16_t* __restrict__ scales, int64_t sstride,
                                                       const uint32_t* __restrict__ tile_ptr,
                                                       const uint32_t* __restrict__ wpatch,
@@ -231,8 +260,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ 
   const int mt = tile / NT, nt = tile - mt * NT;
   const int rb0 = nt * (BN / kRowsPerBlock), m0 = mt * BM;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, tid = threadIdx.x;
-  const int wn = wave & 1, wm = wave >> 1;   // 2 x 2 waves of 128 x 128
-  const int lrb0 = kRbPerWave * wave;        // local row blocks widened by this wave
+  constexpr int RB = Cfg<NWM>::kRb, JB = Cfg<NWM>::kJb, XR = Cfg<NWM>::kXr, TH = Cfg<NWM>::kThreads;
+  const int wn = wave & 1, wm = wave >> 1;   // feature half, token slice
+  const int lrb0 = RB * wave;                // local row blocks widened by this wave
   const int rbw = rb0 + lrb0;
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(X + (int64_t)m0 * K), 0, (int)(min(BM, M - m0) * K * 2), kBufferFlags);
@@ -240,29 +270,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ 
   uint32_t vmask = 0x000F000Fu, vmask4 = 0x00F000F0u, vmagic = 0x64006400u;
   asm volatile("" : "+v"(vmask), "+v"(vmask4), "+v"(vmagic));   // keep the constants in VGPRs for v_and_or_b32
 
-  float16_t acc[4][4];
+  float16_t acc[4][JB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   // Stage s = 2 kt + h is half h of tile kt. H0 / H1 hold the next even /
   // odd stage to prepare; pa / pb the segment bounds of the next refill of
   // H1 / H0.
-  HalfRegs H0, H1;
-  TilePtrs pa, pb;
-  uint4 xr[8];
+  HalfRegs<RB> H0, H1;
+  TilePtrs<RB> pa, pb;
+  uint4 xr[XR];
   load_ptrs(pa, tile_ptr, Kt, Nb, rbw, 0);
   load_half<GSH>(H0, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, 0, 0, lane);
   load_half<GSH>(H1, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, 0, 1, lane);
-  load_x<KTAIL>(xr, xrs, xoff, K, 0, tid);
+  load_x<KTAIL, XR, TH>(xr, xrs, xoff, K, 0, tid);
   write_w<GSH>(H0, buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
-  if (H0.cnt[0] > 64 || H0.cnt[1] > 64 || H0.cnt[2] > 64 || H0.cnt[3] > 64)
-    patch_rest(tile_ptr, Kt, Nb, rbw, 0, buf0, lrb0, 0, lane, wpatch);
-  store_x(xr, buf0 + BN * LDW, tid);
-  load_x<KTAIL>(xr, xrs, xoff, K, BK, tid);
+  if (has_long_segment(H0)) patch_rest<RB>(tile_ptr, Kt, Nb, rbw, 0, buf0, lrb0, 0, lane, wpatch);
+  store_x<XR, TH>(xr, buf0 + BN * LDW, tid);
+  load_x<KTAIL, XR, TH>(xr, xrs, xoff, K, BK, tid);
   load_ptrs(pa, tile_ptr, Kt, Nb, rbw, 1);
   load_half<GSH>(H0, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, 1, 0, lane);
   load_ptrs(pb, tile_ptr, Kt, Nb, rbw, 2);
@@ -272,33 +301,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ 
     // stage 2 kt (buffer 0) runs; stage 2 kt + 1 (H1: half 1 of tile kt) is prepared in buffer 1
     mfma_stage(acc, buf0, buf0 + BN * LDW, wn, wm, lane);
     write_w<GSH>(H1, buf1, dummy, lrb0, 1, lane, vmask, vmask4, vmagic);
-    store_x(xr, buf1 + BN * LDW, tid);
-    load_x<KTAIL>(xr, xrs, xoff, K, (2 * kt + 2) * BK, tid);
-    const bool long1 = H1.cnt[0] > 64 || H1.cnt[1] > 64 || H1.cnt[2] > 64 || H1.cnt[3] > 64;
+    store_x<XR, TH>(xr, buf1 + BN * LDW, tid);
+    load_x<KTAIL, XR, TH>(xr, xrs, xoff, K, (2 * kt + 2) * BK, tid);
+    const bool long1 = has_long_segment(H1);
     load_half<GSH>(H1, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt + 1, 1, lane);
     load_ptrs(pa, tile_ptr, Kt, Nb, rbw, kt + 2);
-    if (long1) patch_rest(tile_ptr, Kt, Nb, rbw, kt, buf1, lrb0, 1, lane, wpatch);
+    if (long1) patch_rest<RB>(tile_ptr, Kt, Nb, rbw, kt, buf1, lrb0, 1, lane, wpatch);
     __syncthreads();
     // stage 2 kt + 1 (buffer 1) runs; stage 2 kt + 2 (H0: half 0 of tile kt + 1) is prepared in buffer 0
     mfma_stage(acc, buf1, buf1 + BN * LDW, wn, wm, lane);
     write_w<GSH>(H0, buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
-    store_x(xr, buf0 + BN * LDW, tid);
-    load_x<KTAIL>(xr, xrs, xoff, K, (2 * kt + 3) * BK, tid);
-    const bool long0 = H0.cnt[0] > 64 || H0.cnt[1] > 64 || H0.cnt[2] > 64 || H0.cnt[3] > 64;
+    store_x<XR, TH>(xr, buf0 + BN * LDW, tid);
+    load_x<KTAIL, XR, TH>(xr, xrs, xoff, K, (2 * kt + 3) * BK, tid);
+    const bool long0 = has_long_segment(H0);
     load_half<GSH>(H0, pb, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt + 2, 0, lane);
     load_ptrs(pb, tile_ptr, Kt, Nb, rbw, kt + 3);
-    if (long0) patch_rest(tile_ptr, Kt, Nb, rbw, kt + 1, buf0, lrb0, 0, lane, wpatch);
+    if (long0) patch_rest<RB>(tile_ptr, Kt, Nb, rbw, kt + 1, buf0, lrb0, 0, lane, wpatch);
     __syncthreads();
   }
 
   // Epilogue: register v of lane l holds D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32]
   // of each 32x32 block (rows = output features, columns = tokens).
   const int nbase = rb0 * kRowsPerBlock + 128 * wn + 4 * (lane >> 5);
-  const int mbase = m0 + 128 * wm + (lane & 31);
+  const int mbase = m0 + 32 * JB * wm + (lane & 31);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < JB; ++j) {
       const int m = mbase + 32 * j;
       if (m >= M) continue;
 #pragma unroll
@@ -312,11 +341,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const uint4* __restrict__ 
   }
 }
 
-template <int GSH, bool KTAIL>
+template <int GSH, bool KTAIL, int NWM>
 hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<GSH, KTAIL>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<GSH, KTAIL, NWM>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -324,7 +353,7 @@ hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y,
   const int NT = (int)((p->Nb + (BN / kRowsPerBlock) - 1) / (BN / kRowsPerBlock));
   const int MT = (int)((M + BM - 1) / BM);
   const int T = NT * MT;
-  k_gemm<GSH, KTAIL><<<dim3((unsigned)T), dim3(kThreads), kLdsBytes, s>>>(
+  k_gemm<GSH, KTAIL, NWM><<<dim3((unsigned)T), dim3(Cfg<NWM>::kThreads), kLdsBytes, s>>>(
       reinterpret_cast<const uint4*>(p->tiles), p->scales, p->sstride, p->tile_ptr, p->wpatch, X, Y, (int)M,
       (int)p->N, (int)p->K, (int)p->Kt, (int)p->Nb, NT, T);
   return hipGetLastError();
@@ -334,9 +363,9 @@ hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y,
 
 template <bool KTAIL>
 hipError_t launch_k(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
-  if (p->G == 128) return launch<0, KTAIL>(p, X, M, Y, s);
-  if (p->G == 64) return launch<1, KTAIL>(p, X, M, Y, s);
-  return launch<2, KTAIL>(p, X, M, Y, s);
+  if (p->G == 128) return launch<0, KTAIL, kGemmNwm>(p, X, M, Y, s);
+  if (p->G == 64) return launch<1, KTAIL, kGemmNwm>(p, X, M, Y, s);
+  return launch<2, KTAIL, kGemmNwm>(p, X, M, Y, s);
 }
 
 hipError_t launch_gemm(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
