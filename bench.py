@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--skip-extra", action="store_true",
+                    help="skip the transformer-block and residual-sweep legs")
     ap.add_argument("--only", choices=["decode", "prefill", "copy"], default=None,
                     help="run one leg only (profiling runs); 'copy' runs the plain device copy that "
                          "calibrates the HBM byte counters")
@@ -293,6 +295,88 @@ def bench_prefill(args, mq, synth, torch):
     return out
 
 
+def bench_block(args, mq, synth, torch):
+    """The seven linears of one 4096-hidden block at M = 16, back to back on
+    one stream (one step = 7 launches), rotated over enough packed copies
+    that the Infinity Cache cannot hold them."""
+    wl = synth.WORKLOADS["block-4096h"]
+    M = wl.batch[0]
+    first = []
+    for layer in wl.layers:
+        W = torch.from_numpy(layer.W()).cuda()
+        first.append(mq.mq_pack(W, layer.group, layer.rho))
+        del W
+    ncopy = max(2, math.ceil(2 * MALL_BYTES / sum(p.device_bytes for p in first)))
+    copies = [first]
+    for _ in range(ncopy - 1):
+        c = []
+        for layer in wl.layers:
+            W = torch.from_numpy(layer.W()).cuda()
+            c.append(mq.mq_pack(W, layer.group, layer.rho))
+            del W
+        copies.append(c)
+    Xs = [torch.from_numpy(layer.X(M)).cuda() for layer in wl.layers]
+    Ys = [torch.empty((M, layer.N), dtype=torch.float16, device="cuda") for layer in wl.layers]
+
+    def step(i):
+        c = copies[i % ncopy]
+        for x, p, y in zip(Xs, c, Ys):
+            mq.mq_linear(x, p, y)
+    med, p10, p90 = replay_spread(torch, step, max(2, args.warmup // 4), max(10, args.steps // 4))
+    nbytes = sum(p.canonical_bytes() + 2 * M * p.K + 2 * M * p.N for p in first)
+    for c in copies:
+        for p in c:
+            p.free()
+    return {"workload": wl.name, "M": M, "launches_per_step": len(wl.layers), "packed_copies": ncopy,
+            "us": round(med * 1e3, 2), "p10_us": round(p10 * 1e3, 2), "p90_us": round(p90 * 1e3, 2),
+            "GBps": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes": nbytes}
+
+
+def bench_sweep(args, mq, synth, torch):
+    """The 14336x4096 residual sweep: for each outlier placement, the layer
+    packed at rho = 0 and at each density; mq_pack timed on its own (GPU
+    events) and the linear at M = 1, 64 (rotated copies, graph replay) and
+    512 (event loop); t(rho) / t(0) per M."""
+    out = {}
+    for mode, _ in synth.SWEEP_MODES:
+        layer0 = synth.sweep_layer(mode, 0.0)
+        W = torch.from_numpy(layer0.W()).cuda()
+        Xs = {M: torch.from_numpy(layer0.X(M)).cuda() for M in synth.SWEEP_BATCH}
+        Ys = {M: torch.empty((M, layer0.N), dtype=torch.float16, device="cuda") for M in synth.SWEEP_BATCH}
+        per = {}
+        for rho in (0.0,) + tuple(synth.SWEEP_RHOS):
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            p = mq.mq_pack(W, layer0.group, rho)
+            ev1.record()
+            torch.cuda.synchronize()
+            entry = {"nnz": p.nnz, "pack_ms": round(ev0.elapsed_time(ev1), 3), "us": {}}
+            ncopy = max(2, math.ceil(2 * MALL_BYTES / p.device_bytes))
+            copies = [p] + [mq.mq_pack(W, layer0.group, rho) for _ in range(ncopy - 1)]
+            for M in synth.SWEEP_BATCH:
+                if M <= mq.GEMV_MAX_M:
+                    def one(i, M=M):
+                        mq.mq_linear(Xs[M], copies[i % ncopy], Ys[M])
+                    us = replay_spread(torch, one, max(2, args.warmup // 4), max(20, args.steps // 4), reps=5)[0] * 1e3
+                else:
+                    def big(i, M=M):
+                        mq.mq_linear(Xs[M], p, Ys[M])
+                    time_events(big, 2)
+                    n = max(3, min(args.steps, 20))
+                    us = time_events(big, n) / n * 1e3
+                entry["us"][str(M)] = round(us, 2)
+            for c in copies:
+                c.free()
+            per[str(rho)] = entry
+        base = per["0.0"]["us"]
+        for rho, entry in per.items():
+            entry["t_over_t0"] = {M: round(v / base[M], 3) for M, v in entry["us"].items()}
+        out[mode] = per
+        del W
+    return {"workload": "sweep-14336x4096", "N": 14336, "K": 4096, "group": 128, "by_placement": out}
+
+
 def cpu_baseline(layer, Ms, min_seconds=10.0, max_steps=60):
     """The oracle, as it stands, on the same decode layer: one step is its
     dequantisation plus the float64 linear for M = 1, 4, 16 (packing by the
@@ -383,6 +467,9 @@ def main():
     if args.only != "decode":
         if not args.skip_prefill:
             line["prefill"] = bench_prefill(args, mq, synth, torch)
+        if not args.skip_extra:
+            line["block_4096h_m16"] = bench_block(args, mq, synth, torch)
+            line["residual_sweep"] = bench_sweep(args, mq, synth, torch)
         if not args.skip_cpu:
             line["cpu_baseline"] = cpu_baseline(d["layer"], [1, 4, 16])
     print(json.dumps(line), flush=True)
