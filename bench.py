@@ -355,7 +355,7 @@ def bench_sweep(args, mq, synth, torch):
             ncopy = max(2, math.ceil(2 * MALL_BYTES / p.device_bytes))
             copies = [p] + [mq.mq_pack(W, layer0.group, rho) for _ in range(ncopy - 1)]
             for M in synth.SWEEP_BATCH:
-                if M <= mq.GEMV_MAX_M:
+                if M <= 64:   # small batches: graph replays over rotated copies (cold weights)
                     def one(i, M=M):
                         mq.mq_linear(Xs[M], copies[i % ncopy], Ys[M])
                     us = replay_spread(torch, one, max(2, args.warmup // 4), max(20, args.steps // 4), reps=5)[0] * 1e3

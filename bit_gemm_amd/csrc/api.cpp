@@ -155,7 +155,7 @@ static mq_status linear_impl(const void* X, int64_t M, const mq_packed* p, void*
   if (kernel < MQ_KERNEL_AUTO || kernel > MQ_KERNEL_GEMM) return MQ_ERR_INVALID_ARG;
   bool gemv;
   if (kernel == MQ_KERNEL_AUTO)
-    gemv = M <= mq::kGemvMaxM;
+    gemv = M <= mq::kAutoGemvMaxM;
   else if (kernel == MQ_KERNEL_GEMV) {
     if (M > mq::kGemvMaxM) return MQ_ERR_UNSUPPORTED;
     gemv = true;

@@ -18,6 +18,9 @@
 //     interleave with the current stage's MFMAs; one barrier per stage;
 //   * workgroups are ordered so that consecutive tiles of one 256-token
 //     slice run on the same XCD and share its L2 for X.
+#include <algorithm>
+#include <type_traits>
+
 #include "kernel_common.h"
 #include "mq_internal.h"
 
@@ -27,31 +30,50 @@ namespace {
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BN = 256;               // output features per workgroup (16 row blocks)
-constexpr int BM = 256;               // tokens per workgroup
 constexpr int BK = 64;                // K columns per LDS stage
 constexpr int LDW = BK + 8;           // LDS row (halves): 144 B, so 8 consecutive rows hit distinct banks
 constexpr int kBufferFlags = 0x00020000;   // buffer descriptor word 3: 32-bit data format, raw (unswizzled) addressing
-// Workgroup layout: 2 (feature halves of 128 rows) x NWM (token slices)
-// waves, each owning a 128 x (256 / NWM) block of the output tile. NWM = 2:
-// 4 waves of 128 x 128 (256 accumulators, one wave per SIMD). NWM = 4: 8
-// waves of 128 x 64 (128 accumulators, two waves per SIMD, so one wave's
-// stalls are covered by the other's MFMAs).
-#ifndef MQ_GEMM_NWM
-#define MQ_GEMM_NWM 4
-#endif
-constexpr int kGemmNwm = MQ_GEMM_NWM;   // token slices per workgroup (2 or 4)
+constexpr int kSplitTarget = 256;       // workgroups to aim for when K is split (one per CU)
 
-template <int NWM>
+// Workgroup shape: a BN x BM_ output tile (features x tokens) computed by
+// NWN_ x NWM_ waves, each owning a (BN / NWN_) x (BM_ / NWM_) block of 32x32
+// MFMA tiles.
+//   * Wide (BM 256, 2 x 4 waves of 128 x 64): 128 accumulators per wave, two
+//     waves per SIMD, so one wave's stalls are covered by the other's MFMAs.
+//   * Narrow (BM 64, 8 x 1 waves of 32 x 64), for up to a few dozen tokens:
+//     a wide tile would spend three quarters of its MFMAs on token rows past
+//     M; here every wave still widens two of the 16 row blocks. Its stages
+//     are short and its accumulators few, so the loads run four stages
+//     ahead (a ring of register sets) instead of two, which keeps twice as
+//     many bytes in flight to cover the memory latency.
+template <int BM_, int NWN_, int NWM_, int PD_>
 struct Cfg {
-  static constexpr int kWaves = 2 * NWM;
+  static constexpr int kBM = BM_;
+  static constexpr int kNwn = NWN_, kNwm = NWM_;
+  static constexpr int kWaves = NWN_ * NWM_;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kRb = 16 / kWaves;            // row blocks widened and patched by each wave
-  static constexpr int kJb = BM / NWM / 32;          // 32-token MFMA blocks per wave
-  static constexpr int kXr = BM * BK / 8 / kThreads; // 16-byte X chunks per thread per stage
+  static constexpr int kRb = 16 / kWaves;              // row blocks widened and patched by each wave
+  static constexpr int kIb = BN / NWN_ / 32;           // 32-feature MFMA blocks per wave
+  static constexpr int kJb = BM_ / NWM_ / 32;          // 32-token MFMA blocks per wave
+  static constexpr int kXr = BM_ * BK / 8 / kThreads;  // 16-byte X chunks per thread per stage
+  static constexpr int kPd = PD_;                      // stages loaded ahead: 2, or a ring of 4 or 8
+  static constexpr size_t kStageHalves = (size_t)(BN + BM_) * LDW;
+  static constexpr size_t kDummyOff = 2 * kStageHalves * sizeof(_Float16);   // [64] halves: patch targets of idle lanes
+  static constexpr size_t kLdsBytes = kDummyOff + 64 * sizeof(_Float16);
+  static_assert(kWaves * kRb == 16 && kXr >= 1 && kIb >= 1 && kJb >= 1, "workgroup shape");
 };
-constexpr size_t kStageHalves = (size_t)(BN + BM) * LDW;
-constexpr size_t kDummyOff = 2 * kStageHalves * sizeof(_Float16);   // [64] halves: patch targets of idle lanes
-constexpr size_t kLdsBytes = kDummyOff + 64 * sizeof(_Float16);
+using CfgWide = Cfg<256, 2, 4, 2>;
+using CfgNarrow = Cfg<64, 8, 1, 4>;
+#ifndef MQ_GEMM_NARROW_MAX_M
+#define MQ_GEMM_NARROW_MAX_M 128
+#endif
+constexpr int64_t kNarrowMaxM = MQ_GEMM_NARROW_MAX_M;   // token counts up to this use the narrow shape
+
+// v_perm_b32 selectors: the low / high fp16 of a dword in both halves
+constexpr uint32_t kSelLo = 0x05040100u, kSelHi = 0x07060302u;
+__device__ __forceinline__ half2_t splat_sel(uint32_t dword, uint32_t sel) {
+  return __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(dword, dword, sel));
+}
 
 // Residual segment bounds of one code tile for the wave's RB row blocks
 // (wave-uniform, so they live in scalar registers). They are fetched a full
@@ -85,7 +107,8 @@ __device__ __forceinline__ void load_ptrs(TilePtrs<RB>& P, const uint32_t* __res
 template <int RB>
 struct HalfRegs {
   uint2 code[RB];        // dwords 2h, 2h + 1 of the lane's 16-byte slice of the tile
-  uint32_t sraw[RB];     // fp16 scale bits of the lane's row: one, or two (G = 32: dword 0 low, 1 high)
+  uint32_t sraw[RB];     // the aligned dword of the lane's scale row holding this stage's scale(s)
+  uint32_t sel;          // byte selector of the scale in it (G = 128 / 64; scalar)
   uint32_t ent[RB];      // patched-weight entry p0 + lane of the tile's segment (valid when lane < cnt)
   uint32_t cnt[RB];      // entries in the tile's segment (scalar)
 };
@@ -112,12 +135,16 @@ __device__ __forceinline__ void load_half(HalfRegs<RB>& H, const TilePtrs<RB>& P
     const int64_t t = (int64_t)rb * Kt + ktc;
     H.code[j] = reinterpret_cast<const uint2*>(tiles)[(t * 64 + lane) * 2 + h];
     const uint16_t* srow = scales + (int64_t)(rb * kRowsPerBlock + r) * sstride;
-    if constexpr (GSH == 0) H.sraw[j] = srow[ktc];
-    else if constexpr (GSH == 1) H.sraw[j] = srow[2 * ktc + h];
+    // whole aligned dwords (scale rows are padded to 8 halves): a 16-bit load
+    // would need a zero-extension, which the compiler may place right after
+    // the load and so wait for it a stage early
+    if constexpr (GSH == 0) H.sraw[j] = reinterpret_cast<const uint32_t*>(srow)[ktc >> 1];
+    else if constexpr (GSH == 1) H.sraw[j] = reinterpret_cast<const uint32_t*>(srow)[ktc];
     else H.sraw[j] = *reinterpret_cast<const uint32_t*>(srow + 4 * ktc + 2 * h);
     H.ent[j] = wpatch[P.p0[j] + lane];
     H.cnt[j] = P.cnt[j];
   }
+  H.sel = (GSH == 0 ? (min(kt, Kt - 1) & 1) : h) ? kSelHi : kSelLo;
 }
 
 // X stage [BM tokens][BK columns]: XR x 16 B per thread, 8 consecutive chunks of
@@ -170,10 +197,10 @@ __device__ __forceinline__ void write_w(const HalfRegs<RB>& H, _Float16* Ws, _Fl
 #pragma unroll
   for (int j = 0; j < RB; ++j) {
     _Float16* dst = Ws + ((lrb0 + j) * kRowsPerBlock + r) * LDW + 8 * g;
-    const uint32_t s0 = GSH == 2 ? H.sraw[j] & 0xFFFFu : H.sraw[j];
-    const uint32_t s1 = GSH == 2 ? H.sraw[j] >> 16 : H.sraw[j];
-    *reinterpret_cast<half8_t*>(dst) = dequant_dword(H.code[j].x, splat_half(s0), vmask, vmask4, vmagic);
-    *reinterpret_cast<half8_t*>(dst + 32) = dequant_dword(H.code[j].y, splat_half(s1), vmask, vmask4, vmagic);
+    const half2_t s0 = splat_sel(H.sraw[j], GSH == 2 ? kSelLo : H.sel);
+    const half2_t s1 = GSH == 2 ? splat_sel(H.sraw[j], kSelHi) : s0;
+    *reinterpret_cast<half8_t*>(dst) = dequant_dword(H.code[j].x, s0, vmask, vmask4, vmagic);
+    *reinterpret_cast<half8_t*>(dst + 32) = dequant_dword(H.code[j].y, s1, vmask, vmask4, vmagic);
   }
 #pragma unroll
   for (int j = 0; j < RB; ++j) {
@@ -206,18 +233,18 @@ __device__ __forceinline__ void patch_rest(const uint32_t* __restrict__ tile_ptr
   }
 }
 
-// One stage of MFMAs: wave (wn, wm) multiplies its 128 weight rows by its
+// One stage of MFMAs: wave (wn, wm) multiplies its 32 IB weight rows by its
 // 32 JB token columns over the stage's 64 columns (4 k-steps of 16). Lane l
 // feeds row / column l % 32 and k 8 (l / 32) .. +7 of each 32x32x16 step.
-template <int JB>
-__device__ __forceinline__ void mfma_stage(float16_t (&acc)[4][JB], const _Float16* Ws, const _Float16* Xs, int wn,
+template <int IB, int JB>
+__device__ __forceinline__ void mfma_stage(float16_t (&acc)[IB][JB], const _Float16* Ws, const _Float16* Xs, int wn,
                                            int wm, int lane) {
   const int r32 = lane & 31, kh = 8 * (lane >> 5);
-  const _Float16* wa = Ws + (128 * wn + r32) * LDW + kh;
+  const _Float16* wa = Ws + (32 * IB * wn + r32) * LDW + kh;
   const _Float16* xb = Xs + (32 * JB * wm + r32) * LDW + kh;
-  half8_t a[2][4], b[2][JB];
+  half8_t a[2][IB], b[2][JB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[0][i] = *reinterpret_cast<const half8_t*>(wa + 32 * i * LDW);
+  for (int i = 0; i < IB; ++i) a[0][i] = *reinterpret_cast<const half8_t*>(wa + 32 * i * LDW);
 #pragma unroll
   for (int j = 0; j < JB; ++j) b[0][j] = *reinterpret_cast<const half8_t*>(xb + 32 * j * LDW);
 #pragma unroll
@@ -225,12 +252,12 @@ __device__ __forceinline__ void mfma_stage(float16_t (&acc)[4][JB], const _Float
     const int cb = ks & 1, nb = cb ^ 1;
     if (ks + 1 < BK / 16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[nb][i] = *reinterpret_cast<const half8_t*>(wa + 32 * i * LDW + 16 * (ks + 1));
+      for (int i = 0; i < IB; ++i) a[nb][i] = *reinterpret_cast<const half8_t*>(wa + 32 * i * LDW + 16 * (ks + 1));
 #pragma unroll
       for (int j = 0; j < JB; ++j) b[nb][j] = *reinterpret_cast<const half8_t*>(xb + 32 * j * LDW + 16 * (ks + 1));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < IB; ++i)
 #pragma unroll
       for (int j = 0; j < JB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cb][i], b[cb][j], acc[i][j], 0, 0, 0);
   }
@@ -244,24 +271,29 @@ __device__ __forceinline__ int xcd_tile(int b, int T) {
   return x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
 }
 
-template <int GSH, bool KTAIL, int NWM>
-__global__ __launch_bounds__(Cfg<NWM>::kThreads, 1) void k_gemm(const uint4* __restrict__ tiles,
+template <int GSH, bool KTAIL, class C>
+__global__ __launch_bounds__(C::kThreads, 1) void k_gemm(const uint4* __restrict__ tiles,
                                                       const uint16_t* __restrict__ scales, int64_t sstride,
                                                       const uint32_t* __restrict__ tile_ptr,
                                                       const uint32_t* __restrict__ wpatch,
                                                       const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
-                                                      int M, int N, int K, int Kt, int Nb, int NT, int T) {
+                                                      float* __restrict__ part, int M, int N, int K, int Kt, int Nb,
+                                                      int NT, int T, int kt_per_split) {
   extern __shared__ __attribute__((aligned(16))) _Float16 lds[];
-  _Float16* const dummy = reinterpret_cast<_Float16*>(reinterpret_cast<char*>(lds) + kDummyOff);
+  constexpr int BM = C::kBM;
+  _Float16* const dummy = reinterpret_cast<_Float16*>(reinterpret_cast<char*>(lds) + C::kDummyOff);
   _Float16* const buf0 = lds;
-  _Float16* const buf1 = lds + kStageHalves;
+  _Float16* const buf1 = lds + C::kStageHalves;
 
   const int tile = xcd_tile(blockIdx.x, T);
+  // split-K: this workgroup covers code tiles [kt0, kt1) (the whole K unless
+  // the layer has too few output tiles to fill the chip)
+  const int kt0 = blockIdx.y * kt_per_split, kt1 = min(Kt, kt0 + kt_per_split);
   const int mt = tile / NT, nt = tile - mt * NT;
   const int rb0 = nt * (BN / kRowsPerBlock), m0 = mt * BM;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, tid = threadIdx.x;
-  constexpr int RB = Cfg<NWM>::kRb, JB = Cfg<NWM>::kJb, XR = Cfg<NWM>::kXr, TH = Cfg<NWM>::kThreads;
-  const int wn = wave & 1, wm = wave >> 1;   // feature half, token slice
+  constexpr int RB = C::kRb, IB = C::kIb, JB = C::kJb, XR = C::kXr, TH = C::kThreads;
+  const int wn = wave % C::kNwn, wm = wave / C::kNwn;   // feature slice, token slice
   const int lrb0 = RB * wave;                // local row blocks widened by this wave
   const int rbw = rb0 + lrb0;
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -270,9 +302,9 @@ __global__ __launch_bounds__(Cfg<NWM>::kThreads, 1) void k_gemm(const uint4* __r
   uint32_t vmask = 0x000F000Fu, vmask4 = 0x00F000F0u, vmagic = 0x64006400u;
   asm volatile("" : "+v"(vmask), "+v"(vmask4), "+v"(vmagic));   // keep the constants in VGPRs for v_and_or_b32
 
-  float16_t acc[4][JB];
+  float16_t acc[IB][JB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < IB; ++i)
 #pragma unroll
     for (int j = 0; j < JB; ++j)
 #pragma unroll
@@ -283,21 +315,22 @@ __global__ __launch_bounds__(Cfg<NWM>::kThreads, 1) void k_gemm(const uint4* __r
   // H1 / H0.
   HalfRegs<RB> H0, H1;
   TilePtrs<RB> pa, pb;
+  if constexpr (C::kPd == 2) {
   uint4 xr[XR];
-  load_ptrs(pa, tile_ptr, Kt, Nb, rbw, 0);
-  load_half<GSH>(H0, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, 0, 0, lane);
-  load_half<GSH>(H1, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, 0, 1, lane);
-  load_x<KTAIL, XR, TH>(xr, xrs, xoff, K, 0, tid);
+  load_ptrs(pa, tile_ptr, Kt, Nb, rbw, kt0);
+  load_half<GSH>(H0, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt0, 0, lane);
+  load_half<GSH>(H1, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt0, 1, lane);
+  load_x<KTAIL, XR, TH>(xr, xrs, xoff, K, 2 * kt0 * BK, tid);
   write_w<GSH>(H0, buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
-  if (has_long_segment(H0)) patch_rest<RB>(tile_ptr, Kt, Nb, rbw, 0, buf0, lrb0, 0, lane, wpatch);
+  if (has_long_segment(H0)) patch_rest<RB>(tile_ptr, Kt, Nb, rbw, kt0, buf0, lrb0, 0, lane, wpatch);
   store_x<XR, TH>(xr, buf0 + BN * LDW, tid);
-  load_x<KTAIL, XR, TH>(xr, xrs, xoff, K, BK, tid);
-  load_ptrs(pa, tile_ptr, Kt, Nb, rbw, 1);
-  load_half<GSH>(H0, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, 1, 0, lane);
-  load_ptrs(pb, tile_ptr, Kt, Nb, rbw, 2);
+  load_x<KTAIL, XR, TH>(xr, xrs, xoff, K, (2 * kt0 + 1) * BK, tid);
+  load_ptrs(pa, tile_ptr, Kt, Nb, rbw, kt0 + 1);
+  load_half<GSH>(H0, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt0 + 1, 0, lane);
+  load_ptrs(pb, tile_ptr, Kt, Nb, rbw, kt0 + 2);
   __syncthreads();
 
-  for (int kt = 0; kt < Kt; ++kt) {
+  for (int kt = kt0; kt < kt1; ++kt) {
     // stage 2 kt (buffer 0) runs; stage 2 kt + 1 (H1: half 1 of tile kt) is prepared in buffer 1
     mfma_stage(acc, buf0, buf0 + BN * LDW, wn, wm, lane);
     write_w<GSH>(H1, buf1, dummy, lrb0, 1, lane, vmask, vmask4, vmagic);
@@ -319,13 +352,88 @@ __global__ __launch_bounds__(Cfg<NWM>::kThreads, 1) void k_gemm(const uint4* __r
     if (long0) patch_rest<RB>(tile_ptr, Kt, Nb, rbw, kt + 1, buf0, lrb0, 0, lane, wpatch);
     __syncthreads();
   }
+  } else {
+    // Ring of PD register sets: before stage s runs, set (s - sb + 1 + i) % PD
+    // holds stage s + 1 + i (i < PD), all in flight. Stage s prepares stage
+    // s + 1 from its set and refills that set with stage s + 1 + PD. PD is a
+    // multiple of 4, so within the unrolled body every set index, tile half
+    // and segment-bounds slot is a constant. The two slots of segment bounds
+    // hold the tiles of even / odd index (from kt0); a slot is reloaded, two
+    // tiles ahead, right after its tile's second half was requested.
+    constexpr int PD = C::kPd;
+    static_assert(PD == 4 || PD == 8, "ring depth");
+    const int sb = 2 * kt0, se = 2 * kt1;   // the split's stages
+    HalfRegs<RB> H[PD];
+    TilePtrs<RB> Pr[2];
+    uint4 xq[PD][XR];
+    load_ptrs(Pr[0], tile_ptr, Kt, Nb, rbw, kt0);
+    load_ptrs(Pr[1], tile_ptr, Kt, Nb, rbw, kt0 + 1);
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      load_x<KTAIL, XR, TH>(xq[u], xrs, xoff, K, (sb + u) * BK, tid);
+      load_half<GSH>(H[u], Pr[(u >> 1) & 1], tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt0 + (u >> 1), u & 1, lane);
+      if (u & 1) load_ptrs(Pr[(u >> 1) & 1], tile_ptr, Kt, Nb, rbw, kt0 + (u >> 1) + 2);
+    }
+    write_w<GSH>(H[0], buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
+    if (has_long_segment(H[0])) patch_rest<RB>(tile_ptr, Kt, Nb, rbw, kt0, buf0, lrb0, 0, lane, wpatch);
+    store_x<XR, TH>(xq[0], buf0 + BN * LDW, tid);
+    load_x<KTAIL, XR, TH>(xq[0], xrs, xoff, K, (sb + PD) * BK, tid);
+    load_half<GSH>(H[0], Pr[(PD >> 1) & 1], tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt0 + PD / 2, 0, lane);
+    __syncthreads();
+
+    // stage s of the ring (U = (s - sb) % PD, a constant)
+    auto stage = [&](auto uc, int s) {
+      constexpr int u = decltype(uc)::value;
+      _Float16* const cur = (u & 1) ? buf1 : buf0;
+      _Float16* const nxt = (u & 1) ? buf0 : buf1;
+      constexpr int v = (u + 1) % PD, h = (u + 1) & 1, pr = ((u + 1 + PD) >> 1) & 1;
+      const int kl = kt0 + ((s + 1 + PD - sb) >> 1);   // tile of the stage requested now
+      mfma_stage(acc, cur, cur + BN * LDW, wn, wm, lane);
+      write_w<GSH>(H[v], nxt, dummy, lrb0, h, lane, vmask, vmask4, vmagic);
+      store_x<XR, TH>(xq[v], nxt + BN * LDW, tid);
+      load_x<KTAIL, XR, TH>(xq[v], xrs, xoff, K, (s + 1 + PD) * BK, tid);
+      const bool lng = has_long_segment(H[v]);
+      load_half<GSH>(H[v], Pr[pr], tiles, scales, sstride, wpatch, Kt, Nb, rbw, kl, h, lane);
+      if (h) load_ptrs(Pr[pr], tile_ptr, Kt, Nb, rbw, kl + 2);
+      if (lng) patch_rest<RB>(tile_ptr, Kt, Nb, rbw, kt0 + ((s + 1 - sb) >> 1), nxt, lrb0, h, lane, wpatch);
+      __syncthreads();
+    };
+    // Whole turns of the ring run unguarded: a guard would let the compiler
+    // assume a path on which the later stages' loads were not issued and wait
+    // for the loads of the ring's next set too early.
+    int s0 = sb;
+    for (; s0 + PD <= se; s0 += PD) {
+      stage(std::integral_constant<int, 0>{}, s0);
+      stage(std::integral_constant<int, 1>{}, s0 + 1);
+      stage(std::integral_constant<int, 2>{}, s0 + 2);
+      stage(std::integral_constant<int, 3>{}, s0 + 3);
+      if constexpr (PD == 8) {
+        stage(std::integral_constant<int, 4>{}, s0 + 4);
+        stage(std::integral_constant<int, 5>{}, s0 + 5);
+        stage(std::integral_constant<int, 6>{}, s0 + 6);
+        stage(std::integral_constant<int, 7>{}, s0 + 7);
+      }
+    }
+    // the rest (fewer than PD stages; the same in every wave)
+    if (s0 < se) stage(std::integral_constant<int, 0>{}, s0);
+    if (s0 + 1 < se) stage(std::integral_constant<int, 1>{}, s0 + 1);
+    if (s0 + 2 < se) stage(std::integral_constant<int, 2>{}, s0 + 2);
+    if constexpr (PD == 8) {
+      if (s0 + 3 < se) stage(std::integral_constant<int, 3>{}, s0 + 3);
+      if (s0 + 4 < se) stage(std::integral_constant<int, 4>{}, s0 + 4);
+      if (s0 + 5 < se) stage(std::integral_constant<int, 5>{}, s0 + 5);
+      if (s0 + 6 < se) stage(std::integral_constant<int, 6>{}, s0 + 6);
+    }
+  }
 
   // Epilogue: register v of lane l holds D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32]
-  // of each 32x32 block (rows = output features, columns = tokens).
-  const int nbase = rb0 * kRowsPerBlock + 128 * wn + 4 * (lane >> 5);
+  // of each 32x32 block (rows = output features, columns = tokens). With
+  // split-K the fp32 sums go to this split's slice of the workspace.
+  const int nbase = rb0 * kRowsPerBlock + 32 * IB * wn + 4 * (lane >> 5);
   const int mbase = m0 + 32 * JB * wm + (lane & 31);
+  float* const pslice = part ? part + (int64_t)blockIdx.y * M * N : nullptr;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < IB; ++i) {
 #pragma unroll
     for (int j = 0; j < JB; ++j) {
       const int m = mbase + 32 * j;
@@ -335,37 +443,104 @@ __global__ __launch_bounds__(Cfg<NWM>::kThreads, 1) void k_gemm(const uint4* __r
         const int n0 = nbase + 32 * i + 8 * q;
         if (n0 >= N) continue;
         const float4_t s = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        store4(Y + (int64_t)m * N + n0, s, N - n0, (N & 3) == 0);
+        if (pslice) {
+          float* dst = pslice + (int64_t)m * N + n0;
+          if ((N & 3) == 0 && n0 + 4 <= N) {
+            *reinterpret_cast<float4_t*>(dst) = s;
+          } else {
+            for (int c = 0; c < 4 && n0 + c < N; ++c) dst[c] = s[c];
+          }
+        } else {
+          store4(Y + (int64_t)m * N + n0, s, N - n0, (N & 3) == 0);
+        }
       }
     }
   }
 }
 
-template <int GSH, bool KTAIL, int NWM>
+// Split-K reduction: Y = fp16(sum of the S partial slices), the slices added
+// in split order (deterministic). One thread per 4 outputs of a token row;
+// the slices are read 8 at a time so the loads overlap.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, uint16_t* __restrict__ Y,
+                                                       int M, int N, int S) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // quad index
+  const int nq = (N + 3) / 4;
+  if (q >= (int64_t)M * nq) return;
+  const int m = (int)(q / nq), n0 = 4 * (int)(q - (int64_t)m * nq);
+  const int64_t slice = (int64_t)M * N;
+  const float* src = part + (int64_t)m * N + n0;
+  float4_t sum = {0.f, 0.f, 0.f, 0.f};
+  if ((N & 3) == 0) {
+    int sp = 0;
+    for (; sp + 8 <= S; sp += 8) {
+      float4_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4_t*>(src + (sp + u) * slice);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; sp < S; ++sp) sum += *reinterpret_cast<const float4_t*>(src + sp * slice);
+  } else {
+    const int w = min(4, N - n0);
+    for (int sp = 0; sp < S; ++sp)
+      for (int c = 0; c < w; ++c) sum[c] += src[sp * slice + c];
+  }
+  store4(Y + (int64_t)m * N + n0, sum, N - n0, (N & 3) == 0);
+}
+
+template <int GSH, bool KTAIL, class C>
 hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
+  constexpr int BM = C::kBM;
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<GSH, KTAIL, NWM>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<GSH, KTAIL, C>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int NT = (int)((p->Nb + (BN / kRowsPerBlock) - 1) / (BN / kRowsPerBlock));
   const int MT = (int)((M + BM - 1) / BM);
   const int T = NT * MT;
-  k_gemm<GSH, KTAIL, NWM><<<dim3((unsigned)T), dim3(Cfg<NWM>::kThreads), kLdsBytes, s>>>(
-      reinterpret_cast<const uint4*>(p->tiles), p->scales, p->sstride, p->tile_ptr, p->wpatch, X, Y, (int)M,
-      (int)p->N, (int)p->K, (int)p->Kt, (int)p->Nb, NT, T);
-  return hipGetLastError();
+  const int Kt = (int)p->Kt;
+  // Split K when the output tiles cannot fill the chip's 256 CUs: about one
+  // round of workgroups, at least 2 code tiles per split.
+  int S = 1;
+  if (T < kSplitTarget) S = std::max(1, std::min(kSplitTarget / T, Kt / 2));
+  const int per = (Kt + S - 1) / S;
+  S = (Kt + per - 1) / per;
+  float* part = nullptr;
+  if (S > 1) {
+    const hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&part), (size_t)S * M * p->N * sizeof(float), s);
+    if (e != hipSuccess) return e;
+  }
+  k_gemm<GSH, KTAIL, C><<<dim3((unsigned)T, (unsigned)S), dim3(C::kThreads), C::kLdsBytes, s>>>(
+      reinterpret_cast<const uint4*>(p->tiles), p->scales, p->sstride, p->tile_ptr, p->wpatch, X, Y, part, (int)M,
+      (int)p->N, (int)p->K, Kt, (int)p->Nb, NT, T, per);
+  hipError_t e = hipGetLastError();
+  if (S > 1) {
+    if (e == hipSuccess) {
+      const int64_t quads = M * ((p->N + 3) / 4);
+      k_splitk_reduce<<<dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s>>>(part, Y, (int)M, (int)p->N, S);
+      e = hipGetLastError();
+    }
+    const hipError_t f = hipFreeAsync(part, s);
+    if (e == hipSuccess) e = f;
+  }
+  return e;
 }
 
 }  // namespace
 
+template <bool KTAIL, class C>
+hipError_t launch_g(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
+  if (p->G == 128) return launch<0, KTAIL, C>(p, X, M, Y, s);
+  if (p->G == 64) return launch<1, KTAIL, C>(p, X, M, Y, s);
+  return launch<2, KTAIL, C>(p, X, M, Y, s);
+}
+
 template <bool KTAIL>
 hipError_t launch_k(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
-  if (p->G == 128) return launch<0, KTAIL, kGemmNwm>(p, X, M, Y, s);
-  if (p->G == 64) return launch<1, KTAIL, kGemmNwm>(p, X, M, Y, s);
-  return launch<2, KTAIL, kGemmNwm>(p, X, M, Y, s);
+  return M <= kNarrowMaxM ? launch_g<KTAIL, CfgNarrow>(p, X, M, Y, s) : launch_g<KTAIL, CfgWide>(p, X, M, Y, s);
 }
 
 hipError_t launch_gemm(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {

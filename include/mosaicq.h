@@ -83,8 +83,15 @@ mq_status mq_pack(const void* W_dev_fp16, int64_t N, int64_t K, int32_t group_si
  *   Y_dev_fp16   [M, N] fp16 output (device, caller-owned, fully overwritten)
  *   hip_stream   stream to enqueue on; the call returns without synchronising
  *
- * Small M (decode) runs a GEMV-style kernel that streams the 4-bit tiles from
- * HBM; large M (prefill) runs an MFMA GEMM. Both are deterministic.
+ * Up to 16 tokens (decode) a GEMV-style kernel streams the 4-bit tiles from
+ * HBM; above that an MFMA GEMM runs. Both are deterministic. When the GEMM's
+ * output tiles are too few to fill the GPU (M times N small against K), it
+ * splits K: the parts write fp32 partial sums to a workspace that the call
+ * takes from the stream-ordered allocator (hipMallocAsync / hipFreeAsync on
+ * hip_stream, so it also works under stream capture, where it becomes a
+ * graph allocation), and a second kernel adds the parts in a fixed order.
+ * The workspace holds at most 256 x 256 x 256 fp32 values (64 MiB); if it
+ * cannot be allocated the call returns MQ_ERR_OUT_OF_MEMORY.
  */
 mq_status mq_linear(const void* X_dev_fp16, int64_t M, const mq_packed* p,
                     void* Y_dev_fp16, void* hip_stream);

@@ -122,3 +122,35 @@ def test_linear_argument_errors(mq):
     with pytest.raises(mq.MQError):
         mq.mq_linear(X[:1], p)
     assert torch.cuda.is_available()
+
+
+@pytest.mark.parametrize("M,kern", [(4, 1), (16, 1), (64, 2), (130, 2), (600, 2)])
+def test_linear_in_graph_replays_match_eager(mq, M, kern):
+    """The kernels captured in a graph (the split-K GEMM included: its
+    workspace becomes a graph allocation) give the eager result on every
+    replay, with other work and synchronisations between the replays."""
+    import torch
+    N, K = 1536, 1024
+    W = _layer(N, K, seed=11)
+    p = mq.mq_pack(to_dev(W), 128, 0.01)
+    Xd = to_dev(_x(M, K, seed=M))
+    ref = mq.mq_linear_with(Xd, p, kern).cpu().numpy()
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        mq.mq_linear_with(Xd, p, kern, Y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mq.mq_linear_with(Xd, p, kern, Y)
+    for rep in range(3):
+        Y.fill_(1.0)
+        junk = mq.mq_linear_with(Xd, p, kern)        # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[graph replay] M={M} kernel={kern} replay={rep}", flush=True)
+        assert np.array_equal(Y.cpu().numpy().view(np.uint16), ref.view(np.uint16))
+        assert np.array_equal(junk.cpu().numpy().view(np.uint16), ref.view(np.uint16))
