@@ -519,9 +519,7 @@ hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y,
   hipError_t e = hipGetLastError();
   if (S > 1) {
     if (e == hipSuccess) {
-      const int64_t quads = M * ((p->N + 3) / 4);
-      k_splitk_reduce<<<dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s>>>(part, Y, (int)M, (int)p->N, S);
-      e = hipGetLastError();
+      e = launch_splitk_reduce(part, Y, M, p->N, S, s);
     }
     const hipError_t f = hipFreeAsync(part, s);
     if (e == hipSuccess) e = f;
@@ -541,6 +539,12 @@ hipError_t launch_g(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* 
 template <bool KTAIL>
 hipError_t launch_k(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
   return M <= kNarrowMaxM ? launch_g<KTAIL, CfgNarrow>(p, X, M, Y, s) : launch_g<KTAIL, CfgWide>(p, X, M, Y, s);
+}
+
+hipError_t launch_splitk_reduce(const float* part, uint16_t* Y, int64_t M, int64_t N, int S, hipStream_t s) {
+  const int64_t quads = M * ((N + 3) / 4);
+  k_splitk_reduce<<<dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s>>>(part, Y, (int)M, (int)N, S);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {

@@ -104,6 +104,80 @@ __device__ __forceinline__ void tile_mma(float4_t (&acc)[MB], const uint4 code, 
   }
 }
 
+// Everything one code tile needs, loaded ahead of its use by the general
+// decode loop: the lane's 16 bytes of codes, the scales of its 4 rows, and the
+// X fragments of every token block (zero for padded 32-column segments). No
+// value is touched after its load (rows past N read the last row's scales and
+// feed outputs that are never stored), so the loads stay in flight until the
+// tile is computed.
+template <int MB, int NS>
+struct TileIn {
+  uint4 code;
+  TileScales<NS> S;
+  half8_t bx[MB][4];
+};
+
+template <int MB, int NS, bool XLDS>
+__device__ __forceinline__ void load_tile_in(TileIn<MB, NS>& T, const uint4* __restrict__ tiles, int64_t tbase,
+                                             const uint16_t* __restrict__ scales, const int (&srow)[4],
+                                             const uint16_t* __restrict__ X, const uint16_t* xs,
+                                             const int (&mrow)[MB], int K, int ldx, int kt, int lane, int g) {
+  T.code = tiles[(tbase + kt) * 64 + lane];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int si = srow[i] + kt * NS;
+    if (NS == 1) {
+      T.S.lo[i] = scales[si];
+    } else if (NS == 2) {
+      T.S.lo[i] = *reinterpret_cast<const uint32_t*>(scales + si);
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(scales + si);
+      T.S.lo[i] = v.x;
+      T.S.hi[i] = v.y;
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int seg = kt * kTileCols + 32 * s4;
+      if (seg >= K)   // padded 32-column segment (uniform branch)
+        T.bx[mb][s4] = as_half8(make_uint4(0u, 0u, 0u, 0u));
+      else if (XLDS)
+        T.bx[mb][s4] = *reinterpret_cast<const half8_t*>(xs + mrow[mb] * ldx + seg + 8 * g);
+      else
+        T.bx[mb][s4] = as_half8(*reinterpret_cast<const uint4*>(X + (int64_t)mrow[mb] * K + seg + 8 * g));
+    }
+  }
+}
+
+// tile_mma on a prefetched tile
+template <int MB, int NS>
+__device__ __forceinline__ void tile_mma_in(float4_t (&acc)[MB], const TileIn<MB, NS>& T, uint32_t vmask,
+                                            uint32_t vmask4, uint32_t vmagic) {
+  constexpr int SPG = 4 / NS;
+  half8_t a[4];
+  a[0] = widen_q(T.code.x, vmask, vmask4, vmagic);
+  a[1] = widen_q(T.code.y, vmask, vmask4, vmagic);
+  a[2] = widen_q(T.code.z, vmask, vmask4, vmagic);
+  a[3] = widen_q(T.code.w, vmask, vmask4, vmagic);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int grp = 0; grp < NS; ++grp) {
+      float4_t tacc = mfma16(a[grp * SPG], T.bx[mb][grp * SPG], float4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int s4 = grp * SPG + 1; s4 < (grp + 1) * SPG; ++s4) tacc = mfma16(a[s4], T.bx[mb][s4], tacc);
+      const int sh = 16 * (grp & 1);
+      const uint32_t* w = (grp >= 2) ? T.S.hi : T.S.lo;
+      acc[mb].x = fmaf(h_to_f((w[0] >> sh) & 0xFFFFu), tacc.x, acc[mb].x);
+      acc[mb].y = fmaf(h_to_f((w[1] >> sh) & 0xFFFFu), tacc.y, acc[mb].y);
+      acc[mb].z = fmaf(h_to_f((w[2] >> sh) & 0xFFFFu), tacc.z, acc[mb].z);
+      acc[mb].w = fmaf(h_to_f((w[3] >> sh) & 0xFFFFu), tacc.w, acc[mb].w);
+    }
+  }
+}
+
 // One residual chunk of 32 entries (8 per lane): an MFMA whose A is one-hot
 // by output row and carries the fp16 residual values, B the X columns the
 // entries name. `first` is the stream index of the chunk's first entry
@@ -561,12 +635,27 @@ __global__ __launch_bounds__(64 * KS) __attribute__((amdgpu_waves_per_eu(KS == 8
       tile_mma<MB, NS, XLDS, false>(acc, code[t], S[t], X, xs, mrow, K, LDX, kt0 + t, g, vmask, vmask4, vmagic);
     }
   } else {
-    for (int kt = kt0; kt < kt1; ++kt) {
-      const uint4 c1 = tiles[(tbase + kt) * 64 + lane];
-      TileScales<NS> s1;
-      load_scales<NS>(s1, scales, srow, rowok, kt);
-      tile_mma<MB, NS, XLDS, true>(acc, c1, s1, X, xs, mrow, K, LDX, kt, g, vmask, vmask4, vmagic);
+    // a ring of PDG register sets, each loaded PDG tiles ahead of its use;
+    // the loop body takes PDG tiles and has no branch (a guarded refill would
+    // make the compiler wait for the other sets' loads); the last tiles follow
+    constexpr int PDG = MB == 1 ? 4 : MB == 2 ? 2 : 1;   // four token blocks: no room for a second set
+    TileIn<MB, NS> T[PDG];
+    const int last = Kt - 1;
+#pragma unroll
+    for (int u = 0; u < PDG; ++u)
+      load_tile_in<MB, NS, XLDS>(T[u], tiles, tbase, scales, srow, X, xs, mrow, K, LDX, min(kt0 + u, last), lane, g);
+    int kt = kt0;
+    for (; kt + PDG <= kt1; kt += PDG) {
+#pragma unroll
+      for (int u = 0; u < PDG; ++u) {
+        tile_mma_in<MB, NS>(acc, T[u], vmask, vmask4, vmagic);
+        load_tile_in<MB, NS, XLDS>(T[u], tiles, tbase, scales, srow, X, xs, mrow, K, LDX, min(kt + PDG + u, last),
+                                   lane, g);
+      }
     }
+#pragma unroll
+    for (int u = 0; u < PDG - 1; ++u)
+      if (kt + u < kt1) tile_mma_in<MB, NS>(acc, T[u], vmask, vmask4, vmagic);
   }
 
   // ---- residual: chunks wave, wave + KS, ... of the row block's entries

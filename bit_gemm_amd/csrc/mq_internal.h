@@ -85,6 +85,10 @@ hipError_t launch_gemm(const mq_packed* p, const uint16_t* X, int64_t M, uint16_
 // canonical CSR, for the unfused comparison.
 hipError_t launch_residual(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
 
+// Y = fp16(sum of the S fp32 slices part[S][M][N]), slices added in order
+// (gemm.hip); used by the kernels that split K.
+hipError_t launch_splitk_reduce(const float* part, uint16_t* Y, int64_t M, int64_t N, int S, hipStream_t stream);
+
 constexpr int64_t kGemvMaxM = 64;       // the GEMV kernels accept up to 64 tokens
 constexpr int64_t kAutoGemvMaxM = 16;   // the automatic choice takes them up to 16
 

@@ -27,7 +27,7 @@ def _x(M, K, seed):
 
 
 SHAPES = [(16, 128, 128, 0.05), (17, 96, 32, 0.1), (100, 640, 64, 0.02), (257, 1024, 128, 0.01),
-          (130, 4224, 128, 0.004)]
+          (130, 4224, 128, 0.004), (40, 4160, 64, 0.01), (24, 8256, 32, 0.02), (70, 12288, 128, 0.003)]
 BATCH = [1, 3, 16, 17, 33, 64, 65, 130]
 
 
