@@ -190,13 +190,14 @@ __device__ __forceinline__ void res_chunk(float4_t (&acc)[MB], const uint4 v0, c
   const uint32_t e[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
   int col[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    int wb = 0;
-    if (MW) {   // column window of the entry: count window starts at or below it
-      const uint32_t idx = first + 8 * g + u;
-      for (int w = 1; w < nwin; ++w) wb += (idx >= rtp[32 * w]) ? kColWindow : 0;
+  for (int u = 0; u < 8; ++u) col[u] = (int)ent_col(e[u]);
+  if (MW) {   // column window of each entry: count the window starts at or below its stream index
+    const uint32_t idx = first + 8 * g;
+    for (int w = 1; w < nwin; ++w) {
+      const uint32_t ws = rtp[32 * w];   // one load per window, shared by the 8 entries
+#pragma unroll
+      for (int u = 0; u < 8; ++u) col[u] += (idx + u >= ws) ? kColWindow : 0;
     }
-    col[u] = wb + (int)ent_col(e[u]);
   }
   u32x4_t av;
 #pragma unroll
@@ -222,6 +223,45 @@ __device__ __forceinline__ void res_chunk(float4_t (&acc)[MB], const uint4 v0, c
       bv[u >> 1] = lo | (hi << 16);
     }
     acc[mb] = mfma16(a, __builtin_bit_cast(half8_t, bv), acc[mb]);
+  }
+}
+
+// Chunks c0, c0 + KS, c0 + 2 KS, ... (< nch) of a row block's residual
+// stream (chunk c starts at stream index E0 + 32 c), with the entries of
+// RD chunks in flight: a dense residual gives a wave many chunks, and
+// loading each only when the previous one is done would expose the memory
+// latency once per chunk. Chunks past nch read the zero entries after the
+// stream, which add nothing; the chunks are added in the same order as one
+// at a time.
+template <int MB, bool XLDS, bool MW, int KS>
+__device__ __forceinline__ void res_rest(float4_t (&acc)[MB], const uint32_t* __restrict__ entries, uint32_t E0,
+                                         uint32_t c0, uint32_t nch, int zero_off, const uint32_t* __restrict__ rtp,
+                                         int nwin, const uint16_t* __restrict__ X, const uint16_t* xs,
+                                         const int (&mrow)[MB], int K, int ldx, int r, int g) {
+  if (c0 >= nch) return;   // the same in every lane
+  constexpr int RD = MB >= 4 ? 2 : 4;   // four token blocks leave room for two
+  uint4 e[RD][2];
+#pragma unroll
+  for (int k = 0; k < RD; ++k) {
+    const uint32_t c = c0 + (uint32_t)(k * KS);
+    const uint4* e4 = reinterpret_cast<const uint4*>((c < nch ? entries + E0 + kChunk * c : entries + zero_off) + 8 * g);
+    e[k][0] = e4[0];
+    e[k][1] = e4[1];
+  }
+  for (uint32_t c = c0; c < nch; c += RD * KS) {
+#pragma unroll
+    for (int k = 0; k < RD; ++k) {
+      const uint32_t ck = c + (uint32_t)(k * KS);
+      // zero chunks cost little with X in LDS; with X in global memory or
+      // several windows they are skipped
+      if ((XLDS && !MW) || ck < nch)
+        res_chunk<MB, XLDS, MW>(acc, e[k][0], e[k][1], E0 + kChunk * ck, rtp, nwin, X, xs, mrow, K, ldx, r, g);
+      const uint32_t cn = ck + (uint32_t)(RD * KS);
+      const uint4* e4 =
+          reinterpret_cast<const uint4*>((cn < nch ? entries + E0 + kChunk * cn : entries + zero_off) + 8 * g);
+      e[k][0] = e4[0];
+      e[k][1] = e4[1];
+    }
   }
 }
 
@@ -381,10 +421,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
   }
   tile(2);
   tile(3);
-  for (uint32_t c = (uint32_t)(wave + 2 * KS); c < nchunks; c += KS) {
-    const uint4* e4 = reinterpret_cast<const uint4*>(entries + E0 + kChunk * c + 8 * g);
-    res_chunk<1, true, false>(acc, e4[0], e4[1], E0 + kChunk * c, tile_ptr + tbase, 1, X, xs, mrow, K, LDX, r, g);
-  }
+  res_rest<1, true, false, KS>(acc, entries, E0, (uint32_t)(wave + 2 * KS), nchunks, zero_off, tile_ptr + tbase, 1, X,
+                               xs, mrow, K, LDX, r, g);
 
   red[wave][lane] = acc[0];
   __syncthreads();
@@ -411,8 +449,8 @@ __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles,
                                                const uint32_t* __restrict__ entries, const uint16_t* __restrict__ X,
                                                uint16_t* __restrict__ Y, int M, int N, int Nb, int zero_off) {
   constexpr int KS = 8, TPW = 4, K = 4096, Kt = 32, NS = 1 << GSH, LDX = K + kXPad;
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][LDX]
-  __shared__ float4_t red[R][KS][64];
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][LDX], then the partials [R][KS][64]
+  static_assert(R * KS * 64 * sizeof(float4_t) <= XR * LDX * sizeof(uint16_t), "partials fit in the X space");
   const int rb0 = blockIdx.x * R;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
@@ -484,6 +522,7 @@ __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles,
 
   uint32_t vmask = 0x000F000Fu, vmask4 = 0x00F000F0u, vmagic = 0x64006400u;
   asm volatile("" : "+v"(vmask), "+v"(vmask4), "+v"(vmagic));   // keep the constants in VGPRs for v_and_or_b32
+  float4_t part[R];
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const int rb = min(rb0 + j, Nb - 1);
@@ -513,18 +552,21 @@ __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles,
       else
         asm volatile("" ::"v"(ent[j][h][0].x), "v"(ent[j][h][1].x));
     }
-    for (uint32_t c = (uint32_t)(wave + 2 * KS); c < nch[j]; c += KS) {
-      const uint4* e4 = reinterpret_cast<const uint4*>(entries + E0[j] + kChunk * c + 8 * g);
-      res_chunk<1, true, false>(acc, e4[0], e4[1], E0[j] + kChunk * c, rtp, 1, X, xs, mrow, K, LDX, r, g);
-    }
-    red[j][wave][lane] = acc[0];
+    res_rest<1, true, false, KS>(acc, entries, E0[j], (uint32_t)(wave + 2 * KS), nch[j], zero_off, rtp, 1, X, xs, mrow,
+                                 K, LDX, r, g);
+    part[j] = acc[0];
   }
+  // the partials go where X was, once every wave is done with X
+  float4_t* red = reinterpret_cast<float4_t*>(xs);   // [R][KS][64]
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < R; ++j) red[(j * KS + wave) * 64 + lane] = part[j];
   __syncthreads();
   if (wave < R && live[wave]) {   // wave j sums row block j
     const int j = wave, rb = rb0 + j;
-    float4_t sum = red[j][0][lane];
+    float4_t sum = red[(j * KS) * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < KS; ++w) sum += red[j][w][lane];
+    for (int w = 1; w < KS; ++w) sum += red[(j * KS + w) * 64 + lane];
     const int n0 = rb * kRowsPerBlock + 4 * g;
     if (r < M) store4(Y + (int64_t)r * N + n0, sum, N - n0, (N & 3) == 0);
   }
@@ -662,10 +704,8 @@ __global__ __launch_bounds__(64 * KS) __attribute__((amdgpu_waves_per_eu(KS == 8
   res_chunk<MB, XLDS, MW>(acc, ent[0][0], ent[0][1], E0 + kChunk * wave, tile_ptr + tbase, nwin, X, xs, mrow, K, LDX, r, g);
   res_chunk<MB, XLDS, MW>(acc, ent[1][0], ent[1][1], E0 + kChunk * (wave + KS), tile_ptr + tbase, nwin, X, xs, mrow, K,
                           LDX, r, g);
-  for (uint32_t c = (uint32_t)(wave + 2 * KS); c < nchunks; c += KS) {
-    const uint4* e4 = reinterpret_cast<const uint4*>(entries + E0 + kChunk * c + 8 * g);
-    res_chunk<MB, XLDS, MW>(acc, e4[0], e4[1], E0 + kChunk * c, tile_ptr + tbase, nwin, X, xs, mrow, K, LDX, r, g);
-  }
+  res_rest<MB, XLDS, MW, KS>(acc, entries, E0, (uint32_t)(wave + 2 * KS), nchunks, zero_off, tile_ptr + tbase, nwin, X,
+                             xs, mrow, K, LDX, r, g);
 
   // ---- fixed-order sum of the KS partial tiles, fp16 output
 #pragma unroll
@@ -712,8 +752,7 @@ hipError_t launch_r(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, h
   static bool done = false;
   if (!done) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_r<GSH, XR, R>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)(kLdsMaxBytes - R * 8 * 64 * sizeof(float4_t)));
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMaxBytes);
     if (e != hipSuccess) return e;
     done = true;
   }
@@ -724,15 +763,20 @@ hipError_t launch_r(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, h
   return hipGetLastError();
 }
 
-// row blocks per workgroup so that one wave of workgroups covers the layer
-// (G = 32 keeps 4 scales per tile and row: at most 2 row blocks fit the registers)
+// Row blocks per workgroup: X fills the LDS, so one workgroup runs per CU,
+// and ceil(Nb / 256) row blocks each make one round of workgroups (a few
+// workgroups past 256 would take a second round on their own). Up to 4 row
+// blocks fit the registers, 2 when G = 32 (4 scales per tile and row).
 template <int GSH, int XR>
 hipError_t launch_r_any(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
   if (p->Nb <= 256) return launch_r<GSH, XR, 1>(p, X, M, Y, s);
-  if constexpr (GSH < 2) {
-    if (p->Nb > 512) return launch_r<GSH, XR, 3>(p, X, M, Y, s);
+  if constexpr (GSH == 2) {
+    return launch_r<GSH, XR, 2>(p, X, M, Y, s);
+  } else {
+    if (p->Nb <= 512) return launch_r<GSH, XR, 2>(p, X, M, Y, s);
+    if (p->Nb <= 768) return launch_r<GSH, XR, 3>(p, X, M, Y, s);
+    return launch_r<GSH, XR, 4>(p, X, M, Y, s);
   }
-  return launch_r<GSH, XR, 2>(p, X, M, Y, s);
 }
 
 // XL: X copied whole into LDS ([M][K + kXPad], at most kXldsMax bytes)
