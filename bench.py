@@ -336,8 +336,8 @@ def bench_block(args, mq, synth, torch):
 def bench_sweep(args, mq, synth, torch):
     """The 14336x4096 residual sweep: for each outlier placement, the layer
     packed at rho = 0 and at each density; mq_pack timed on its own (GPU
-    events) and the linear at M = 1, 64 (rotated copies, graph replay) and
-    512 (event loop); t(rho) / t(0) per M."""
+    events) and the linear at M = 1, 64 and 512 (rotated copies, graph
+    replay); t(rho) / t(0) per M."""
     out = {}
     for mode, _ in synth.SWEEP_MODES:
         layer0 = synth.sweep_layer(mode, 0.0)
@@ -355,16 +355,12 @@ def bench_sweep(args, mq, synth, torch):
             ncopy = max(2, math.ceil(2 * MALL_BYTES / p.device_bytes))
             copies = [p] + [mq.mq_pack(W, layer0.group, rho) for _ in range(ncopy - 1)]
             for M in synth.SWEEP_BATCH:
-                if M <= 64:   # small batches: graph replays over rotated copies (cold weights)
-                    def one(i, M=M):
-                        mq.mq_linear(Xs[M], copies[i % ncopy], Ys[M])
-                    us = replay_spread(torch, one, max(2, args.warmup // 4), max(20, args.steps // 4), reps=5)[0] * 1e3
-                else:
-                    def big(i, M=M):
-                        mq.mq_linear(Xs[M], p, Ys[M])
-                    time_events(big, 2)
-                    n = max(3, min(args.steps, 20))
-                    us = time_events(big, n) / n * 1e3
+                # graph replays over the rotated copies (cold weights); fewer
+                # launches per graph at M = 512, where one takes ~0.1 ms
+                def one(i, M=M):
+                    mq.mq_linear(Xs[M], copies[i % ncopy], Ys[M])
+                steps = max(20, args.steps // 4) if M <= 64 else 20
+                us = replay_spread(torch, one, max(2, args.warmup // 4), steps, reps=5)[0] * 1e3
                 entry["us"][str(M)] = round(us, 2)
             for c in copies:
                 c.free()
