@@ -34,7 +34,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 void release(mq_packed* p) {
-  void* bufs[] = {p->tiles, p->scales, p->row_ptr, p->col, p->rcodes, p->rscale, p->tile_ptr, p->entries, p->wpatch};
+  void* bufs[] = {p->tiles,    p->scales,  p->row_ptr, p->col, p->rcodes, p->rscale,
+                  p->tile_ptr, p->entries, p->wpatch,  p->blk, p->bscale, p->bcodes};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   p->magic = 0;
@@ -167,6 +168,115 @@ static mq_status linear_impl(const void* X, int64_t M, const mq_packed* p, void*
   return from_hip(e);
 }
 
+MQ_API mq_status mq_pack_blocks(const void* W_dev_fp16, int64_t N, int64_t K, int32_t group_size,
+                                double block_fraction, const float* h_dev_f32, void* hip_stream, mq_packed** out) {
+  if (out) *out = nullptr;
+  if (!W_dev_fp16 || !h_dev_f32 || !out) return MQ_ERR_INVALID_ARG;
+  if (N <= 0 || K <= 0) return MQ_ERR_INVALID_ARG;
+  if (!(block_fraction >= 0.0 && block_fraction <= 1.0)) return MQ_ERR_INVALID_ARG;   // NaN fails too
+  if (group_size != 32 && group_size != 64 && group_size != 128) return MQ_ERR_UNSUPPORTED;
+  if (K % group_size != 0) return MQ_ERR_INVALID_ARG;
+  if (K > 65536) return MQ_ERR_UNSUPPORTED;
+  if (N >= (int64_t(1) << 31) / K) return MQ_ERR_UNSUPPORTED;   // N * K < 2^31
+  if ((reinterpret_cast<uintptr_t>(W_dev_fp16) & 15u) != 0 || (reinterpret_cast<uintptr_t>(h_dev_f32) & 3u) != 0)
+    return MQ_ERR_INVALID_ARG;
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return MQ_ERR_DEVICE;
+  mq_packed* p = new (std::nothrow) mq_packed();
+  if (!p) return MQ_ERR_OUT_OF_MEMORY;
+  std::memset(p, 0, sizeof(*p));
+  p->N = N;
+  p->K = K;
+  p->G = group_size;
+  p->rho = block_fraction;
+  p->Nb = ceil_div(N, mq::kRowsPerBlock);
+  p->Kt = ceil_div(K, mq::kTileCols);
+  p->sstride = round_up(p->Kt * mq::kTileCols / group_size, 8);
+  p->device = dev;
+  p->blocks = 1;
+  const int64_t nblocks = p->Nb * p->Kt;
+  int64_t nsel = (int64_t)std::floor(block_fraction * (double)nblocks);   // one float64 product, then floor
+  if (nsel > nblocks) nsel = nblocks;
+  p->nblk = nsel;
+  // every entry of a selected block may carry a nonzero code; row blocks pad to 32 entries
+  p->stream_cap = nsel * mq::kRowsPerBlock * mq::kTileCols + (int64_t)(mq::kChunk - 1) * p->Nb;
+
+  const size_t n_tiles = (size_t)nblocks;
+  const size_t sz_ent = (size_t)(p->stream_cap + mq::kEntryPad) * sizeof(uint32_t);
+  const size_t nb1 = (size_t)std::max<int64_t>(nsel, 1);
+  struct {
+    void** dst;
+    size_t n;
+  } allocs[] = {{(void**)&p->tiles, n_tiles * mq::kTileBytes},
+                {(void**)&p->scales, (size_t)(p->Nb * mq::kRowsPerBlock * p->sstride) * sizeof(uint16_t)},
+                {(void**)&p->tile_ptr, (n_tiles + 1) * sizeof(uint32_t)},
+                {(void**)&p->entries, sz_ent},
+                {(void**)&p->wpatch, sz_ent},
+                {(void**)&p->blk, nb1 * sizeof(int32_t)},
+                {(void**)&p->bscale, nb1 * mq::kRowsPerBlock * sizeof(float)},
+                {(void**)&p->bcodes, nb1 * mq::kRowsPerBlock * (mq::kTileCols / 2)}};
+  size_t total = 0;
+  for (auto& a : allocs) {
+    e = hipMalloc(a.dst, a.n);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      release(p);
+      return e == hipErrorOutOfMemory ? MQ_ERR_OUT_OF_MEMORY : MQ_ERR_DEVICE;
+    }
+    total += a.n;
+  }
+  p->bytes = total;
+
+  uint32_t flags = 0;
+  e = mq::pack_blocks_on_device(static_cast<const uint16_t*>(W_dev_fp16), h_dev_f32, p,
+                                static_cast<hipStream_t>(hip_stream), &flags);
+  if (e != hipSuccess) {
+    release(p);
+    return from_hip(e);
+  }
+  mq_status st = MQ_OK;
+  if (flags & mq::kFlagNonFinite) st = MQ_ERR_NONFINITE;
+  else if (flags & mq::kFlagBadHessian) st = MQ_ERR_INVALID_ARG;
+  else if (flags & mq::kFlagScaleOverflow) st = MQ_ERR_UNSUPPORTED;
+  else if (flags & mq::kFlagCountMismatch) st = MQ_ERR_DEVICE;
+  if (st != MQ_OK) {
+    release(p);
+    return st;
+  }
+  p->magic = mq::kMagic;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_live.insert(p);
+  }
+  *out = p;
+  return MQ_OK;
+}
+
+MQ_API mq_status mq_block_count(const mq_packed* p, int64_t* nblk) {
+  if (!is_live(p)) return MQ_ERR_BAD_HANDLE;
+  if (!nblk) return MQ_ERR_INVALID_ARG;
+  *nblk = p->blocks ? p->nblk : -1;
+  return MQ_OK;
+}
+
+MQ_API mq_status mq_export_blocks(const mq_packed* p, void* blk_i32, void* rscale_f32, void* rcodes_u8,
+                                  void* hip_stream) {
+  if (!is_live(p)) return MQ_ERR_BAD_HANDLE;
+  if (!p->blocks) return MQ_ERR_UNSUPPORTED;
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const size_t n = (size_t)p->nblk;
+  hipError_t e = hipSuccess;
+  if (n == 0) return MQ_OK;
+  if (blk_i32) e = hipMemcpyAsync(blk_i32, p->blk, n * sizeof(int32_t), hipMemcpyDefault, s);
+  if (e == hipSuccess && rscale_f32)
+    e = hipMemcpyAsync(rscale_f32, p->bscale, n * mq::kRowsPerBlock * sizeof(float), hipMemcpyDefault, s);
+  if (e == hipSuccess && rcodes_u8)
+    e = hipMemcpyAsync(rcodes_u8, p->bcodes, n * mq::kRowsPerBlock * (mq::kTileCols / 2), hipMemcpyDefault, s);
+  return from_hip(e);
+}
+
 MQ_API mq_status mq_linear(const void* X_dev_fp16, int64_t M, const mq_packed* p, void* Y_dev_fp16,
                            void* hip_stream) {
   return linear_impl(X_dev_fp16, M, p, Y_dev_fp16, hip_stream, MQ_KERNEL_AUTO);
@@ -181,6 +291,7 @@ MQ_API mq_status mq_residual_add(const void* X_dev_fp16, int64_t M, const mq_pac
                                  void* hip_stream) {
   if (!is_live(p)) return MQ_ERR_BAD_HANDLE;
   if (!X_dev_fp16 || !Y_dev_fp16 || M <= 0) return MQ_ERR_INVALID_ARG;
+  if (p->blocks) return MQ_ERR_UNSUPPORTED;   // it reads the element-wise CSR
   if (M > (int64_t(1) << 31) / p->K || M > (int64_t(1) << 31) / p->N) return MQ_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(X_dev_fp16) & 15u) != 0 || (reinterpret_cast<uintptr_t>(Y_dev_fp16) & 1u) != 0)
     return MQ_ERR_INVALID_ARG;
@@ -202,6 +313,7 @@ MQ_API mq_status mq_packed_info(const mq_packed* p, int64_t* N, int64_t* K, int3
 MQ_API mq_status mq_export_canonical(const mq_packed* p, void* codes_u8, void* scales_f16, void* row_ptr_i32,
                                      void* col_u16, void* rcodes_u8, void* rscale_f32, void* hip_stream) {
   if (!is_live(p)) return MQ_ERR_BAD_HANDLE;
+  if (p->blocks && (row_ptr_i32 || col_u16 || rcodes_u8 || rscale_f32)) return MQ_ERR_UNSUPPORTED;
   const hipStream_t s = static_cast<hipStream_t>(hip_stream);
   hipError_t e = hipSuccess;
   if (codes_u8) {

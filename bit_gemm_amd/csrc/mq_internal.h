@@ -31,6 +31,7 @@ struct SelState {
 constexpr uint32_t kFlagNonFinite = 1u;
 constexpr uint32_t kFlagScaleOverflow = 2u;
 constexpr uint32_t kFlagCountMismatch = 4u;
+constexpr uint32_t kFlagBadHessian = 8u;   // a Hessian weight is negative or not finite
 
 constexpr int kDigitBits = 13;                  // radix digit width of the top-k select
 constexpr int kDigitBins = 1 << kDigitBits;
@@ -62,6 +63,12 @@ struct mq_packed {
   int64_t nstream;      // entries in the stream incl. the per-row-block zero padding
   int64_t stream_cap;   // allocated stream length (excluding the trailing zero pad)
   size_t bytes;
+  // block-wise residual (mq_pack_blocks); the CSR fields above are unused then
+  int32_t blocks;       // 1 for a handle from mq_pack_blocks
+  int64_t nblk;         // selected 16 x 128 residual blocks
+  int32_t* blk;         // [nblk] block indices rb * Kt + kt, ascending
+  float* bscale;        // [nblk][16] residual scale of each block row
+  uint8_t* bcodes;      // [nblk][16][64] residual codes u = qr + 8, even column in the low nibble
 };
 
 namespace mq {
@@ -71,6 +78,16 @@ constexpr uint64_t kMagic = 0x4d6f736169635134ull;  // "MosaicQ4"
 // Packing pipeline (pack.hip). Runs every kernel on `stream`; returns the
 // first HIP error. Temporary buffers are allocated and freed inside.
 hipError_t pack_on_device(const uint16_t* W, mq_packed* p, hipStream_t stream, uint32_t* flags_out);
+
+// Block-wise packing (pack_blocks.hip): base as pack_on_device, then the
+// nsel = p->nblk blocks with the largest Hessian-weighted score get their
+// residual. h: [K] fp32 device weights.
+hipError_t pack_blocks_on_device(const uint16_t* W, const float* h, mq_packed* p, hipStream_t stream,
+                                 uint32_t* flags_out);
+
+// Pieces of the element-wise pipeline the block packer reuses (pack.hip).
+hipError_t launch_pack_base(const uint16_t* W, mq_packed* p, SelState* st, hipStream_t stream);
+hipError_t launch_scan_tiles(const uint32_t* tile_cnt, int64_t ntiles, uint32_t* tile_ptr, hipStream_t stream);
 
 // Canonical / tiled export (pack.hip).
 hipError_t export_codes(const mq_packed* p, uint8_t* codes, hipStream_t stream);

@@ -22,7 +22,8 @@ KERNEL_AUTO, KERNEL_GEMV, KERNEL_GEMM = 0, 1, 2
 GEMV_MAX_M = 64
 
 EXPORTED = ("mq_pack", "mq_linear", "mq_linear_with", "mq_residual_add", "mq_packed_info",
-            "mq_export_canonical", "mq_export_tiled", "mq_free", "mq_status_string")
+            "mq_export_canonical", "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks",
+            "mq_free", "mq_status_string")
 
 
 class MQError(RuntimeError):
@@ -51,6 +52,12 @@ def _load():
     lib.mq_export_canonical.restype = ctypes.c_int
     lib.mq_export_tiled.argtypes = [vp] * 5
     lib.mq_export_tiled.restype = ctypes.c_int
+    lib.mq_pack_blocks.argtypes = [vp, i64, i64, i32, ctypes.c_double, vp, vp, ctypes.POINTER(vp)]
+    lib.mq_pack_blocks.restype = ctypes.c_int
+    lib.mq_block_count.argtypes = [vp, ctypes.POINTER(i64)]
+    lib.mq_block_count.restype = ctypes.c_int
+    lib.mq_export_blocks.argtypes = [vp] * 5
+    lib.mq_export_blocks.restype = ctypes.c_int
     lib.mq_free.argtypes = [vp]
     lib.mq_free.restype = None
     lib.mq_status_string.argtypes = [ctypes.c_int]
@@ -131,6 +138,44 @@ def mq_pack(W, group_size: int = 128, residual_density: float = 0.0, stream=None
     return Packed(out, N, K, group_size, float(residual_density))
 
 
+def mq_pack_blocks(W, group_size: int, block_fraction: float, h, stream=None) -> Packed:
+    """Pack with a block-wise residual chosen by the Hessian-guided score (see
+    mq_pack_blocks in include/mosaicq.h); h: float32 [K] device tensor."""
+    import torch
+    ptr = _dev_fp16(W, "W")
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [N, K]")
+    N, K = W.shape
+    if not isinstance(h, torch.Tensor) or not h.is_cuda or h.dtype != torch.float32 or tuple(h.shape) != (K,):
+        raise TypeError(f"h must be a float32 [{K}] tensor on the GPU")
+    h = h.contiguous()
+    out = ctypes.c_void_p()
+    _check(lib.mq_pack_blocks(ptr, N, K, group_size, float(block_fraction), ctypes.c_void_p(h.data_ptr()),
+                              _stream_handle(stream), ctypes.byref(out)), "mq_pack_blocks")
+    p = Packed(out, N, K, group_size, float(block_fraction))
+    nb = ctypes.c_int64()
+    _check(lib.mq_block_count(p.handle, ctypes.byref(nb)), "mq_block_count")
+    p.nblk = nb.value
+    return p
+
+
+def export_blocks(packed: Packed, stream=None) -> dict:
+    """The block residual of a handle from mq_pack_blocks as host numpy arrays
+    (blk [B], rscale [B, 16], rcodes [B, 16, 64]); synchronises."""
+    import torch
+    nb = ctypes.c_int64()
+    _check(lib.mq_block_count(packed.handle, ctypes.byref(nb)), "mq_block_count")
+    B = max(nb.value, 0)
+    out = {"blk": torch.empty(max(B, 1), dtype=torch.int32, device="cuda"),
+           "rscale": torch.empty((max(B, 1), 16), dtype=torch.float32, device="cuda"),
+           "rcodes": torch.empty((max(B, 1), 16, 64), dtype=torch.uint8, device="cuda")}
+    _check(lib.mq_export_blocks(packed.handle, *[ctypes.c_void_p(out[k].data_ptr()) for k in
+                                                 ("blk", "rscale", "rcodes")], _stream_handle(stream)),
+           "mq_export_blocks")
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy()[:B] for k, v in out.items()}
+
+
 def mq_linear_with(X, packed: Packed, kernel: int = KERNEL_AUTO, Y=None, stream=None):
     """Y = X (deq(base) + deq(residual))^T, enqueued on `stream` (no sync)."""
     import torch
@@ -173,26 +218,32 @@ def mq_packed_info(packed: Packed) -> dict:
     return {"N": N.value, "K": K.value, "G": G.value, "nnz": nnz.value, "bytes": nbytes.value}
 
 
-def mq_export_canonical(packed: Packed, stream=None) -> dict:
-    """Canonical arrays as device tensors (synchronises the stream)."""
+def mq_export_canonical(packed: Packed, stream=None, residual: bool = True) -> dict:
+    """Canonical arrays as device tensors (synchronises the stream); with
+    residual=False only the base codes and scales (all a handle from
+    mq_pack_blocks exports here)."""
     import torch
     dev = torch.device("cuda", torch.cuda.current_device())
     N, K, G, nnz = packed.N, packed.K, packed.G, packed.nnz
     out = {
         "codes": torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
         "scales": torch.empty((N, K // G), dtype=torch.float16, device=dev),
-        "row_ptr": torch.empty(N + 1, dtype=torch.int32, device=dev),
-        "col": torch.empty(max(nnz, 1), dtype=torch.int16, device=dev),
-        "rcodes": torch.empty(max((nnz + 1) // 2, 1), dtype=torch.uint8, device=dev),
-        "rscale": torch.empty(N, dtype=torch.float32, device=dev),
     }
+    names = ("codes", "scales", "row_ptr", "col", "rcodes", "rscale")
+    if residual:
+        out.update({
+            "row_ptr": torch.empty(N + 1, dtype=torch.int32, device=dev),
+            "col": torch.empty(max(nnz, 1), dtype=torch.int16, device=dev),
+            "rcodes": torch.empty(max((nnz + 1) // 2, 1), dtype=torch.uint8, device=dev),
+            "rscale": torch.empty(N, dtype=torch.float32, device=dev),
+        })
     s = _stream_handle(stream)
-    _check(lib.mq_export_canonical(packed.handle, *[ctypes.c_void_p(out[k].data_ptr()) for k in
-                                                    ("codes", "scales", "row_ptr", "col", "rcodes", "rscale")],
-                                   s), "mq_export_canonical")
+    _check(lib.mq_export_canonical(packed.handle, *[ctypes.c_void_p(out[k].data_ptr()) if k in out else None
+                                                    for k in names], s), "mq_export_canonical")
     torch.cuda.synchronize()
-    out["col"] = out["col"][:nnz]
-    out["rcodes"] = out["rcodes"][:(nnz + 1) // 2]
+    if residual:
+        out["col"] = out["col"][:nnz]
+        out["rcodes"] = out["rcodes"][:(nnz + 1) // 2]
     return out
 
 

@@ -183,6 +183,64 @@ mq_status mq_export_canonical(const mq_packed* p, void* codes_u8, void* scales_f
 mq_status mq_export_tiled(const mq_packed* p, void* tiles_u8, void* tile_ptr_u32,
                           void* entries_u32, void* hip_stream);
 
+/*
+ * mq_pack_blocks -- pack W with a block-wise residual chosen by a
+ * Hessian-guided score (MosaicQuant explainer, Methodology section 2,
+ * Block-Wise Residual Allocation: the budget goes to blocks; a Delta-score
+ * weights each block's residual error with the diagonal Hessian estimate of
+ * the input channels and approximates the drop of the output distortion;
+ * the top-K blocks get a 4-bit residual).
+ *
+ * The base is exactly that of mq_pack. A block is one 16 x 128 tile (rows
+ * 16 rb .., columns 128 kt ..; partial at the edges). For every block and
+ * every row i of it: sr = fp32(max |e_ij| / 7) over the block's columns and
+ * qr = clamp(rne(e / sr), -7, 7), e = w - s q the exact base error. The score
+ * is Delta = sum, over the block's rows and then columns in ascending order,
+ * of h_j * (r * (2 e - r)) with r = sr * qr, every operation rounded to
+ * float64 (a fixed order, so the selection is reproducible); it equals the
+ * drop of sum_j h_j (w - W~)^2 the block's residual brings. The
+ * floor(block_fraction * number of blocks) blocks first in the order (Delta
+ * descending, block index rb * ceil(K/128) + kt ascending) keep their
+ * residual; the other entries keep the base only.
+ *
+ *   W_dev_fp16, N, K, group_size, hip_stream, out  as for mq_pack
+ *   block_fraction  in [0, 1]
+ *   h_dev_f32       [K] fp32 device weights of the input channels, >= 0 and
+ *                   finite (for calibration activations X: h_j = sum_m X_mj^2);
+ *                   read during the call only, 4-byte aligned
+ *
+ * The handle runs in mq_linear / mq_linear_with like any other (the selected
+ * blocks' nonzero residual codes become entries of the residual stream
+ * described at mq_export_tiled). mq_packed_info's nnz counts those entries.
+ * mq_residual_add and the residual arrays of mq_export_canonical are not
+ * available for it (MQ_ERR_UNSUPPORTED; codes and scales export as usual);
+ * mq_export_blocks gives the residual. Synchronises hip_stream once, like
+ * mq_pack. Errors as mq_pack, plus MQ_ERR_INVALID_ARG for block_fraction
+ * outside [0, 1] (or NaN), a NULL or misaligned h, or a negative or
+ * non-finite h value.
+ */
+mq_status mq_pack_blocks(const void* W_dev_fp16, int64_t N, int64_t K, int32_t group_size,
+                         double block_fraction, const float* h_dev_f32, void* hip_stream,
+                         mq_packed** out);
+
+/* mq_block_count -- number of residual blocks of a handle from mq_pack_blocks
+ * (-1 for a handle from mq_pack). */
+mq_status mq_block_count(const mq_packed* p, int64_t* nblk);
+
+/*
+ * mq_export_blocks -- the block residual of a handle from mq_pack_blocks, in
+ * canonical form (device destinations, any may be NULL; enqueued on
+ * hip_stream). With B = mq_block_count:
+ *   blk_i32     [B]           selected block indices rb * ceil(K/128) + kt, ascending
+ *   rscale_f32  [B, 16]       residual scale of each block row (0 past row N - 1)
+ *   rcodes_u8   [B, 16, 64]   residual code u = qr + 8 of each block row; byte b
+ *                             holds column 2b in the low nibble and 2b+1 in the
+ *                             high nibble; entries past the matrix hold 8
+ * MQ_ERR_UNSUPPORTED for a handle from mq_pack.
+ */
+mq_status mq_export_blocks(const mq_packed* p, void* blk_i32, void* rscale_f32, void* rcodes_u8,
+                           void* hip_stream);
+
 /* mq_free -- release a handle and its device memory (NULL is accepted). The
  * caller must make sure no enqueued mq_linear still reads it. */
 void mq_free(mq_packed* p);

@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["mq_pack", "mq_linear", "mq_linear_with", "mq_residual_add", "mq_packed_info", "mq_export_canonical",
-         "mq_export_tiled", "mq_free", "mq_status_string"])
+         "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks", "mq_free",
+         "mq_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -68,6 +69,21 @@ def test_pack_argument_validation(lib, kw, code):
     assert _pack(lib, **kw) == code
 
 
+def _pack_blocks(lib, W=FAKE, N=32, K=256, G=128, frac=0.1, h=FAKE, out=True):
+    hd = ctypes.c_void_p()
+    return lib.mq_pack_blocks(W, N, K, G, frac, h, None, ctypes.byref(hd) if out else None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=None), -1), (dict(h=None), -1), (dict(out=False), -1), (dict(N=0), -1),
+    (dict(frac=-0.1), -1), (dict(frac=1.01), -1), (dict(frac=math.nan), -1),
+    (dict(G=48), -2), (dict(K=96, G=64), -1), (dict(K=65536 + 128), -2),
+    (dict(h=ctypes.c_void_p((1 << 20) + 2)), -1), (dict(W=ctypes.c_void_p((1 << 20) + 8)), -1),
+])
+def test_pack_blocks_argument_validation(lib, kw, code):
+    assert _pack_blocks(lib, **kw) == code
+
+
 def test_pack_without_a_device_reports_device_error(lib):
     import torch
     if torch.cuda.is_available():
@@ -86,5 +102,7 @@ def test_bad_handles_are_rejected(lib):
     assert lib.mq_packed_info(bogus, ctypes.byref(n), None, None, None, None) == -6
     assert lib.mq_export_canonical(bogus, None, None, None, None, None, None, None) == -6
     assert lib.mq_export_tiled(bogus, None, None, None, None) == -6
+    assert lib.mq_block_count(bogus, ctypes.byref(n)) == -6
+    assert lib.mq_export_blocks(bogus, None, None, None, None) == -6
     lib.mq_free(None)        # accepted
     lib.mq_free(bogus)       # unknown handle: ignored, no crash
