@@ -50,8 +50,8 @@ def parse():
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-extra", action="store_true",
-                    help="skip the transformer-block and residual-sweep legs")
-    ap.add_argument("--only", choices=["decode", "prefill", "copy"], default=None,
+                    help="skip the transformer-block, residual-sweep and block-residual legs")
+    ap.add_argument("--only", choices=["decode", "prefill", "copy", "blocks"], default=None,
                     help="run one leg only (profiling runs); 'copy' runs the plain device copy that "
                          "calibrates the HBM byte counters")
     ap.add_argument("--no-warm", action="store_true",
@@ -373,6 +373,67 @@ def bench_sweep(args, mq, synth, torch):
     return {"workload": "sweep-14336x4096", "N": 14336, "K": 4096, "group": 128, "by_placement": out}
 
 
+def bench_blocks(args, mq, synth, torch):
+    """Block-wise residual (Hessian-guided top-K of 16x128 blocks) on the
+    11008x4096 decode layer: for each block fraction, mq_pack_blocks time, the
+    share of the output distortion of the plain W4 base it recovers on
+    held-out activations (||Y - X W^T||^2 against an fp32 torch product, over
+    256 tokens that share the calibration set's 4 hot channels), and the
+    decode time at M = 1 and 16 (rotated copies, graph replay). Beside each,
+    the element-wise residual with the same canonical residual bytes."""
+    layer = synth.WORKLOADS["decode-11008x4096"].layers[0]
+    N, K = layer.N, layer.K
+    W = torch.from_numpy(layer.W()).cuda()
+    Xcal = torch.from_numpy(layer.calibration(256, 4)).cuda()
+    Xev = torch.from_numpy(layer.calibration(256, 4, held_out=True)).cuda()
+    h = (Xcal.float() ** 2).sum(0)                       # diagonal Hessian estimate of the input channels
+    Yref = Xev.float() @ W.float().t()
+    Xs = {M: torch.from_numpy(layer.X(M)).cuda() for M in (1, 16)}
+
+    def distortion(p):
+        Y = mq.mq_linear(Xev, p).float()
+        return float(((Y - Yref) ** 2).sum())
+
+    def decode_us(make):
+        p0 = make()
+        ncopy = max(2, math.ceil(2 * MALL_BYTES / p0.device_bytes))
+        copies = [p0] + [make() for _ in range(ncopy - 1)]
+        out = {}
+        for M, X in Xs.items():
+            Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+
+            def one(i, X=X, Y=Y):
+                mq.mq_linear(X, copies[i % ncopy], Y)
+            out[str(M)] = round(replay_spread(torch, one, 4, 40, reps=5)[0] * 1e3, 2)
+        for c in copies:
+            c.free()
+        return out
+
+    base = mq.mq_pack(W, layer.group, 0.0)
+    D0 = distortion(base)
+    res = {"workload": "decode-11008x4096", "block": "16x128", "calibration_tokens": 256,
+           "D_base": D0, "base_us": decode_us(lambda: mq.mq_pack(W, layer.group, 0.0)), "by_fraction": {}}
+    base.free()
+    for beta in (0.01, 0.05, 0.1, 0.2):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        p = mq.mq_pack_blocks(W, layer.group, beta, h)
+        ev1.record()
+        torch.cuda.synchronize()
+        rbytes = p.nblk * (16 * 64 + 16 * 4)             # 4-bit codes + fp32 scale per block row
+        entry = {"nblk": p.nblk, "entries": p.nnz, "pack_ms": round(ev0.elapsed_time(ev1), 3),
+                 "residual_bytes": rbytes, "recovered": round(1.0 - distortion(p) / D0, 4),
+                 "us": decode_us(lambda: mq.mq_pack_blocks(W, layer.group, beta, h))}
+        p.free()
+        rho = rbytes / 2.5 / (N * K)                     # element-wise: 2 B column + 1/2 B code per entry
+        pe = mq.mq_pack(W, layer.group, rho)
+        entry["elementwise_same_bytes"] = {"rho": round(rho, 5), "recovered": round(1.0 - distortion(pe) / D0, 4),
+                                           "us": decode_us(lambda: mq.mq_pack(W, layer.group, rho))}
+        pe.free()
+        res["by_fraction"][str(beta)] = entry
+    return res
+
+
 def cpu_baseline(layer, Ms, min_seconds=10.0, max_steps=60):
     """The oracle, as it stands, on the same decode layer: one step is its
     dequantisation plus the float64 linear for M = 1, 4, 16 (packing by the
@@ -434,6 +495,9 @@ def main():
     if args.only == "prefill":
         print(json.dumps({"prefill": bench_prefill(args, mq, synth, torch)}), flush=True)
         return
+    if args.only == "blocks":
+        print(json.dumps({"block_residual": bench_blocks(args, mq, synth, torch)}), flush=True)
+        return
     d = bench_decode(args, mq, synth, torch)
     value = d["bytes_step"] / (d["ms_per_step"] * 1e-3) / 1e9
     # dominant kernel: the decode launch with the longest average duration
@@ -466,6 +530,7 @@ def main():
         if not args.skip_extra:
             line["block_4096h_m16"] = bench_block(args, mq, synth, torch)
             line["residual_sweep"] = bench_sweep(args, mq, synth, torch)
+            line["block_residual"] = bench_blocks(args, mq, synth, torch)
         if not args.skip_cpu:
             line["cpu_baseline"] = cpu_baseline(d["layer"], [1, 4, 16])
     print(json.dumps(line), flush=True)

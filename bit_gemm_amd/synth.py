@@ -15,7 +15,9 @@ Recipe (numpy ``default_rng``):
   X = fp16_RNE(N(0, 1)) drawn in float32; optionally h activation channels
       (drawn without replacement) multiplied by 50 before the rounding.
   seed of a tensor = 1000 * workload + 10 * matrix + role, role 0 = W,
-  1 = X, 2 = outlier positions, 3 = hot activation channels.
+  1 = X, 2 = outlier positions, 3 = hot activation channels, 4 = calibration
+  activations, 5 = held-out evaluation activations (both with the layer's
+  hot channels, role 3, so they share one activation profile).
 
 The shapes are Llama-family linear layers; they stand in for the real models'
 weights, which are not available (no trained checkpoints are used).
@@ -97,6 +99,11 @@ class Layer:
     def X(self, M: int) -> np.ndarray:
         return activations(M, self.K, seed_of(self.workload, self.matrix, 1),
                            seed_of(self.workload, self.matrix, 3), self.hot_channels)
+
+    def calibration(self, M: int, hot_channels: int, held_out: bool = False) -> np.ndarray:
+        """Calibration (or held-out evaluation) activations with hot channels."""
+        return activations(M, self.K, seed_of(self.workload, self.matrix, 5 if held_out else 4),
+                           seed_of(self.workload, self.matrix, 3), hot_channels)
 
 
 @dataclass(frozen=True)
