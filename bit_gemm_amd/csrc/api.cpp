@@ -34,8 +34,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 void release(mq_packed* p) {
-  void* bufs[] = {p->tiles,    p->scales,  p->row_ptr, p->col, p->rcodes, p->rscale,
-                  p->tile_ptr, p->entries, p->wpatch,  p->blk, p->bscale, p->bcodes};
+  void* bufs[] = {p->tiles,    p->scales,  p->row_ptr, p->col,    p->rcodes, p->rscale,  p->tile_ptr,
+                  p->entries, p->wpatch,  p->blk,     p->bscale, p->bcodes, p->rt_ptr, p->rt_tiles};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   p->magic = 0;
@@ -205,7 +205,7 @@ MQ_API mq_status mq_pack_blocks(const void* W_dev_fp16, int64_t N, int64_t K, in
 
   const size_t n_tiles = (size_t)nblocks;
   const size_t sz_ent = (size_t)(p->stream_cap + mq::kEntryPad) * sizeof(uint32_t);
-  const size_t nb1 = (size_t)std::max<int64_t>(nsel, 1);
+  const size_t nb1 = (size_t)nsel + 1;   // one more all-zero block slot
   struct {
     void** dst;
     size_t n;
@@ -216,7 +216,9 @@ MQ_API mq_status mq_pack_blocks(const void* W_dev_fp16, int64_t N, int64_t K, in
                 {(void**)&p->wpatch, sz_ent},
                 {(void**)&p->blk, nb1 * sizeof(int32_t)},
                 {(void**)&p->bscale, nb1 * mq::kRowsPerBlock * sizeof(float)},
-                {(void**)&p->bcodes, nb1 * mq::kRowsPerBlock * (mq::kTileCols / 2)}};
+                {(void**)&p->bcodes, nb1 * mq::kRowsPerBlock * (mq::kTileCols / 2)},
+                {(void**)&p->rt_ptr, (size_t)(p->Nb + 1) * sizeof(uint32_t)},
+                {(void**)&p->rt_tiles, nb1 * mq::kTileBytes}};
   size_t total = 0;
   for (auto& a : allocs) {
     e = hipMalloc(a.dst, a.n);

@@ -287,6 +287,46 @@ __device__ __forceinline__ void load_scales_run(uint32_t (&w)[4][TPW / 2], const
   }
 }
 
+// Block residual kept as 4-bit code tiles (handles from mq_pack_blocks):
+// row block rb's residual tiles are blk[rt_ptr[rb] .. rt_ptr[rb + 1]), tile i
+// holds codes in the base tile layout and one fp32 scale per row; slot
+// `zero` is an all-zero tile. K = 4096 here, so the column tile is blk & 31.
+struct DenseRes {
+  const uint32_t* rt_ptr;
+  const uint4* tiles;
+  const float* scale;
+  const int32_t* blk;
+  uint32_t zero;
+};
+
+struct ResTile {
+  uint4 code;
+  float4_t sc;   // scales of rows 4 g .. 4 g + 3
+  int kt;
+};
+
+__device__ __forceinline__ void load_res_tile(ResTile& T, const DenseRes& D, uint32_t i, int lane, int g) {
+  T.code = D.tiles[(int64_t)i * 64 + lane];
+  T.sc = *reinterpret_cast<const float4_t*>(D.scale + (int64_t)i * kRowsPerBlock + 4 * g);
+  T.kt = D.blk[i] & 31;
+}
+
+// One residual tile, like a base tile of its own scale: the exact 4-bit codes
+// times the tile's X columns (from LDS) on the MFMA path, scaled per row in fp32.
+__device__ __forceinline__ void res_tile(float4_t (&acc)[1], const ResTile& T, const uint16_t* xs, int mrow, int ldx,
+                                         int g, uint32_t vmask, uint32_t vmask4, uint32_t vmagic) {
+  const uint16_t* xp = xs + mrow * ldx + T.kt * kTileCols + 8 * g;
+  float4_t tacc = mfma16(widen_q(T.code.x, vmask, vmask4, vmagic), *reinterpret_cast<const half8_t*>(xp),
+                         float4_t{0.f, 0.f, 0.f, 0.f});
+  tacc = mfma16(widen_q(T.code.y, vmask, vmask4, vmagic), *reinterpret_cast<const half8_t*>(xp + 32), tacc);
+  tacc = mfma16(widen_q(T.code.z, vmask, vmask4, vmagic), *reinterpret_cast<const half8_t*>(xp + 64), tacc);
+  tacc = mfma16(widen_q(T.code.w, vmask, vmask4, vmagic), *reinterpret_cast<const half8_t*>(xp + 96), tacc);
+  acc[0].x = fmaf(T.sc.x, tacc.x, acc[0].x);
+  acc[0].y = fmaf(T.sc.y, tacc.y, acc[0].y);
+  acc[0].z = fmaf(T.sc.z, tacc.z, acc[0].z);
+  acc[0].w = fmaf(T.sc.w, tacc.w, acc[0].w);
+}
+
 // Fast decode kernel for K = 4096 and up to 4 tokens (XR = M rounded up to a
 // power of two). One workgroup of 8 waves per 16-row block, 4 code tiles
 // per wave. Memory counters retire in issue order, so the issue order is
@@ -304,11 +344,11 @@ __device__ __forceinline__ void load_scales_run(uint32_t (&w)[4][TPW / 2], const
 // from LDS), then tiles 2 and 3, so the residual work overlaps the second
 // half of the stream. Partial 16 x 1 tiles are summed in LDS in a fixed
 // order.
-template <int GSH, int XR>
+template <int GSH, int XR, bool DR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 6 : 1, 8))) void k_gemv_x(
     const uint4* __restrict__ tiles, const uint16_t* __restrict__ scales, int sstride,
     const uint32_t* __restrict__ tile_ptr, const uint32_t* __restrict__ entries, const uint16_t* __restrict__ X,
-    uint16_t* __restrict__ Y, int M, int N, int zero_off) {
+    uint16_t* __restrict__ Y, int M, int N, int zero_off, DenseRes D) {
   constexpr int KS = 8, TPW = 4, K = 4096, Kt = 32, NS = 1 << GSH, LDX = K + kXPad;
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][LDX]
   __shared__ float4_t red[KS][64];
@@ -362,17 +402,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
 
   // 3. residual chunks wave and wave + 8: two aligned 16-byte loads per lane
   // each (row-block segments are whole 32-entry chunks); an index past the
-  // row block reads the zero entries after the stream
-  const uint32_t E0 = tile_ptr[tbase], E1 = tile_ptr[tbase + Kt];
-  const uint32_t nchunks = (E1 - E0) / (uint32_t)kChunk;
+  // row block reads the zero entries after the stream. DR: residual tiles
+  // wave and wave + 8 of the row block instead (past its end: the zero tile).
+  uint32_t E0 = 0, nchunks = 0;
   uint4 ent[2][2];
+  uint32_t R0 = 0, nrt = 0;
+  ResTile rt[2];
+  if constexpr (DR) {
+    R0 = D.rt_ptr[rb];
+    nrt = D.rt_ptr[rb + 1] - R0;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const uint32_t c = (uint32_t)(wave + j * KS);
-    const uint32_t* ep = (c < nchunks) ? entries + E0 + kChunk * c : entries + zero_off;
-    const uint4* e4 = reinterpret_cast<const uint4*>(ep + 8 * g);
-    ent[j][0] = e4[0];
-    ent[j][1] = e4[1];
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t c = (uint32_t)(wave + j * KS);
+      load_res_tile(rt[j], D, c < nrt ? R0 + c : D.zero, lane, g);
+    }
+  } else {
+    E0 = tile_ptr[tbase];
+    nchunks = (tile_ptr[tbase + Kt] - E0) / (uint32_t)kChunk;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t c = (uint32_t)(wave + j * KS);
+      const uint32_t* ep = (c < nchunks) ? entries + E0 + kChunk * c : entries + zero_off;
+      const uint4* e4 = reinterpret_cast<const uint4*>(ep + 8 * g);
+      ent[j][0] = e4[0];
+      ent[j][1] = e4[1];
+    }
   }
 
   // 4. code tiles 2 and 3
@@ -409,20 +463,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
   };
   tile(0);
   tile(1);
-  // residual chunks of this wave; a chunk past the row block is skipped (the
-  // empty use keeps its load ahead of the tiles instead of inside the branch)
+  if constexpr (DR) {
+    // residual tiles of this wave (the zero tile adds nothing: no branch)
+    res_tile(acc, rt[0], xs, mrow[0], LDX, g, vmask, vmask4, vmagic);
+    res_tile(acc, rt[1], xs, mrow[0], LDX, g, vmask, vmask4, vmagic);
+    tile(2);
+    tile(3);
+    for (uint32_t c = (uint32_t)(wave + 2 * KS); c < nrt; c += KS) {
+      ResTile t2;
+      load_res_tile(t2, D, R0 + c, lane, g);
+      res_tile(acc, t2, xs, mrow[0], LDX, g, vmask, vmask4, vmagic);
+    }
+  } else {
+    // residual chunks of this wave; a chunk past the row block is skipped (the
+    // empty use keeps its load ahead of the tiles instead of inside the branch)
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const uint32_t c = (uint32_t)(wave + j * KS);
-    if (c < nchunks)
-      res_chunk<1, true, false>(acc, ent[j][0], ent[j][1], E0 + kChunk * c, tile_ptr + tbase, 1, X, xs, mrow, K, LDX, r, g);
-    else
-      asm volatile("" ::"v"(ent[j][0].x), "v"(ent[j][1].x));
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t c = (uint32_t)(wave + j * KS);
+      if (c < nchunks)
+        res_chunk<1, true, false>(acc, ent[j][0], ent[j][1], E0 + kChunk * c, tile_ptr + tbase, 1, X, xs, mrow, K, LDX,
+                                  r, g);
+      else
+        asm volatile("" ::"v"(ent[j][0].x), "v"(ent[j][1].x));
+    }
+    tile(2);
+    tile(3);
+    res_rest<1, true, false, KS>(acc, entries, E0, (uint32_t)(wave + 2 * KS), nchunks, zero_off, tile_ptr + tbase, 1,
+                                 X, xs, mrow, K, LDX, r, g);
   }
-  tile(2);
-  tile(3);
-  res_rest<1, true, false, KS>(acc, entries, E0, (uint32_t)(wave + 2 * KS), nchunks, zero_off, tile_ptr + tbase, 1, X,
-                               xs, mrow, K, LDX, r, g);
 
   red[wave][lane] = acc[0];
   __syncthreads();
@@ -443,11 +511,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
 // residual chunks of all R row blocks before computing anything. The row
 // blocks are computed in order (residual chunks gather their X columns from
 // LDS) and the 8 partials of each are summed in LDS in a fixed order.
-template <int GSH, int XR, int R>
+template <int GSH, int XR, int R, bool DR>
 __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles, const uint16_t* __restrict__ scales,
                                                int sstride, const uint32_t* __restrict__ tile_ptr,
                                                const uint32_t* __restrict__ entries, const uint16_t* __restrict__ X,
-                                               uint16_t* __restrict__ Y, int M, int N, int Nb, int zero_off) {
+                                               uint16_t* __restrict__ Y, int M, int N, int Nb, int zero_off,
+                                               DenseRes D) {
   constexpr int KS = 8, TPW = 4, K = 4096, Kt = 32, NS = 1 << GSH, LDX = K + kXPad;
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][LDX], then the partials [R][KS][64]
   static_assert(R * KS * 64 * sizeof(float4_t) <= XR * LDX * sizeof(uint16_t), "partials fit in the X space");
@@ -458,13 +527,20 @@ __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles,
   int mrow[1];
   token_rows<1>(M, r, mrow);
 
-  // residual segment of each row block (scalar loads, they land during the X copy)
+  // residual segment of each row block (scalar loads, they land during the
+  // X copy); DR: its residual tiles instead
   uint32_t E0[R], nch[R];
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    const int tbase = min(rb0 + j, Nb - 1) * Kt;
-    E0[j] = tile_ptr[tbase];
-    nch[j] = (tile_ptr[tbase + Kt] - E0[j]) / (uint32_t)kChunk;
+    const int rbc = min(rb0 + j, Nb - 1);
+    if constexpr (DR) {
+      E0[j] = D.rt_ptr[rbc];
+      nch[j] = D.rt_ptr[rbc + 1] - E0[j];
+    } else {
+      const int tbase = rbc * Kt;
+      E0[j] = tile_ptr[tbase];
+      nch[j] = (tile_ptr[tbase + Kt] - E0[j]) / (uint32_t)kChunk;
+    }
   }
 
   // X slice of this wave, one 1 KiB copy per token row straight from global
@@ -484,7 +560,8 @@ __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles,
   // residual chunks: indices wave and wave + 8, zero entries past the end)
   uint4 code[R][TPW];
   uint2 sraw[R][4][NS == 1 ? 1 : TPW];
-  uint4 ent[R][2][2];
+  uint4 ent[R][DR ? 1 : 2][2];
+  ResTile rt[R];
   bool live[R];
 #pragma unroll
   for (int j = 0; j < R; ++j) {
@@ -508,13 +585,18 @@ __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles,
     const uint4* tp = tiles + (tbase + kt0) * 64 + lane;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) code[j][t] = tp[t * 64];
+    if constexpr (DR) {   // residual tile `wave` of the row block (past its end: the zero tile)
+      const uint32_t c = (uint32_t)wave;
+      load_res_tile(rt[j], D, c < nch[j] ? E0[j] + c : D.zero, lane, g);
+    } else {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t c = (uint32_t)(wave + h * KS);
-      const uint32_t* ep = (c < nch[j]) ? entries + E0[j] + kChunk * c : entries + zero_off;
-      const uint4* e4 = reinterpret_cast<const uint4*>(ep + 8 * g);
-      ent[j][h][0] = e4[0];
-      ent[j][h][1] = e4[1];
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t c = (uint32_t)(wave + h * KS);
+        const uint32_t* ep = (c < nch[j]) ? entries + E0[j] + kChunk * c : entries + zero_off;
+        const uint4* e4 = reinterpret_cast<const uint4*>(ep + 8 * g);
+        ent[j][h][0] = e4[0];
+        ent[j][h][1] = e4[1];
+      }
     }
     __builtin_amdgcn_sched_barrier(0);   // keep row block j's requests ahead of row block j + 1's
   }
@@ -543,17 +625,26 @@ __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles,
       }
       tile_mma<1, NS, true, false>(acc, code[j][t], S, X, xs, mrow, K, LDX, kt0 + t, g, vmask, vmask4, vmagic);
     }
-    const uint32_t* rtp = tile_ptr + rb * Kt;
+    if constexpr (DR) {   // residual tiles wave, wave + 8, ... (the zero tile adds nothing)
+      res_tile(acc, rt[j], xs, mrow[0], LDX, g, vmask, vmask4, vmagic);
+      for (uint32_t c = (uint32_t)(wave + KS); c < nch[j]; c += KS) {
+        ResTile t2;
+        load_res_tile(t2, D, E0[j] + c, lane, g);
+        res_tile(acc, t2, xs, mrow[0], LDX, g, vmask, vmask4, vmagic);
+      }
+    } else {
+      const uint32_t* rtp = tile_ptr + rb * Kt;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {   // a chunk past the row block is skipped; the empty use keeps its load in place
-      if ((uint32_t)(wave + h * KS) < nch[j])
-        res_chunk<1, true, false>(acc, ent[j][h][0], ent[j][h][1], E0[j] + kChunk * (wave + h * KS), rtp, 1, X, xs,
-                                  mrow, K, LDX, r, g);
-      else
-        asm volatile("" ::"v"(ent[j][h][0].x), "v"(ent[j][h][1].x));
+      for (int h = 0; h < 2; ++h) {   // a chunk past the row block is skipped; the empty use keeps its load in place
+        if ((uint32_t)(wave + h * KS) < nch[j])
+          res_chunk<1, true, false>(acc, ent[j][h][0], ent[j][h][1], E0[j] + kChunk * (wave + h * KS), rtp, 1, X, xs,
+                                    mrow, K, LDX, r, g);
+        else
+          asm volatile("" ::"v"(ent[j][h][0].x), "v"(ent[j][h][1].x));
+      }
+      res_rest<1, true, false, KS>(acc, entries, E0[j], (uint32_t)(wave + 2 * KS), nch[j], zero_off, rtp, 1, X, xs,
+                                   mrow, K, LDX, r, g);
     }
-    res_rest<1, true, false, KS>(acc, entries, E0[j], (uint32_t)(wave + 2 * KS), nch[j], zero_off, rtp, 1, X, xs, mrow,
-                                 K, LDX, r, g);
     part[j] = acc[0];
   }
   // the partials go where X was, once every wave is done with X
@@ -734,32 +825,37 @@ hipError_t allow_lds(F* fn, bool& done) {
   return e;
 }
 
-template <int GSH, int XR>
+// the block residual of a handle from mq_pack_blocks as code tiles (unused otherwise)
+DenseRes dense_res(const mq_packed* p) {
+  return DenseRes{p->rt_ptr, reinterpret_cast<const uint4*>(p->rt_tiles), p->bscale, p->blk, (uint32_t)p->nblk};
+}
+
+template <int GSH, int XR, bool DR>
 hipError_t launch_x(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
   static bool done = false;
-  const hipError_t e = allow_lds(&k_gemv_x<GSH, XR>, done);
+  const hipError_t e = allow_lds(&k_gemv_x<GSH, XR, DR>, done);
   if (e != hipSuccess) return e;
-  k_gemv_x<GSH, XR><<<dim3((unsigned)p->Nb), dim3(512), (size_t)XR * (4096 + kXPad) * 2, s>>>(
+  k_gemv_x<GSH, XR, DR><<<dim3((unsigned)p->Nb), dim3(512), (size_t)XR * (4096 + kXPad) * 2, s>>>(
       reinterpret_cast<const uint4*>(p->tiles), p->scales, (int)p->sstride, p->tile_ptr, p->entries, X, Y, M,
-      (int)p->N, (int)p->stream_cap);
+      (int)p->N, (int)p->stream_cap, dense_res(p));
   return hipGetLastError();
 }
 
 constexpr size_t kLdsMaxBytes = 160 * 1024;   // LDS of one CU
 
-template <int GSH, int XR, int R>
+template <int GSH, int XR, int R, bool DR>
 hipError_t launch_r(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
   static bool done = false;
   if (!done) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_r<GSH, XR, R>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_r<GSH, XR, R, DR>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMaxBytes);
     if (e != hipSuccess) return e;
     done = true;
   }
   const unsigned grid = (unsigned)((p->Nb + R - 1) / R);
-  k_gemv_r<GSH, XR, R><<<dim3(grid), dim3(512), (size_t)XR * (4096 + kXPad) * 2, s>>>(
+  k_gemv_r<GSH, XR, R, DR><<<dim3(grid), dim3(512), (size_t)XR * (4096 + kXPad) * 2, s>>>(
       reinterpret_cast<const uint4*>(p->tiles), p->scales, (int)p->sstride, p->tile_ptr, p->entries, X, Y, M,
-      (int)p->N, (int)p->Nb, (int)p->stream_cap);
+      (int)p->N, (int)p->Nb, (int)p->stream_cap, dense_res(p));
   return hipGetLastError();
 }
 
@@ -767,15 +863,15 @@ hipError_t launch_r(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, h
 // and ceil(Nb / 256) row blocks each make one round of workgroups (a few
 // workgroups past 256 would take a second round on their own). Up to 4 row
 // blocks fit the registers, 2 when G = 32 (4 scales per tile and row).
-template <int GSH, int XR>
+template <int GSH, int XR, bool DR>
 hipError_t launch_r_any(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
-  if (p->Nb <= 256) return launch_r<GSH, XR, 1>(p, X, M, Y, s);
+  if (p->Nb <= 256) return launch_r<GSH, XR, 1, DR>(p, X, M, Y, s);
   if constexpr (GSH == 2) {
-    return launch_r<GSH, XR, 2>(p, X, M, Y, s);
+    return launch_r<GSH, XR, 2, DR>(p, X, M, Y, s);
   } else {
-    if (p->Nb <= 512) return launch_r<GSH, XR, 2>(p, X, M, Y, s);
-    if (p->Nb <= 768) return launch_r<GSH, XR, 3>(p, X, M, Y, s);
-    return launch_r<GSH, XR, 4>(p, X, M, Y, s);
+    if (p->Nb <= 512) return launch_r<GSH, XR, 2, DR>(p, X, M, Y, s);
+    if (p->Nb <= 768) return launch_r<GSH, XR, 3, DR>(p, X, M, Y, s);
+    return launch_r<GSH, XR, 4, DR>(p, X, M, Y, s);
   }
 }
 
@@ -819,13 +915,22 @@ template <int MB, int GSH>
 hipError_t run(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
   if constexpr (MB == 1) {
     if (p->K == 4096 && M <= 4) {   // fast kernel: X slices in LDS, residual amid the tiles
-      if (M == 1) return launch_x<GSH, 1>(p, X, M, Y, s);
-      if (M == 2) return launch_x<GSH, 2>(p, X, M, Y, s);
-      return launch_x<GSH, 4>(p, X, M, Y, s);
+      if (p->blocks) {   // the block residual as code tiles
+        if (M == 1) return launch_x<GSH, 1, true>(p, X, M, Y, s);
+        if (M == 2) return launch_x<GSH, 2, true>(p, X, M, Y, s);
+        return launch_x<GSH, 4, true>(p, X, M, Y, s);
+      }
+      if (M == 1) return launch_x<GSH, 1, false>(p, X, M, Y, s);
+      if (M == 2) return launch_x<GSH, 2, false>(p, X, M, Y, s);
+      return launch_x<GSH, 4, false>(p, X, M, Y, s);
     }
     if (p->K == 4096) {   // 5..16 tokens: X whole in LDS, several row blocks per workgroup
-      if (M <= 8) return launch_r_any<GSH, 8>(p, X, M, Y, s);
-      return launch_r_any<GSH, 16>(p, X, M, Y, s);
+      if (p->blocks) {
+        if (M <= 8) return launch_r_any<GSH, 8, true>(p, X, M, Y, s);
+        return launch_r_any<GSH, 16, true>(p, X, M, Y, s);
+      }
+      if (M <= 8) return launch_r_any<GSH, 8, false>(p, X, M, Y, s);
+      return launch_r_any<GSH, 16, false>(p, X, M, Y, s);
     }
     if ((size_t)M * (p->K + kXPad) * 2 <= kXldsMax) return run_x<MB, GSH, 1>(p, X, M, Y, s);
   }

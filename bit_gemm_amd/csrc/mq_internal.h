@@ -69,6 +69,9 @@ struct mq_packed {
   int32_t* blk;         // [nblk] block indices rb * Kt + kt, ascending
   float* bscale;        // [nblk][16] residual scale of each block row
   uint8_t* bcodes;      // [nblk][16][64] residual codes u = qr + 8, even column in the low nibble
+  uint32_t* rt_ptr;     // [Nb + 1]: the blocks of row block rb are blk[rt_ptr[rb] .. rt_ptr[rb + 1])
+  uint8_t* rt_tiles;    // [nblk + 1][1 KiB]: the blocks' codes in the code-tile layout; slot nblk
+                        // (like blk[nblk] = 0 and bscale[nblk][*] = 0) is an all-zero residual
 };
 
 namespace mq {

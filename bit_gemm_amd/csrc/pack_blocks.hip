@@ -23,7 +23,10 @@
 //   5. k_block_emit: the residual stream the fused kernels read (entries with
 //      fp16(sr qr), and the patched weights fp16(s q + fp16(sr qr))), in the
 //      same (row block, tile, row, column) order as element-wise packing, so
-//      the decode and prefill kernels run these handles unchanged.
+//      the prefill and general decode kernels run these handles unchanged;
+//      the blocks are also kept as 4-bit code tiles (with k_block_rtptr's
+//      per-row-block ranges), which the K = 4096 decode kernels multiply on
+//      the MFMA path like the base tiles.
 #include "mq_internal.h"
 #include "pack_common.h"
 #include "quant_exact.h"
@@ -168,6 +171,7 @@ __global__ __launch_bounds__(kWave) void k_block_codes(const uint16_t* __restric
                                                        const uint16_t* __restrict__ scales, int N, int K, int G,
                                                        int Kt, int64_t sstride, const int32_t* __restrict__ blk,
                                                        float* __restrict__ bscale, uint8_t* __restrict__ bcodes,
+                                                       uint8_t* __restrict__ rt_tiles,
                                                        uint32_t* __restrict__ row_cnt,
                                                        uint32_t* __restrict__ tile_cnt,
                                                        unsigned long long* __restrict__ nnz) {
@@ -188,6 +192,17 @@ __global__ __launch_bounds__(kWave) void k_block_codes(const uint16_t* __restric
   uint8_t* dst = bcodes + ((int64_t)n * kRowsPerBlock + r) * (kTileCols / 2) + 16 * kq;
 #pragma unroll
   for (int t = 0; t < 16; ++t) dst[t] = (uint8_t)(u[r][32 * kq + 2 * t] | (u[r][32 * kq + 2 * t + 1] << 4));
+  // the same codes in the code-tile layout (as the base tiles): lane r + 16 g,
+  // dword s4 holds columns 32 s4 + 8 g + c at nibble nib_pos(c)
+  uint32_t d[4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v |= (uint32_t)u[r][32 * s4 + 8 * kq + c] << (4 * nib_pos(c));
+    d[s4] = v;
+  }
+  reinterpret_cast<uint4*>(rt_tiles)[(int64_t)n * kWave + lane] = make_uint4(d[0], d[1], d[2], d[3]);
   uint32_t ex, tot;
   row_lanes(nz, lane, &ex, &tot);
   if (kq == 0) row_cnt[(int64_t)n * kRowsPerBlock + r] = tot;
@@ -198,6 +213,22 @@ __global__ __launch_bounds__(kWave) void k_block_codes(const uint16_t* __restric
     tile_cnt[b] = v;
     atomicAdd(nnz, (unsigned long long)v);
   }
+}
+
+// rt_ptr[rb] = first selected block of row block rb (blk is ascending, so a
+// row block's blocks are contiguous): a lower bound by binary search.
+__global__ __launch_bounds__(256) void k_block_rtptr(const int32_t* __restrict__ blk, int64_t nsel, int64_t Nb,
+                                                     int Kt, uint32_t* __restrict__ rt_ptr) {
+  const int64_t rb = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (rb > Nb) return;
+  const int64_t key = rb * Kt;
+  int64_t lo = 0, hi = nsel;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if ((int64_t)blk[mid] < key) lo = mid + 1;
+    else hi = mid;
+  }
+  rt_ptr[rb] = (uint32_t)lo;
 }
 
 // A row block's stream segment ends on a whole 32-entry chunk (zero entries).
@@ -291,6 +322,11 @@ hipError_t pack_blocks_on_device(const uint16_t* W, const float* h, mq_packed* p
   MQ_TRY(hipMemsetAsync(p->entries, 0, (size_t)(p->stream_cap + kEntryPad) * sizeof(uint32_t), stream));
   MQ_TRY(hipMemsetAsync(p->wpatch, 0, (size_t)(p->stream_cap + kEntryPad) * sizeof(uint32_t), stream));
   MQ_TRY(launch_pack_base(W, p, st, stream));
+  // the all-zero block slot nblk: block 0's column tile, scales 0, codes 8 (q = 0)
+  MQ_TRY(hipMemsetAsync(p->blk + nsel, 0, sizeof(int32_t), stream));
+  MQ_TRY(hipMemsetAsync(p->bscale + nsel * kRowsPerBlock, 0, kRowsPerBlock * sizeof(float), stream));
+  MQ_TRY(hipMemsetAsync(p->rt_tiles + nsel * kTileBytes, 0x88, kTileBytes, stream));
+  MQ_TRY(hipMemsetAsync(p->rt_ptr, 0, (size_t)(Nb + 1) * sizeof(uint32_t), stream));
 
   MQ_TRY(hipMalloc(&t_keys.p, (size_t)ntiles * sizeof(uint64_t)));
   MQ_TRY(hipMalloc(&t_tc.p, (size_t)ntiles * sizeof(uint32_t)));
@@ -308,8 +344,10 @@ hipError_t pack_blocks_on_device(const uint16_t* W, const float* h, mq_packed* p
     k_block_select<<<dim3(1), dim3(1024), 0, stream>>>(keys, ntiles, nsel, p->blk);
     MQ_TRY(hipGetLastError());
     k_block_codes<<<dim3((unsigned)nsel), dim3(kWave), 0, stream>>>(
-        W, p->scales, N, K, G, Kt, p->sstride, p->blk, p->bscale, p->bcodes, rcnt, tcnt,
+        W, p->scales, N, K, G, Kt, p->sstride, p->blk, p->bscale, p->bcodes, p->rt_tiles, rcnt, tcnt,
         static_cast<unsigned long long*>(t_nnz.p));
+    MQ_TRY(hipGetLastError());
+    k_block_rtptr<<<dim3((unsigned)((Nb + 1 + 255) / 256)), dim3(256), 0, stream>>>(p->blk, nsel, Nb, Kt, p->rt_ptr);
     MQ_TRY(hipGetLastError());
     k_block_pad<<<dim3((unsigned)((Nb + 255) / 256)), dim3(256), 0, stream>>>(tcnt, Nb, Kt);
     MQ_TRY(hipGetLastError());

@@ -50,8 +50,11 @@ def _assert_blocks_equal(got, base, ref):
     assert np.array_equal(got["rcodes"], ref["rcodes"]), "block codes differ"
 
 
+# K = 4096 runs the decode kernels that carry the blocks as code tiles
+# (4200 rows: several row blocks per workgroup at M > 4)
 SHAPES = [(16, 128, 128, 0.5), (48, 256, 128, 0.25), (37, 384, 64, 0.3), (130, 4224, 128, 0.1),
-          (20, 96, 32, 1.0), (64, 1024, 128, 0.0), (257, 2048, 32, 0.07)]
+          (20, 96, 32, 1.0), (64, 1024, 128, 0.0), (257, 2048, 32, 0.07), (40, 4096, 128, 0.2),
+          (24, 4096, 32, 0.3), (90, 4096, 64, 1.0), (4200, 4096, 128, 0.05)]
 
 
 @pytest.mark.parametrize("N,K,G,beta", SHAPES)
