@@ -35,7 +35,8 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 void release(mq_packed* p) {
   void* bufs[] = {p->tiles,    p->scales,  p->row_ptr, p->col,    p->rcodes, p->rscale,  p->tile_ptr,
-                  p->entries, p->wpatch,  p->blk,     p->bscale, p->bcodes, p->rt_ptr, p->rt_tiles};
+                  p->entries, p->wpatch,  p->blk,     p->bscale, p->bcodes, p->rt_ptr, p->rt_tiles,
+                  p->rt_slot};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   p->magic = 0;
@@ -218,7 +219,8 @@ MQ_API mq_status mq_pack_blocks(const void* W_dev_fp16, int64_t N, int64_t K, in
                 {(void**)&p->bscale, nb1 * mq::kRowsPerBlock * sizeof(float)},
                 {(void**)&p->bcodes, nb1 * mq::kRowsPerBlock * (mq::kTileCols / 2)},
                 {(void**)&p->rt_ptr, (size_t)(p->Nb + 1) * sizeof(uint32_t)},
-                {(void**)&p->rt_tiles, nb1 * mq::kTileBytes}};
+                {(void**)&p->rt_tiles, nb1 * mq::kTileBytes},
+                {(void**)&p->rt_slot, n_tiles * sizeof(int32_t)}};
   size_t total = 0;
   for (auto& a : allocs) {
     e = hipMalloc(a.dst, a.n);

@@ -18,6 +18,10 @@
 //     interleave with the current stage's MFMAs; one barrier per stage;
 //   * workgroups are ordered so that consecutive tiles of one 256-token
 //     slice run on the same XCD and share its L2 for X.
+// Handles from mq_pack_blocks (Methodology section 2: residual blocks) carry
+// their residual as 4-bit code tiles; for them (DR) each stage also widens
+// the tile's residual codes with the row's residual scale and adds them to
+// the staged weights, instead of patching single entries.
 #include <algorithm>
 #include <type_traits>
 
@@ -83,16 +87,31 @@ struct TilePtrs {
   uint32_t p0[RB], cnt[RB];
 };
 
-template <int RB>
-__device__ __forceinline__ void load_ptrs(TilePtrs<RB>& P, const uint32_t* __restrict__ tile_ptr, int Kt, int Nb,
-                                          int rbw, int kt) {
+// Block residual kept as 4-bit code tiles (handles from mq_pack_blocks):
+// slot[rb * Kt + kt] is the residual tile of (rb, kt), or an all-zero slot;
+// tiles in the base tile layout, one fp32 scale per row.
+struct DenseGemm {
+  const int32_t* slot;
+  const uint2* tiles;
+  const float* scale;
+};
+
+// DR: p0 holds the residual slot of the tile (no patched-weight entries).
+template <bool DR, int RB>
+__device__ __forceinline__ void load_ptrs(TilePtrs<RB>& P, const uint32_t* __restrict__ tile_ptr,
+                                          const DenseGemm& dr, int Kt, int Nb, int rbw, int kt) {
 #pragma unroll
   for (int j = 0; j < RB; ++j) {
     const bool ok = rbw + j < Nb && kt < Kt;
     const int64_t t = (int64_t)min(rbw + j, Nb - 1) * Kt + min(kt, Kt - 1);
-    const uint32_t p0 = tile_ptr[t], p1 = tile_ptr[t + 1];
-    P.p0[j] = p0;
-    P.cnt[j] = ok ? p1 - p0 : 0u;
+    if constexpr (DR) {
+      P.p0[j] = (uint32_t)dr.slot[t];
+      P.cnt[j] = 0u;
+    } else {
+      const uint32_t p0 = tile_ptr[t], p1 = tile_ptr[t + 1];
+      P.p0[j] = p0;
+      P.cnt[j] = ok ? p1 - p0 : 0u;
+    }
   }
 }
 
@@ -109,8 +128,10 @@ struct HalfRegs {
   uint2 code[RB];        // dwords 2h, 2h + 1 of the lane's 16-byte slice of the tile
   uint32_t sraw[RB];     // the aligned dword of the lane's scale row holding this stage's scale(s)
   uint32_t sel;          // byte selector of the scale in it (G = 128 / 64; scalar)
-  uint32_t ent[RB];      // patched-weight entry p0 + lane of the tile's segment (valid when lane < cnt)
+  uint32_t ent[RB];      // patched-weight entry p0 + lane of the tile's segment (valid when lane < cnt);
+                         // DR: fp32 bits of the residual scale of the lane's row
   uint32_t cnt[RB];      // entries in the tile's segment (scalar)
+  uint2 rcode[RB];       // DR: the same two dwords of the tile's residual codes
 };
 
 template <int RB>
@@ -123,11 +144,11 @@ __device__ __forceinline__ bool has_long_segment(const HalfRegs<RB>& H) {
 
 // Branch- and wait-free: clamped indices keep every load in bounds (1024 zero
 // entries follow the stream, so p0 + lane is always readable).
-template <int GSH, int RB>
+template <int GSH, bool DR, int RB>
 __device__ __forceinline__ void load_half(HalfRegs<RB>& H, const TilePtrs<RB>& P, const uint4* __restrict__ tiles,
                                           const uint16_t* __restrict__ scales, int64_t sstride,
-                                          const uint32_t* __restrict__ wpatch, int Kt, int Nb, int rbw, int kt, int h,
-                                          int lane) {
+                                          const uint32_t* __restrict__ wpatch, const DenseGemm& dr, int Kt, int Nb,
+                                          int rbw, int kt, int h, int lane) {
   const int r = lane & 15;
 #pragma unroll
   for (int j = 0; j < RB; ++j) {
@@ -141,7 +162,12 @@ __device__ __forceinline__ void load_half(HalfRegs<RB>& H, const TilePtrs<RB>& P
     if constexpr (GSH == 0) H.sraw[j] = reinterpret_cast<const uint32_t*>(srow)[ktc >> 1];
     else if constexpr (GSH == 1) H.sraw[j] = reinterpret_cast<const uint32_t*>(srow)[ktc];
     else H.sraw[j] = *reinterpret_cast<const uint32_t*>(srow + 4 * ktc + 2 * h);
-    H.ent[j] = wpatch[P.p0[j] + lane];
+    if constexpr (DR) {
+      H.rcode[j] = dr.tiles[((int64_t)P.p0[j] * 64 + lane) * 2 + h];
+      H.ent[j] = __builtin_bit_cast(uint32_t, dr.scale[(int64_t)P.p0[j] * kRowsPerBlock + r]);
+    } else {
+      H.ent[j] = wpatch[P.p0[j] + lane];
+    }
     H.cnt[j] = P.cnt[j];
   }
   H.sel = (GSH == 0 ? (min(kt, Kt - 1) & 1) : h) ? kSelHi : kSelLo;
@@ -190,7 +216,9 @@ __device__ __forceinline__ void store_x(const uint4 (&x)[XR], _Float16* Xs, int 
 // becomes an exec-masked branch, and branches split the stage into separate
 // scheduling regions, which keeps the widening from interleaving with the
 // MFMAs.
-template <int GSH, int RB>
+// DR: the residual tile's codes are widened the same way with the row's
+// residual scale (rounded to fp16) and added in fp16; no patches follow.
+template <int GSH, bool DR, int RB>
 __device__ __forceinline__ void write_w(const HalfRegs<RB>& H, _Float16* Ws, _Float16* dummy, int lrb0, int h,
                                         int lane, uint32_t vmask, uint32_t vmask4, uint32_t vmagic) {
   const int r = lane & 15, g = lane >> 4;
@@ -199,9 +227,18 @@ __device__ __forceinline__ void write_w(const HalfRegs<RB>& H, _Float16* Ws, _Fl
     _Float16* dst = Ws + ((lrb0 + j) * kRowsPerBlock + r) * LDW + 8 * g;
     const half2_t s0 = splat_sel(H.sraw[j], GSH == 2 ? kSelLo : H.sel);
     const half2_t s1 = GSH == 2 ? splat_sel(H.sraw[j], kSelHi) : s0;
-    *reinterpret_cast<half8_t*>(dst) = dequant_dword(H.code[j].x, s0, vmask, vmask4, vmagic);
-    *reinterpret_cast<half8_t*>(dst + 32) = dequant_dword(H.code[j].y, s1, vmask, vmask4, vmagic);
+    half8_t w0 = dequant_dword(H.code[j].x, s0, vmask, vmask4, vmagic);
+    half8_t w1 = dequant_dword(H.code[j].y, s1, vmask, vmask4, vmagic);
+    if constexpr (DR) {
+      const _Float16 sr = (_Float16)__builtin_bit_cast(float, H.ent[j]);
+      const half2_t srs = {sr, sr};
+      w0 += dequant_dword(H.rcode[j].x, srs, vmask, vmask4, vmagic);
+      w1 += dequant_dword(H.rcode[j].y, srs, vmask, vmask4, vmagic);
+    }
+    *reinterpret_cast<half8_t*>(dst) = w0;
+    *reinterpret_cast<half8_t*>(dst + 32) = w1;
   }
+  if constexpr (DR) return;
 #pragma unroll
   for (int j = 0; j < RB; ++j) {
     const uint32_t v = H.ent[j];
@@ -222,7 +259,7 @@ __device__ __forceinline__ void patch_rest(const uint32_t* __restrict__ tile_ptr
                                            _Float16* Ws, int lrb0, int h, int lane,
                                            const uint32_t* __restrict__ wpatch) {
   TilePtrs<RB> P;
-  load_ptrs(P, tile_ptr, Kt, Nb, rbw, kt);
+  load_ptrs<false>(P, tile_ptr, DenseGemm{}, Kt, Nb, rbw, kt);
   for (int j = 0; j < RB; ++j) {
     for (uint32_t e = P.p0[j] + 64 + lane; e < P.p0[j] + P.cnt[j]; e += 64) {
       const uint32_t v = wpatch[e];
@@ -271,14 +308,14 @@ __device__ __forceinline__ int xcd_tile(int b, int T) {
   return x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
 }
 
-template <int GSH, bool KTAIL, class C>
+template <int GSH, bool KTAIL, class C, bool DR>
 __global__ __launch_bounds__(C::kThreads, 1) void k_gemm(const uint4* __restrict__ tiles,
                                                       const uint16_t* __restrict__ scales, int64_t sstride,
                                                       const uint32_t* __restrict__ tile_ptr,
                                                       const uint32_t* __restrict__ wpatch,
                                                       const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
                                                       float* __restrict__ part, int M, int N, int K, int Kt, int Nb,
-                                                      int NT, int T, int kt_per_split) {
+                                                      int NT, int T, int kt_per_split, DenseGemm dr) {
   extern __shared__ __attribute__((aligned(16))) _Float16 lds[];
   constexpr int BM = C::kBM;
   _Float16* const dummy = reinterpret_cast<_Float16*>(reinterpret_cast<char*>(lds) + C::kDummyOff);
@@ -317,38 +354,38 @@ __global__ __launch_bounds__(C::kThreads, 1) void k_gemm(const uint4* __restrict
   TilePtrs<RB> pa, pb;
   if constexpr (C::kPd == 2) {
   uint4 xr[XR];
-  load_ptrs(pa, tile_ptr, Kt, Nb, rbw, kt0);
-  load_half<GSH>(H0, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt0, 0, lane);
-  load_half<GSH>(H1, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt0, 1, lane);
+  load_ptrs<DR>(pa, tile_ptr, dr, Kt, Nb, rbw, kt0);
+  load_half<GSH, DR>(H0, pa, tiles, scales, sstride, wpatch, dr, Kt, Nb, rbw, kt0, 0, lane);
+  load_half<GSH, DR>(H1, pa, tiles, scales, sstride, wpatch, dr, Kt, Nb, rbw, kt0, 1, lane);
   load_x<KTAIL, XR, TH>(xr, xrs, xoff, K, 2 * kt0 * BK, tid);
-  write_w<GSH>(H0, buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
+  write_w<GSH, DR>(H0, buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
   if (has_long_segment(H0)) patch_rest<RB>(tile_ptr, Kt, Nb, rbw, kt0, buf0, lrb0, 0, lane, wpatch);
   store_x<XR, TH>(xr, buf0 + BN * LDW, tid);
   load_x<KTAIL, XR, TH>(xr, xrs, xoff, K, (2 * kt0 + 1) * BK, tid);
-  load_ptrs(pa, tile_ptr, Kt, Nb, rbw, kt0 + 1);
-  load_half<GSH>(H0, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt0 + 1, 0, lane);
-  load_ptrs(pb, tile_ptr, Kt, Nb, rbw, kt0 + 2);
+  load_ptrs<DR>(pa, tile_ptr, dr, Kt, Nb, rbw, kt0 + 1);
+  load_half<GSH, DR>(H0, pa, tiles, scales, sstride, wpatch, dr, Kt, Nb, rbw, kt0 + 1, 0, lane);
+  load_ptrs<DR>(pb, tile_ptr, dr, Kt, Nb, rbw, kt0 + 2);
   __syncthreads();
 
   for (int kt = kt0; kt < kt1; ++kt) {
     // stage 2 kt (buffer 0) runs; stage 2 kt + 1 (H1: half 1 of tile kt) is prepared in buffer 1
     mfma_stage(acc, buf0, buf0 + BN * LDW, wn, wm, lane);
-    write_w<GSH>(H1, buf1, dummy, lrb0, 1, lane, vmask, vmask4, vmagic);
+    write_w<GSH, DR>(H1, buf1, dummy, lrb0, 1, lane, vmask, vmask4, vmagic);
     store_x<XR, TH>(xr, buf1 + BN * LDW, tid);
     load_x<KTAIL, XR, TH>(xr, xrs, xoff, K, (2 * kt + 2) * BK, tid);
     const bool long1 = has_long_segment(H1);
-    load_half<GSH>(H1, pa, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt + 1, 1, lane);
-    load_ptrs(pa, tile_ptr, Kt, Nb, rbw, kt + 2);
+    load_half<GSH, DR>(H1, pa, tiles, scales, sstride, wpatch, dr, Kt, Nb, rbw, kt + 1, 1, lane);
+    load_ptrs<DR>(pa, tile_ptr, dr, Kt, Nb, rbw, kt + 2);
     if (long1) patch_rest<RB>(tile_ptr, Kt, Nb, rbw, kt, buf1, lrb0, 1, lane, wpatch);
     __syncthreads();
     // stage 2 kt + 1 (buffer 1) runs; stage 2 kt + 2 (H0: half 0 of tile kt + 1) is prepared in buffer 0
     mfma_stage(acc, buf1, buf1 + BN * LDW, wn, wm, lane);
-    write_w<GSH>(H0, buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
+    write_w<GSH, DR>(H0, buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
     store_x<XR, TH>(xr, buf0 + BN * LDW, tid);
     load_x<KTAIL, XR, TH>(xr, xrs, xoff, K, (2 * kt + 3) * BK, tid);
     const bool long0 = has_long_segment(H0);
-    load_half<GSH>(H0, pb, tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt + 2, 0, lane);
-    load_ptrs(pb, tile_ptr, Kt, Nb, rbw, kt + 3);
+    load_half<GSH, DR>(H0, pb, tiles, scales, sstride, wpatch, dr, Kt, Nb, rbw, kt + 2, 0, lane);
+    load_ptrs<DR>(pb, tile_ptr, dr, Kt, Nb, rbw, kt + 3);
     if (long0) patch_rest<RB>(tile_ptr, Kt, Nb, rbw, kt + 1, buf0, lrb0, 0, lane, wpatch);
     __syncthreads();
   }
@@ -366,19 +403,21 @@ __global__ __launch_bounds__(C::kThreads, 1) void k_gemm(const uint4* __restrict
     HalfRegs<RB> H[PD];
     TilePtrs<RB> Pr[2];
     uint4 xq[PD][XR];
-    load_ptrs(Pr[0], tile_ptr, Kt, Nb, rbw, kt0);
-    load_ptrs(Pr[1], tile_ptr, Kt, Nb, rbw, kt0 + 1);
+    load_ptrs<DR>(Pr[0], tile_ptr, dr, Kt, Nb, rbw, kt0);
+    load_ptrs<DR>(Pr[1], tile_ptr, dr, Kt, Nb, rbw, kt0 + 1);
 #pragma unroll
     for (int u = 0; u < PD; ++u) {
       load_x<KTAIL, XR, TH>(xq[u], xrs, xoff, K, (sb + u) * BK, tid);
-      load_half<GSH>(H[u], Pr[(u >> 1) & 1], tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt0 + (u >> 1), u & 1, lane);
-      if (u & 1) load_ptrs(Pr[(u >> 1) & 1], tile_ptr, Kt, Nb, rbw, kt0 + (u >> 1) + 2);
+      load_half<GSH, DR>(H[u], Pr[(u >> 1) & 1], tiles, scales, sstride, wpatch, dr, Kt, Nb, rbw, kt0 + (u >> 1),
+                         u & 1, lane);
+      if (u & 1) load_ptrs<DR>(Pr[(u >> 1) & 1], tile_ptr, dr, Kt, Nb, rbw, kt0 + (u >> 1) + 2);
     }
-    write_w<GSH>(H[0], buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
+    write_w<GSH, DR>(H[0], buf0, dummy, lrb0, 0, lane, vmask, vmask4, vmagic);
     if (has_long_segment(H[0])) patch_rest<RB>(tile_ptr, Kt, Nb, rbw, kt0, buf0, lrb0, 0, lane, wpatch);
     store_x<XR, TH>(xq[0], buf0 + BN * LDW, tid);
     load_x<KTAIL, XR, TH>(xq[0], xrs, xoff, K, (sb + PD) * BK, tid);
-    load_half<GSH>(H[0], Pr[(PD >> 1) & 1], tiles, scales, sstride, wpatch, Kt, Nb, rbw, kt0 + PD / 2, 0, lane);
+    load_half<GSH, DR>(H[0], Pr[(PD >> 1) & 1], tiles, scales, sstride, wpatch, dr, Kt, Nb, rbw, kt0 + PD / 2, 0,
+                       lane);
     __syncthreads();
 
     // stage s of the ring (U = (s - sb) % PD, a constant)
@@ -389,12 +428,12 @@ __global__ __launch_bounds__(C::kThreads, 1) void k_gemm(const uint4* __restrict
       constexpr int v = (u + 1) % PD, h = (u + 1) & 1, pr = ((u + 1 + PD) >> 1) & 1;
       const int kl = kt0 + ((s + 1 + PD - sb) >> 1);   // tile of the stage requested now
       mfma_stage(acc, cur, cur + BN * LDW, wn, wm, lane);
-      write_w<GSH>(H[v], nxt, dummy, lrb0, h, lane, vmask, vmask4, vmagic);
+      write_w<GSH, DR>(H[v], nxt, dummy, lrb0, h, lane, vmask, vmask4, vmagic);
       store_x<XR, TH>(xq[v], nxt + BN * LDW, tid);
       load_x<KTAIL, XR, TH>(xq[v], xrs, xoff, K, (s + 1 + PD) * BK, tid);
       const bool lng = has_long_segment(H[v]);
-      load_half<GSH>(H[v], Pr[pr], tiles, scales, sstride, wpatch, Kt, Nb, rbw, kl, h, lane);
-      if (h) load_ptrs(Pr[pr], tile_ptr, Kt, Nb, rbw, kl + 2);
+      load_half<GSH, DR>(H[v], Pr[pr], tiles, scales, sstride, wpatch, dr, Kt, Nb, rbw, kl, h, lane);
+      if (h) load_ptrs<DR>(Pr[pr], tile_ptr, dr, Kt, Nb, rbw, kl + 2);
       if (lng) patch_rest<RB>(tile_ptr, Kt, Nb, rbw, kt0 + ((s + 1 - sb) >> 1), nxt, lrb0, h, lane, wpatch);
       __syncthreads();
     };
@@ -488,12 +527,12 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   store4(Y + (int64_t)m * N + n0, sum, N - n0, (N & 3) == 0);
 }
 
-template <int GSH, bool KTAIL, class C>
+template <int GSH, bool KTAIL, class C, bool DR>
 hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
   constexpr int BM = C::kBM;
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<GSH, KTAIL, C>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<GSH, KTAIL, C, DR>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -513,9 +552,11 @@ hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y,
     const hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&part), (size_t)S * M * p->N * sizeof(float), s);
     if (e != hipSuccess) return e;
   }
-  k_gemm<GSH, KTAIL, C><<<dim3((unsigned)T, (unsigned)S), dim3(C::kThreads), C::kLdsBytes, s>>>(
+  const DenseGemm dr = DR ? DenseGemm{p->rt_slot, reinterpret_cast<const uint2*>(p->rt_tiles), p->bscale}
+                          : DenseGemm{nullptr, nullptr, nullptr};
+  k_gemm<GSH, KTAIL, C, DR><<<dim3((unsigned)T, (unsigned)S), dim3(C::kThreads), C::kLdsBytes, s>>>(
       reinterpret_cast<const uint4*>(p->tiles), p->scales, p->sstride, p->tile_ptr, p->wpatch, X, Y, part, (int)M,
-      (int)p->N, (int)p->K, Kt, (int)p->Nb, NT, T, per);
+      (int)p->N, (int)p->K, Kt, (int)p->Nb, NT, T, per, dr);
   hipError_t e = hipGetLastError();
   if (S > 1) {
     if (e == hipSuccess) {
@@ -529,16 +570,22 @@ hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y,
 
 }  // namespace
 
-template <bool KTAIL, class C>
+template <bool KTAIL, class C, bool DR>
 hipError_t launch_g(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
-  if (p->G == 128) return launch<0, KTAIL, C>(p, X, M, Y, s);
-  if (p->G == 64) return launch<1, KTAIL, C>(p, X, M, Y, s);
-  return launch<2, KTAIL, C>(p, X, M, Y, s);
+  if (p->G == 128) return launch<0, KTAIL, C, DR>(p, X, M, Y, s);
+  if (p->G == 64) return launch<1, KTAIL, C, DR>(p, X, M, Y, s);
+  return launch<2, KTAIL, C, DR>(p, X, M, Y, s);
+}
+
+// handles from mq_pack_blocks carry their residual as code tiles (DR)
+template <bool KTAIL, class C>
+hipError_t launch_d(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
+  return p->blocks ? launch_g<KTAIL, C, true>(p, X, M, Y, s) : launch_g<KTAIL, C, false>(p, X, M, Y, s);
 }
 
 template <bool KTAIL>
 hipError_t launch_k(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
-  return M <= kNarrowMaxM ? launch_g<KTAIL, CfgNarrow>(p, X, M, Y, s) : launch_g<KTAIL, CfgWide>(p, X, M, Y, s);
+  return M <= kNarrowMaxM ? launch_d<KTAIL, CfgNarrow>(p, X, M, Y, s) : launch_d<KTAIL, CfgWide>(p, X, M, Y, s);
 }
 
 hipError_t launch_splitk_reduce(const float* part, uint16_t* Y, int64_t M, int64_t N, int S, hipStream_t s) {

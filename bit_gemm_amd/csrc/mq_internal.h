@@ -72,6 +72,7 @@ struct mq_packed {
   uint32_t* rt_ptr;     // [Nb + 1]: the blocks of row block rb are blk[rt_ptr[rb] .. rt_ptr[rb + 1])
   uint8_t* rt_tiles;    // [nblk + 1][1 KiB]: the blocks' codes in the code-tile layout; slot nblk
                         // (like blk[nblk] = 0 and bscale[nblk][*] = 0) is an all-zero residual
+  int32_t* rt_slot;     // [Nb * Kt]: the residual slot of each tile (nblk where it has none)
 };
 
 namespace mq {

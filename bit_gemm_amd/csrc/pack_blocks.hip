@@ -25,8 +25,9 @@
 //      same (row block, tile, row, column) order as element-wise packing, so
 //      the prefill and general decode kernels run these handles unchanged;
 //      the blocks are also kept as 4-bit code tiles (with k_block_rtptr's
-//      per-row-block ranges), which the K = 4096 decode kernels multiply on
-//      the MFMA path like the base tiles.
+//      per-row-block ranges and k_block_slots' per-tile slots), which the
+//      K = 4096 decode kernels multiply on the MFMA path like the base tiles
+//      and the prefill GEMM widens into the weight tile it stages.
 #include "mq_internal.h"
 #include "pack_common.h"
 #include "quant_exact.h"
@@ -231,6 +232,19 @@ __global__ __launch_bounds__(256) void k_block_rtptr(const int32_t* __restrict__
   rt_ptr[rb] = (uint32_t)lo;
 }
 
+// rt_slot[b] = n for the n-th selected block b, the zero slot nsel elsewhere.
+__global__ __launch_bounds__(256) void k_block_slots(const int32_t* __restrict__ blk, int64_t nsel, int64_t ntiles,
+                                                     int32_t* __restrict__ rt_slot) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < ntiles) rt_slot[i] = (int32_t)nsel;
+}
+
+__global__ __launch_bounds__(256) void k_block_slots_set(const int32_t* __restrict__ blk, int64_t nsel,
+                                                         int32_t* __restrict__ rt_slot) {
+  const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (n < nsel) rt_slot[blk[n]] = (int32_t)n;
+}
+
 // A row block's stream segment ends on a whole 32-entry chunk (zero entries).
 __global__ __launch_bounds__(256) void k_block_pad(uint32_t* __restrict__ tile_cnt, int64_t Nb, int Kt) {
   const int64_t rb = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -327,6 +341,8 @@ hipError_t pack_blocks_on_device(const uint16_t* W, const float* h, mq_packed* p
   MQ_TRY(hipMemsetAsync(p->bscale + nsel * kRowsPerBlock, 0, kRowsPerBlock * sizeof(float), stream));
   MQ_TRY(hipMemsetAsync(p->rt_tiles + nsel * kTileBytes, 0x88, kTileBytes, stream));
   MQ_TRY(hipMemsetAsync(p->rt_ptr, 0, (size_t)(Nb + 1) * sizeof(uint32_t), stream));
+  k_block_slots<<<dim3((unsigned)((ntiles + 255) / 256)), dim3(256), 0, stream>>>(p->blk, nsel, ntiles, p->rt_slot);
+  MQ_TRY(hipGetLastError());
 
   MQ_TRY(hipMalloc(&t_keys.p, (size_t)ntiles * sizeof(uint64_t)));
   MQ_TRY(hipMalloc(&t_tc.p, (size_t)ntiles * sizeof(uint32_t)));
@@ -348,6 +364,8 @@ hipError_t pack_blocks_on_device(const uint16_t* W, const float* h, mq_packed* p
         static_cast<unsigned long long*>(t_nnz.p));
     MQ_TRY(hipGetLastError());
     k_block_rtptr<<<dim3((unsigned)((Nb + 1 + 255) / 256)), dim3(256), 0, stream>>>(p->blk, nsel, Nb, Kt, p->rt_ptr);
+    MQ_TRY(hipGetLastError());
+    k_block_slots_set<<<dim3((unsigned)((nsel + 255) / 256)), dim3(256), 0, stream>>>(p->blk, nsel, p->rt_slot);
     MQ_TRY(hipGetLastError());
     k_block_pad<<<dim3((unsigned)((Nb + 255) / 256)), dim3(256), 0, stream>>>(tcnt, Nb, Kt);
     MQ_TRY(hipGetLastError());
