@@ -4,18 +4,21 @@
 // residual inside the dense 4-bit GEMM so X is read once and no partial
 // outputs are merged afterwards. Here the residual is folded into the dense
 // weight tile before the matrix cores consume it:
-//   * a workgroup of 4 waves computes a 256 (output features) x 256 (tokens)
-//     tile, each wave a 128 x 128 block of 4 x 4 32x32x16 fp16 MFMAs with
-//     fp32 accumulators;
+//   * a workgroup of 8 waves computes a 256 (output features) x 256 (tokens)
+//     tile, each wave a 128 x 64 block of 4 x 2 32x32x16 fp16 MFMAs with
+//     fp32 accumulators (two waves per SIMD); up to 128 tokens a 256 x 64
+//     tile of 8 waves of 32 x 64 (Cfg); when the tiles cannot fill the GPU,
+//     K is split across workgroups and a second kernel adds the fp32 parts;
 //   * K advances in stages of 64 columns (half a code tile), double-buffered
 //     in LDS: the weight stage is widened from the 4-bit tiles to fp16(s q)
-//     by the wave that owns those 4 row blocks, which then patches the
+//     by the wave that owns those 2 row blocks, which then patches the
 //     stage's residual entries into it (fp16(s q + sr qr), rounded once) --
 //     a wave's LDS operations execute in order, so no barrier is needed
 //     between its writes and its patches; X is staged through registers;
-//   * one loop iteration is one code tile (two stages); its body has no
-//     branches, so the widening, patching and X staging of the next stage
-//     interleave with the current stage's MFMAs; one barrier per stage;
+//   * one loop iteration is one code tile (two stages; four with the
+//     narrow tile's ring); its body has no branches, so the widening,
+//     patching and X staging of the next stage interleave with the current
+//     stage's MFMAs; one barrier per stage;
 //   * workgroups are ordered so that consecutive tiles of one 256-token
 //     slice run on the same XCD and share its L2 for X.
 // Handles from mq_pack_blocks (Methodology section 2: residual blocks) carry
