@@ -431,6 +431,28 @@ def bench_blocks(args, mq, synth, torch):
                                            "us": decode_us(lambda: mq.mq_pack(W, layer.group, rho))}
         pe.free()
         res["by_fraction"][str(beta)] = entry
+    # the prefill GEMM with 10 % of the blocks, against plain W4 and the
+    # element-wise residual of that layer (rho 1 %), on the 28672x8192 layer
+    pl = synth.WORKLOADS["prefill-28672x8192"].layers[0]
+    Wp = torch.from_numpy(pl.W()).cuda()
+    hp = (torch.from_numpy(pl.calibration(256, 4)).cuda().float() ** 2).sum(0)
+    pre = {}
+    for name, make in (("plain_w4", lambda: mq.mq_pack(Wp, pl.group, 0.0)),
+                       ("elementwise_rho_0.01", lambda: mq.mq_pack(Wp, pl.group, 0.01)),
+                       ("blocks_0.1", lambda: mq.mq_pack_blocks(Wp, pl.group, 0.1, hp))):
+        p = make()
+        pre[name] = {}
+        for M in (512, 2048):
+            X = torch.from_numpy(pl.X(M)).cuda()
+            Y = torch.empty((M, pl.N), dtype=torch.float16, device="cuda")
+
+            def run(i, X=X, Y=Y, p=p):
+                mq.mq_linear(X, p, Y)
+            time_events(run, 3)
+            us = time_events(run, 10) / 10 * 1e3
+            pre[name][str(M)] = {"us": round(us, 1), "TFLOPs": round(2.0 * M * pl.N * pl.K / us / 1e6, 1)}
+        p.free()
+    res["prefill_28672x8192"] = pre
     return res
 
 
