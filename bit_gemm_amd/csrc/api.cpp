@@ -281,6 +281,34 @@ MQ_API mq_status mq_export_blocks(const mq_packed* p, void* blk_i32, void* rscal
   return from_hip(e);
 }
 
+MQ_API mq_status mq_smooth_weights(const void* W_dev_fp16, int64_t N, int64_t K, const float* amax_x_dev_f32,
+                                   void* W_out_dev_fp16, int32_t* e_out_dev_i32, void* hip_stream) {
+  if (!W_dev_fp16 || !amax_x_dev_f32 || !W_out_dev_fp16 || !e_out_dev_i32) return MQ_ERR_INVALID_ARG;
+  if (N <= 0 || K <= 0) return MQ_ERR_INVALID_ARG;
+  if (N >= (int64_t(1) << 31) / K) return MQ_ERR_UNSUPPORTED;   // N * K < 2^31
+  if ((reinterpret_cast<uintptr_t>(W_dev_fp16) & 1u) || (reinterpret_cast<uintptr_t>(W_out_dev_fp16) & 1u) ||
+      (reinterpret_cast<uintptr_t>(amax_x_dev_f32) & 3u) || (reinterpret_cast<uintptr_t>(e_out_dev_i32) & 3u))
+    return MQ_ERR_INVALID_ARG;
+  uint32_t flags = 0;
+  const hipError_t e = mq::smooth_weights(static_cast<const uint16_t*>(W_dev_fp16), N, K, amax_x_dev_f32,
+                                          static_cast<uint16_t*>(W_out_dev_fp16), e_out_dev_i32,
+                                          static_cast<hipStream_t>(hip_stream), &flags);
+  if (e != hipSuccess) return from_hip(e);
+  return flags ? MQ_ERR_INVALID_ARG : MQ_OK;
+}
+
+MQ_API mq_status mq_smooth_activations(const void* X_dev_fp16, int64_t M, int64_t K, const int32_t* e_dev_i32,
+                                       void* X_out_dev_fp16, void* hip_stream) {
+  if (!X_dev_fp16 || !e_dev_i32 || !X_out_dev_fp16) return MQ_ERR_INVALID_ARG;
+  if (M <= 0 || K <= 0) return MQ_ERR_INVALID_ARG;
+  if (M >= (int64_t(1) << 31) / K) return MQ_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(X_dev_fp16) & 1u) || (reinterpret_cast<uintptr_t>(X_out_dev_fp16) & 1u) ||
+      (reinterpret_cast<uintptr_t>(e_dev_i32) & 3u))
+    return MQ_ERR_INVALID_ARG;
+  return from_hip(mq::smooth_activations(static_cast<const uint16_t*>(X_dev_fp16), M, K, e_dev_i32,
+                                         static_cast<uint16_t*>(X_out_dev_fp16), static_cast<hipStream_t>(hip_stream)));
+}
+
 MQ_API mq_status mq_linear(const void* X_dev_fp16, int64_t M, const mq_packed* p, void* Y_dev_fp16,
                            void* hip_stream) {
   return linear_impl(X_dev_fp16, M, p, Y_dev_fp16, hip_stream, MQ_KERNEL_AUTO);

@@ -93,6 +93,15 @@ hipError_t pack_blocks_on_device(const uint16_t* W, const float* h, mq_packed* p
 hipError_t launch_pack_base(const uint16_t* W, mq_packed* p, SelState* st, hipStream_t stream);
 hipError_t launch_scan_tiles(const uint32_t* tile_cnt, int64_t ntiles, uint32_t* tile_ptr, hipStream_t stream);
 
+// Outlier migration (migrate.hip): e_j and W^ = W 2^e (W_out may be W);
+// synchronises; *flags_out != 0 when an activation maximum is negative or not
+// finite.
+hipError_t smooth_weights(const uint16_t* W, int64_t N, int64_t K, const float* amax_x, uint16_t* W_out,
+                          int32_t* e_out, hipStream_t stream, uint32_t* flags_out);
+// X^ = X 2^-e (X_out may be X); enqueued only.
+hipError_t smooth_activations(const uint16_t* X, int64_t M, int64_t K, const int32_t* e, uint16_t* X_out,
+                              hipStream_t stream);
+
 // Canonical / tiled export (pack.hip).
 hipError_t export_codes(const mq_packed* p, uint8_t* codes, hipStream_t stream);
 

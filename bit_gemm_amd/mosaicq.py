@@ -23,7 +23,7 @@ GEMV_MAX_M = 64
 
 EXPORTED = ("mq_pack", "mq_linear", "mq_linear_with", "mq_residual_add", "mq_packed_info",
             "mq_export_canonical", "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks",
-            "mq_free", "mq_status_string")
+            "mq_smooth_weights", "mq_smooth_activations", "mq_free", "mq_status_string")
 
 
 class MQError(RuntimeError):
@@ -58,6 +58,10 @@ def _load():
     lib.mq_block_count.restype = ctypes.c_int
     lib.mq_export_blocks.argtypes = [vp] * 5
     lib.mq_export_blocks.restype = ctypes.c_int
+    lib.mq_smooth_weights.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+    lib.mq_smooth_weights.restype = ctypes.c_int
+    lib.mq_smooth_activations.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.mq_smooth_activations.restype = ctypes.c_int
     lib.mq_free.argtypes = [vp]
     lib.mq_free.restype = None
     lib.mq_status_string.argtypes = [ctypes.c_int]
@@ -174,6 +178,36 @@ def export_blocks(packed: Packed, stream=None) -> dict:
            "mq_export_blocks")
     torch.cuda.synchronize()
     return {k: v.cpu().numpy()[:B] for k, v in out.items()}
+
+
+def mq_smooth_weights(W, amax_x, stream=None):
+    """(W^, e): activation outliers moved into W (see mq_smooth_weights in
+    include/mosaicq.h); amax_x: float32 [K] device tensor."""
+    import torch
+    ptr = _dev_fp16(W, "W")
+    N, K = W.shape
+    if not isinstance(amax_x, torch.Tensor) or not amax_x.is_cuda or amax_x.dtype != torch.float32 \
+            or tuple(amax_x.shape) != (K,):
+        raise TypeError(f"amax_x must be a float32 [{K}] tensor on the GPU")
+    amax_x = amax_x.contiguous()
+    Wh = torch.empty_like(W)
+    e = torch.empty(K, dtype=torch.int32, device=W.device)
+    _check(lib.mq_smooth_weights(ptr, N, K, ctypes.c_void_p(amax_x.data_ptr()), ctypes.c_void_p(Wh.data_ptr()),
+                                 ctypes.c_void_p(e.data_ptr()), _stream_handle(stream)), "mq_smooth_weights")
+    return Wh, e
+
+
+def mq_smooth_activations(X, e, out=None, stream=None):
+    """X^ = X 2^-e for the weights from mq_smooth_weights (enqueued, no sync)."""
+    import torch
+    xp = _dev_fp16(X, "X")
+    M, K = X.shape
+    if e.dtype != torch.int32 or tuple(e.shape) != (K,) or not e.is_cuda:
+        raise TypeError(f"e must be an int32 [{K}] tensor on the GPU")
+    out = torch.empty_like(X) if out is None else out
+    _check(lib.mq_smooth_activations(xp, M, K, ctypes.c_void_p(e.data_ptr()), _dev_fp16(out, "out"),
+                                     _stream_handle(stream)), "mq_smooth_activations")
+    return out
 
 
 def mq_linear_with(X, packed: Packed, kernel: int = KERNEL_AUTO, Y=None, stream=None):

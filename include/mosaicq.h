@@ -241,6 +241,44 @@ mq_status mq_block_count(const mq_packed* p, int64_t* nblk);
 mq_status mq_export_blocks(const mq_packed* p, void* blk_i32, void* rscale_f32, void* rcodes_u8,
                            void* hip_stream);
 
+/*
+ * mq_smooth_weights -- move activation outliers into the weights before
+ * packing (MosaicQuant explainer, Methodology section 1: an equivalent
+ * transformation such as SmoothQuant migrates the activation outliers into
+ * W, and the migrated matrix is what gets decomposed).
+ *
+ * SmoothQuant at strength 1/2 with power-of-two factors: for input channel
+ * j, e_j = floor((E_x - E_w) / 2) where E_x = floor(log2 amax_x[j]) and
+ * E_w = floor(log2 max_i |W_ij|) (from the floats' exponents); e_j = 0 when
+ * either maximum is 0; e_j is clamped so that neither scaled maximum exceeds
+ * fp16's range (exponent 15) and to [-24, 24]. Then W^_ij = fp16(W_ij 2^e_j),
+ * exact unless the result is fp16-subnormal (round half to even). Pack W^ and
+ * feed mq_linear activations from mq_smooth_activations: X^ W^^T = X W^T.
+ *
+ *   W_dev_fp16      [N, K] fp16 weights (device, 2-byte aligned)
+ *   amax_x_dev_f32  [K] max |X_mj| per input channel over calibration
+ *                   activations (device, >= 0 and finite)
+ *   W_out_dev_fp16  [N, K] fp16 output W^ (device; may be W itself)
+ *   e_out_dev_i32   [K] the exponents e_j (device)
+ *   hip_stream      stream; the call synchronises it once (to check amax_x)
+ *
+ * Errors: MQ_ERR_INVALID_ARG (NULL or misaligned pointers, N or K <= 0, a
+ * negative or non-finite amax_x value), MQ_ERR_UNSUPPORTED (N * K >= 2^31),
+ * MQ_ERR_OUT_OF_MEMORY, MQ_ERR_DEVICE.
+ */
+mq_status mq_smooth_weights(const void* W_dev_fp16, int64_t N, int64_t K, const float* amax_x_dev_f32,
+                            void* W_out_dev_fp16, int32_t* e_out_dev_i32, void* hip_stream);
+
+/*
+ * mq_smooth_activations -- X^_mj = fp16(X_mj 2^-e_j), the activations that go
+ * with W^ from mq_smooth_weights (same rounding rule). X_out may be X.
+ * Enqueued on hip_stream without synchronising. Errors: MQ_ERR_INVALID_ARG
+ * (NULL or misaligned pointers, M or K <= 0), MQ_ERR_UNSUPPORTED
+ * (M * K >= 2^31), MQ_ERR_DEVICE.
+ */
+mq_status mq_smooth_activations(const void* X_dev_fp16, int64_t M, int64_t K, const int32_t* e_dev_i32,
+                                void* X_out_dev_fp16, void* hip_stream);
+
 /* mq_free -- release a handle and its device memory (NULL is accepted). The
  * caller must make sure no enqueued mq_linear still reads it. */
 void mq_free(mq_packed* p);

@@ -29,8 +29,8 @@ def declared_functions():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["mq_pack", "mq_linear", "mq_linear_with", "mq_residual_add", "mq_packed_info", "mq_export_canonical",
-         "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks", "mq_free",
-         "mq_status_string"])
+         "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks", "mq_smooth_weights",
+         "mq_smooth_activations", "mq_free", "mq_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -82,6 +82,16 @@ def _pack_blocks(lib, W=FAKE, N=32, K=256, G=128, frac=0.1, h=FAKE, out=True):
 ])
 def test_pack_blocks_argument_validation(lib, kw, code):
     assert _pack_blocks(lib, **kw) == code
+
+
+def test_smooth_argument_validation(lib):
+    assert lib.mq_smooth_weights(None, 4, 8, FAKE, FAKE, FAKE, None) == -1
+    assert lib.mq_smooth_weights(FAKE, 0, 8, FAKE, FAKE, FAKE, None) == -1
+    assert lib.mq_smooth_weights(FAKE, 4, 8, ctypes.c_void_p((1 << 20) + 2), FAKE, FAKE, None) == -1
+    assert lib.mq_smooth_weights(FAKE, (1 << 31) // 8, 8, FAKE, FAKE, FAKE, None) == -2
+    assert lib.mq_smooth_activations(FAKE, 4, 8, None, FAKE, None) == -1
+    assert lib.mq_smooth_activations(FAKE, 4, -8, FAKE, FAKE, None) == -1
+    assert lib.mq_smooth_activations(ctypes.c_void_p((1 << 20) + 1), 4, 8, FAKE, FAKE, None) == -1
 
 
 def test_pack_without_a_device_reports_device_error(lib):
