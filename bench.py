@@ -50,8 +50,8 @@ def parse():
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-extra", action="store_true",
-                    help="skip the transformer-block, residual-sweep and block-residual legs")
-    ap.add_argument("--only", choices=["decode", "prefill", "copy", "blocks"], default=None,
+                    help="skip the transformer-block, residual-sweep, block-residual and migration legs")
+    ap.add_argument("--only", choices=["decode", "prefill", "copy", "blocks", "migration"], default=None,
                     help="run one leg only (profiling runs); 'copy' runs the plain device copy that "
                          "calibrates the HBM byte counters")
     ap.add_argument("--no-warm", action="store_true",
@@ -456,6 +456,57 @@ def bench_blocks(args, mq, synth, torch):
     return res
 
 
+def bench_migration(args, mq, synth, torch):
+    """Outlier migration before packing on the 11008x4096 decode layer: the
+    output distortion ||Y - X W^T||^2 on 256 held-out tokens (4 hot channels
+    x50, the same channels as the 256 calibration tokens the migration and
+    the block scores use) of plain W4, the element-wise residual (rho 0.5 %)
+    and the block residual (10 % of the blocks), each without and with
+    migration; and the time of mq_smooth_weights and of one
+    mq_smooth_activations call at M = 16."""
+    layer = synth.WORKLOADS["decode-11008x4096"].layers[0]
+    W = torch.from_numpy(layer.W()).cuda()
+    Xcal = torch.from_numpy(layer.calibration(256, 4)).cuda()
+    Xev = torch.from_numpy(layer.calibration(256, 4, held_out=True)).cuda()
+    Yref = Xev.float() @ W.float().t()
+    amax = Xcal.float().abs().amax(0)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    Wm, e = mq.mq_smooth_weights(W, amax)
+    ev1.record()
+    torch.cuda.synchronize()
+    smooth_ms = ev0.elapsed_time(ev1)
+    Xev_m = mq.mq_smooth_activations(Xev, e)
+    Xcal_m = mq.mq_smooth_activations(Xcal, e)
+
+    def dist(p, X):
+        Y = mq.mq_linear(X, p).float()
+        return float(((Y - Yref) ** 2).sum())
+
+    out = {"workload": "decode-11008x4096", "smooth_weights_ms": round(smooth_ms, 3),
+           "channels_moved": int((e != 0).sum())}
+    for tag, Wx, Xe, Xc in (("without", W, Xev, Xcal), ("with", Wm, Xev_m, Xcal_m)):
+        h = (Xc.float() ** 2).sum(0)
+        d = {}
+        for name, make in (("plain_w4", lambda: mq.mq_pack(Wx, layer.group, 0.0)),
+                           ("elementwise_rho_0.005", lambda: mq.mq_pack(Wx, layer.group, 0.005)),
+                           ("blocks_0.1", lambda: mq.mq_pack_blocks(Wx, layer.group, 0.1, h))):
+            p = make()
+            d[name] = dist(p, Xe)
+            p.free()
+        out[tag + "_migration"] = d
+    base = out["without_migration"]["plain_w4"]
+    out["relative_to_plain_w4_without"] = {
+        tag: {k: round(v / base, 4) for k, v in out[tag + "_migration"].items()} for tag in ("without", "with")}
+    X16 = torch.from_numpy(layer.X(16)).cuda()
+    Xo = torch.empty_like(X16)
+
+    def smooth(i):
+        mq.mq_smooth_activations(X16, e, Xo)
+    out["smooth_activations_us_M16"] = round(replay_spread(torch, smooth, 4, 40, reps=5)[0] * 1e3, 2)
+    return out
+
+
 def cpu_baseline(layer, Ms, min_seconds=10.0, max_steps=60):
     """The oracle, as it stands, on the same decode layer: one step is its
     dequantisation plus the float64 linear for M = 1, 4, 16 (packing by the
@@ -520,6 +571,9 @@ def main():
     if args.only == "blocks":
         print(json.dumps({"block_residual": bench_blocks(args, mq, synth, torch)}), flush=True)
         return
+    if args.only == "migration":
+        print(json.dumps({"migration": bench_migration(args, mq, synth, torch)}), flush=True)
+        return
     d = bench_decode(args, mq, synth, torch)
     value = d["bytes_step"] / (d["ms_per_step"] * 1e-3) / 1e9
     # dominant kernel: the decode launch with the longest average duration
@@ -553,6 +607,7 @@ def main():
             line["block_4096h_m16"] = bench_block(args, mq, synth, torch)
             line["residual_sweep"] = bench_sweep(args, mq, synth, torch)
             line["block_residual"] = bench_blocks(args, mq, synth, torch)
+            line["migration"] = bench_migration(args, mq, synth, torch)
         if not args.skip_cpu:
             line["cpu_baseline"] = cpu_baseline(d["layer"], [1, 4, 16])
     print(json.dumps(line), flush=True)
