@@ -136,3 +136,56 @@ def test_block_handle_errors(mq):
     assert mq.lib.mq_export_blocks(q.handle, None, None, None, None) == -2
     n = ctypes.c_int64()
     assert mq.lib.mq_block_count(q.handle, ctypes.byref(n)) == 0 and n.value == -1
+
+
+@pytest.mark.parametrize("M", [4, 16, 64, 300])
+def test_block_handles_in_graph_replays(mq, M):
+    """The block-residual kernels captured in a graph give the eager result on
+    every replay (other work and synchronisations between the replays)."""
+    import torch
+    N, K = 512, 4096
+    W = _layer(N, K, 21)
+    p = mq.mq_pack_blocks(to_dev(W), 128, 0.1, to_dev(_h(K, 22)))
+    Xd = to_dev(np.random.default_rng(M).standard_normal((M, K)).astype(np.float16))
+    ref = mq.mq_linear(Xd, p).cpu().numpy()
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        mq.mq_linear(Xd, p, Y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mq.mq_linear(Xd, p, Y)
+    for rep in range(3):
+        Y.fill_(0.5)
+        other = mq.mq_linear(Xd, p)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[block graph] M={M} replay={rep}", flush=True)
+        assert np.array_equal(Y.cpu().numpy().view(np.uint16), ref.view(np.uint16))
+        assert np.array_equal(other.cpu().numpy().view(np.uint16), ref.view(np.uint16))
+
+
+@pytest.mark.timeout(600)
+def test_prefill_layer_blocks_sampled(mq):
+    # the 28672 x 8192 layer with 10 % of its blocks, GEMM at M = 512 on sampled outputs
+    from bit_gemm_amd import synth
+    from tests.test_gpu_fullsize import _sampled_check
+    layer = synth.WORKLOADS["prefill-28672x8192"].layers[0]
+    W = layer.W()
+    h = ob.hessian_diag(layer.calibration(128, 4))
+    print("[block pack] prefill-28672x8192 beta=0.1", flush=True)
+    p = mq.mq_pack_blocks(to_dev(W), layer.group, 0.1, to_dev(h))
+    got = mq.export_blocks(p)
+    ref = ob.pack_blocks(W, layer.group, 0.1, h)
+    del W
+    assert np.array_equal(got["blk"], ref["blk"])
+    assert np.array_equal(got["rcodes"], ref["rcodes"])
+    Wt = ob.dequant_blocks(ref)
+    del ref
+    print("[block linear] prefill-28672x8192 M=512", flush=True)
+    _sampled_check(mq, p, layer.X(512), Wt, mq.KERNEL_GEMM, "prefill blocks M=512", seed=512)
+    p.free()
