@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmosaicq.so")
 HOSTCHECK = os.path.join(HERE, "libmq_hostcheck.so")
-SOURCES = ["api.cpp", "pack.hip", "pack_blocks.hip", "gemv.hip", "gemm.hip", "residual.hip", "migrate.hip"]
+SOURCES = ["api.cpp", "pack.hip", "pack_blocks.hip", "gemv.hip", "gemm.hip", "residual.hip", "migrate.hip", "w4a4.hip"]
 # per-source code generation options: the prefill GEMM's stage body is one
 # long basic block; the ILP-oriented machine scheduler interleaves its
 # widening arithmetic with the MFMAs instead of clustering it after them

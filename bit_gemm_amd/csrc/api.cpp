@@ -331,6 +331,39 @@ MQ_API mq_status mq_residual_add(const void* X_dev_fp16, int64_t M, const mq_pac
                                       static_cast<uint16_t*>(Y_dev_fp16), static_cast<hipStream_t>(hip_stream)));
 }
 
+MQ_API mq_status mq_quantize_activations(const void* X_dev_fp16, int64_t M, int64_t K, int32_t group_size,
+                                         void* xq_dev_u8, void* xmeta_dev_u32, void* hip_stream) {
+  if (!X_dev_fp16 || !xq_dev_u8 || !xmeta_dev_u32 || M <= 0 || K <= 0) return MQ_ERR_INVALID_ARG;
+  if (group_size != 32 && group_size != 64 && group_size != 128) return MQ_ERR_INVALID_ARG;
+  if (K % group_size != 0 || K > 65536) return MQ_ERR_INVALID_ARG;
+  const int64_t Kp = ceil_div(K, mq::kTileCols) * mq::kTileCols;
+  if (M >= (int64_t(1) << 31) / Kp) return MQ_ERR_UNSUPPORTED;   // M * Kp < 2^31
+  if ((reinterpret_cast<uintptr_t>(X_dev_fp16) & 15u) || (reinterpret_cast<uintptr_t>(xq_dev_u8) & 15u) ||
+      (reinterpret_cast<uintptr_t>(xmeta_dev_u32) & 3u))
+    return MQ_ERR_INVALID_ARG;
+  return from_hip(mq::quantize_a4(static_cast<const uint16_t*>(X_dev_fp16), M, K, group_size,
+                                  static_cast<uint8_t*>(xq_dev_u8), static_cast<uint32_t*>(xmeta_dev_u32),
+                                  static_cast<hipStream_t>(hip_stream)));
+}
+
+MQ_API mq_status mq_linear_a4(const void* xq_dev_u8, const void* xmeta_dev_u32, int64_t M, const mq_packed* p,
+                              void* Y_dev_fp16, void* hip_stream) {
+  if (!is_live(p)) return MQ_ERR_BAD_HANDLE;
+  if (!xq_dev_u8 || !xmeta_dev_u32 || !Y_dev_fp16 || M <= 0) return MQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(xq_dev_u8) & 15u) || (reinterpret_cast<uintptr_t>(xmeta_dev_u32) & 3u) ||
+      (reinterpret_cast<uintptr_t>(Y_dev_fp16) & 1u))
+    return MQ_ERR_INVALID_ARG;
+  // single residual entries carry their own scale, which the integer MFMA sum cannot take
+  if (!p->blocks && p->nnz > 0) return MQ_ERR_UNSUPPORTED;
+  const int64_t Kp = p->Kt * mq::kTileCols;
+  if (M >= (int64_t(1) << 31) / Kp || M >= (int64_t(1) << 31) / p->N) return MQ_ERR_UNSUPPORTED;
+  // the kernel addresses the handle's arrays with 32-bit byte offsets
+  if (p->Nb * p->Kt * mq::kTileBytes >= (int64_t(1) << 31)) return MQ_ERR_UNSUPPORTED;
+  return from_hip(mq::launch_gemm_a4(p, static_cast<const uint8_t*>(xq_dev_u8),
+                                     static_cast<const uint32_t*>(xmeta_dev_u32), M,
+                                     static_cast<uint16_t*>(Y_dev_fp16), static_cast<hipStream_t>(hip_stream)));
+}
+
 MQ_API mq_status mq_packed_info(const mq_packed* p, int64_t* N, int64_t* K, int32_t* G, int64_t* nnz,
                                 size_t* bytes) {
   if (!is_live(p)) return MQ_ERR_BAD_HANDLE;

@@ -119,6 +119,13 @@ hipError_t launch_residual(const mq_packed* p, const uint16_t* X, int64_t M, uin
 // (gemm.hip); used by the kernels that split K.
 hipError_t launch_splitk_reduce(const float* part, uint16_t* Y, int64_t M, int64_t N, int S, hipStream_t stream);
 
+// 4-bit activations (w4a4.hip): the activation quantizer (codes in tile
+// order, per-(token, group) scale and code sum), and the W4A4 GEMM.
+hipError_t quantize_a4(const uint16_t* X, int64_t M, int64_t K, int G, uint8_t* xq, uint32_t* xmeta,
+                       hipStream_t stream);
+hipError_t launch_gemm_a4(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, int64_t M, uint16_t* Y,
+                          hipStream_t stream);
+
 constexpr int64_t kGemvMaxM = 64;       // the GEMV kernels accept up to 64 tokens
 constexpr int64_t kAutoGemvMaxM = 16;   // the automatic choice takes them up to 16
 

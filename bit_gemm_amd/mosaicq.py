@@ -23,7 +23,8 @@ GEMV_MAX_M = 64
 
 EXPORTED = ("mq_pack", "mq_linear", "mq_linear_with", "mq_residual_add", "mq_packed_info",
             "mq_export_canonical", "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks",
-            "mq_smooth_weights", "mq_smooth_activations", "mq_free", "mq_status_string")
+            "mq_smooth_weights", "mq_smooth_activations", "mq_quantize_activations", "mq_linear_a4",
+            "mq_free", "mq_status_string")
 
 
 class MQError(RuntimeError):
@@ -62,6 +63,10 @@ def _load():
     lib.mq_smooth_weights.restype = ctypes.c_int
     lib.mq_smooth_activations.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.mq_smooth_activations.restype = ctypes.c_int
+    lib.mq_quantize_activations.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    lib.mq_quantize_activations.restype = ctypes.c_int
+    lib.mq_linear_a4.argtypes = [vp, vp, i64, vp, vp, vp]
+    lib.mq_linear_a4.restype = ctypes.c_int
     lib.mq_free.argtypes = [vp]
     lib.mq_free.restype = None
     lib.mq_status_string.argtypes = [ctypes.c_int]
@@ -208,6 +213,50 @@ def mq_smooth_activations(X, e, out=None, stream=None):
     _check(lib.mq_smooth_activations(xp, M, K, ctypes.c_void_p(e.data_ptr()), _dev_fp16(out, "out"),
                                      _stream_handle(stream)), "mq_smooth_activations")
     return out
+
+
+def mq_quantize_activations(X, G: int, xq=None, xmeta=None, stream=None):
+    """4-bit activation codes of X for mq_linear_a4 (enqueued, no sync).
+    Returns (xq uint8 [M, Kp], xmeta int32 [M, Kp / G]), Kp = 128 ceil(K / 128):
+    e4m3 codes in tile order, and fp16 scale bits | code sum << 16."""
+    import torch
+    xp = _dev_fp16(X, "X")
+    if X.dim() != 2:
+        raise ValueError("X must be [M, K]")
+    M, K = X.shape
+    Kp = -(-K // 128) * 128
+    if xq is None:
+        xq = torch.empty((M, Kp), dtype=torch.uint8, device=X.device)
+    if xmeta is None:
+        xmeta = torch.empty((M, Kp // G), dtype=torch.int32, device=X.device)
+    if xq.dtype != torch.uint8 or tuple(xq.shape) != (M, Kp) or not xq.is_contiguous():
+        raise TypeError(f"xq must be a contiguous uint8 [{M}, {Kp}] tensor")
+    if xmeta.dtype != torch.int32 or tuple(xmeta.shape) != (M, Kp // G) or not xmeta.is_contiguous():
+        raise TypeError(f"xmeta must be a contiguous int32 [{M}, {Kp // G}] tensor")
+    _check(lib.mq_quantize_activations(xp, M, K, int(G), ctypes.c_void_p(xq.data_ptr()),
+                                       ctypes.c_void_p(xmeta.data_ptr()), _stream_handle(stream)),
+           "mq_quantize_activations")
+    return xq, xmeta
+
+
+def mq_linear_a4(xq, xmeta, packed: Packed, Y=None, stream=None):
+    """Y = X^ (deq(base) + deq(residual))^T from the 4-bit activation codes of
+    mq_quantize_activations (enqueued, no sync)."""
+    import torch
+    M = xq.shape[0]
+    Kp = -(-packed.K // 128) * 128
+    if xq.dtype != torch.uint8 or tuple(xq.shape) != (M, Kp) or not xq.is_contiguous():
+        raise TypeError(f"xq must be a contiguous uint8 [M, {Kp}] tensor")
+    if xmeta.dtype != torch.int32 or tuple(xmeta.shape) != (M, Kp // packed.G) or not xmeta.is_contiguous():
+        raise TypeError(f"xmeta must be a contiguous int32 [M, {Kp // packed.G}] tensor")
+    if Y is None:
+        Y = torch.empty((M, packed.N), dtype=torch.float16, device=xq.device)
+    yp = _dev_fp16(Y, "Y")
+    if tuple(Y.shape) != (M, packed.N):
+        raise ValueError(f"Y must be [{M}, {packed.N}]")
+    _check(lib.mq_linear_a4(ctypes.c_void_p(xq.data_ptr()), ctypes.c_void_p(xmeta.data_ptr()), M, packed.handle,
+                            yp, _stream_handle(stream)), "mq_linear_a4")
+    return Y
 
 
 def mq_linear_with(X, packed: Packed, kernel: int = KERNEL_AUTO, Y=None, stream=None):

@@ -279,6 +279,62 @@ mq_status mq_smooth_weights(const void* W_dev_fp16, int64_t N, int64_t K, const 
 mq_status mq_smooth_activations(const void* X_dev_fp16, int64_t M, int64_t K, const int32_t* e_dev_i32,
                                 void* X_out_dev_fp16, void* hip_stream);
 
+/*
+ * mq_quantize_activations -- 4-bit activations for mq_linear_a4 (MosaicQuant
+ * explainer, Experimental Results: weights and activations both in 4 bits;
+ * Methodology section 3: quantization is a stage of the fused pipeline).
+ * Each token row is quantized like the base weights, per group of G columns:
+ * sx = fp16(max |x| / 7) (round half to even), qx = clamp(rne(x / sx), -7, 7),
+ * qx = 0 where sx = 0; decided exactly.
+ *
+ *   X_dev_fp16      [M, K] fp16 activations (device, 16-byte aligned)
+ *   M, K            M >= 1; K % G == 0, K <= 65536; M * Kp < 2^31 with
+ *                   Kp = 128 * ceil(K / 128)
+ *   group_size      G in {32, 64, 128}; must be the G of the handle the codes
+ *                   are used with
+ *   xq_dev_u8       [M, Kp] bytes out (device, 16-byte aligned): qx as OCP
+ *                   e4m3 bytes in tile order -- for token m and column tile
+ *                   kt, byte 32 g + 8 t + p of the tile's 128 bytes holds
+ *                   column 128 kt + 32 t + 8 g + perm[p], perm = {0, 4, 1, 5,
+ *                   2, 6, 3, 7}; columns K .. Kp - 1 hold 0
+ *   xmeta_dev_u32   [M, Kp / G] out (device, 4-byte aligned): the fp16 bits of
+ *                   sx in bits 0-15 and the group's code sum (int16) in bits
+ *                   16-31; groups past K hold 0
+ *   hip_stream      stream to enqueue on (no synchronisation)
+ *
+ * A group holding an inf or NaN gets a NaN scale and zero codes, so its
+ * outputs in mq_linear_a4 are NaN. Errors: MQ_ERR_INVALID_ARG (NULL or
+ * misaligned pointers, M or K out of range, G not supported or not dividing
+ * K), MQ_ERR_UNSUPPORTED (M * Kp >= 2^31), MQ_ERR_DEVICE.
+ */
+mq_status mq_quantize_activations(const void* X_dev_fp16, int64_t M, int64_t K, int32_t group_size,
+                                  void* xq_dev_u8, void* xmeta_dev_u32, void* hip_stream);
+
+/*
+ * mq_linear_a4 -- Y = X^ (deq(Q_base) + deq(R))^T with the 4-bit activations
+ * X^ = sx * qx of mq_quantize_activations (W4A4; the residual, when the
+ * handle has one, is applied inside the same kernel as in mq_linear).
+ *
+ *   xq_dev_u8, xmeta_dev_u32  codes and metadata from mq_quantize_activations
+ *                   with this handle's K and G (device, 16- / 4-byte aligned)
+ *   M               number of tokens, M >= 1; M * Kp and M * N < 2^31
+ *   p               a handle from mq_pack_blocks, or from mq_pack with
+ *                   residual_density giving no entries (nnz = 0)
+ *   Y_dev_fp16      [M, N] fp16 output (device, 2-byte aligned, overwritten)
+ *   hip_stream      stream to enqueue on (no synchronisation)
+ *
+ * The products run on the fp8 matrix cores exactly (4-bit integers) and each
+ * group's sum is scaled and added in fp32. Like mq_linear's GEMM it splits K
+ * when the output tiles are few, with a stream-ordered fp32 workspace of at
+ * most 64 MiB (MQ_ERR_OUT_OF_MEMORY if it cannot be had). Deterministic.
+ * Errors: MQ_ERR_BAD_HANDLE, MQ_ERR_INVALID_ARG, MQ_ERR_UNSUPPORTED (a
+ * handle with single residual entries: their per-entry scale cannot join the
+ * integer sum; pack with mq_pack_blocks instead; or base codes of 2 GiB or
+ * more), MQ_ERR_DEVICE.
+ */
+mq_status mq_linear_a4(const void* xq_dev_u8, const void* xmeta_dev_u32, int64_t M, const mq_packed* p,
+                       void* Y_dev_fp16, void* hip_stream);
+
 /* mq_free -- release a handle and its device memory (NULL is accepted). The
  * caller must make sure no enqueued mq_linear still reads it. */
 void mq_free(mq_packed* p);

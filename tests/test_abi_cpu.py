@@ -23,14 +23,14 @@ def lib():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(mq_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(mq_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["mq_pack", "mq_linear", "mq_linear_with", "mq_residual_add", "mq_packed_info", "mq_export_canonical",
          "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks", "mq_smooth_weights",
-         "mq_smooth_activations", "mq_free", "mq_status_string"])
+         "mq_smooth_activations", "mq_quantize_activations", "mq_linear_a4", "mq_free", "mq_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -116,3 +116,23 @@ def test_bad_handles_are_rejected(lib):
     assert lib.mq_export_blocks(bogus, None, None, None, None) == -6
     lib.mq_free(None)        # accepted
     lib.mq_free(bogus)       # unknown handle: ignored, no crash
+
+
+def test_quantize_activations_validation(lib):
+    f = lib.mq_quantize_activations
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    assert f(None, 4, 256, 128, FAKE, FAKE, None) == -1
+    assert f(FAKE, 0, 256, 128, FAKE, FAKE, None) == -1
+    assert f(FAKE, 4, 256, 96, FAKE, FAKE, None) == -1          # G not supported
+    assert f(FAKE, 4, 192, 128, FAKE, FAKE, None) == -1         # K % G != 0
+    assert f(FAKE, 4, 131072, 128, FAKE, FAKE, None) == -1      # K > 65536
+    assert f(mis, 4, 256, 128, FAKE, FAKE, None) == -1          # X not 16-byte aligned
+    assert f(FAKE, 4, 256, 128, mis, FAKE, None) == -1          # codes not 16-byte aligned
+    assert f(FAKE, 4, 256, 128, FAKE, ctypes.c_void_p((1 << 20) + 2), None) == -1
+    assert f(FAKE, 1 << 20, 4096, 128, FAKE, FAKE, None) == -2  # M * Kp >= 2^31
+
+
+def test_linear_a4_validation(lib):
+    f = lib.mq_linear_a4
+    assert f(FAKE, FAKE, 4, None, FAKE, None) == -6              # no handle
+    assert f(FAKE, FAKE, 4, FAKE, FAKE, None) == -6              # not a live handle

@@ -1,0 +1,185 @@
+"""4-bit activations (mq_quantize_activations, mq_linear_a4) against the CPU
+oracle (oracle/w4a4.py).
+
+* The quantizer bit-exact: every code (decoded from its e4m3 byte, found at
+  the tile-order position the header defines), every scale and code sum, and
+  zeros in the padding past K.
+* The W4A4 linear within |Y - Y64| <= 2e-3 * sum|x^||w~| + 1e-5 of the
+  float64 oracle X^ W~^T on the oracle's own 4-bit activations and the
+  dequantized weights of the oracle's packing (the 4-bit products are exact
+  on the matrix cores; what remains is fp32 scaling and accumulation and the
+  fp16 output rounding), for plain handles and block-residual handles, over
+  the three workgroup shapes, split K and ragged N, M and K.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import blocks as ob
+from oracle import w4a4 as oa
+from tests.gpu_util import check_linear, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+PERM = [0, 4, 1, 5, 2, 6, 3, 7]          # byte p of an 8-byte chunk holds column PERM[p]
+INV = [PERM.index(c) for c in range(8)]
+E4M3_MAG = [0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E]   # OCP e4m3 of 0..7
+
+
+@pytest.fixture(scope="module")
+def mq():
+    return require_gpu()
+
+
+def _byte_pos(K):
+    j = np.arange(K)
+    c = j % 128
+    return 128 * (j // 128) + 32 * ((c % 32) // 8) + 8 * (c // 32) + np.array(INV)[c % 8]
+
+
+def _decode(xq, K):
+    lut = np.full(256, 99, dtype=np.int64)
+    for q in range(-7, 8):
+        lut[(0x80 if q < 0 else 0) | E4M3_MAG[abs(q)]] = q
+    return lut[xq[:, _byte_pos(K)]]
+
+
+def _acts(M, K, seed, hot=4):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((M, K)).astype(np.float32) * np.exp2(rng.integers(-4, 4, (M, 1)))
+    X[:, rng.choice(K, hot, replace=False)] *= 50
+    return X.astype(np.float16)
+
+
+def _check_quant(mq, X, G):
+    M, K = X.shape
+    xq, xm = mq.mq_quantize_activations(to_dev(X), G)
+    xq, xm = xq.cpu().numpy(), xm.cpu().numpy().view(np.uint32)
+    qx, sx = oa.quantize_activations(X, G)
+    Kp = xq.shape[1]
+    assert np.array_equal(_decode(xq, K), qx.astype(np.int64)), "codes differ"
+    pad = np.setdiff1d(np.arange(Kp), _byte_pos(K))
+    assert not xq[:, pad].any(), "padding bytes are not zero"
+    ng = K // G
+    assert np.array_equal((xm[:, :ng] & 0xFFFF).astype(np.uint16), sx.view(np.uint16)), "scales differ"
+    sums = (xm[:, :ng] >> 16).astype(np.uint16).view(np.int16).astype(np.int32)
+    assert np.array_equal(sums, oa.code_sums(qx, G)), "code sums differ"
+    assert not xm[:, ng:].any(), "padding groups are not zero"
+    return qx, sx
+
+
+QSHAPES = [(1, 128, 128), (5, 256, 64), (37, 384, 32), (16, 4160, 64), (3, 8256, 32), (64, 4096, 128),
+           (130, 1024, 128), (2, 65536, 128)]
+
+
+@pytest.mark.parametrize("M,K,G", QSHAPES)
+def test_quantizer_bit_exact(mq, M, K, G):
+    print(f"[a4 quant] M={M} K={K} G={G}", flush=True)
+    X = _acts(M, K, M + K + G)
+    X[0, :G] = 0                                         # a zero group
+    if M > 2:
+        X[2, 5] = np.float16(2.0 ** -24)                 # subnormal inputs and a tiny group
+        X[2, G:2 * G] = np.float16(2.0 ** -20) * np.arange(G, dtype=np.float16)
+    _check_quant(mq, X, G)
+
+
+def test_quantizer_non_finite_group(mq):
+    X = _acts(4, 256, 1)
+    X[1, 130] = np.inf
+    X[2, 7] = np.nan
+    xq, xm = mq.mq_quantize_activations(to_dev(X), 128)
+    xq, xm = xq.cpu().numpy(), xm.cpu().numpy().view(np.uint32)
+    assert xm[1, 1] & 0xFFFF == 0x7E00 and xm[2, 0] & 0xFFFF == 0x7E00
+    assert not xq[1, 128:256].any() and not xq[2, :128].any()
+    qx, sx = oa.quantize_activations(X[[0, 3]], 128)      # the finite rows are unaffected
+    assert np.array_equal(_decode(xq[[0, 3]], 256), qx.astype(np.int64))
+
+
+def _layer(N, K, seed):
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, rng.choice(K, 3, replace=False)] *= 20
+    return W.astype(np.float16)
+
+
+def _linear_cases(mq, p, Wt, K, G, Ms, what):
+    for M in Ms:
+        X = _acts(M, K, 1000 + M)
+        print(f"[a4 linear] {what} M={M}", flush=True)
+        xq, xm = mq.mq_quantize_activations(to_dev(X), G)
+        Y = mq.mq_linear_a4(xq, xm, p).cpu().numpy()
+        qx, sx = oa.quantize_activations(X, G)
+        check_linear(Y, oa.dequant_activations(qx, sx, G), Wt, f"{what} M={M}")
+
+
+# (N, K, G): ragged N and K, several 256-feature tiles, split K at small M
+LSHAPES = [(16, 128, 128), (200, 384, 64), (300, 4160, 64), (96, 256, 32), (520, 4096, 128), (64, 8192, 128)]
+MS = (1, 5, 16, 17, 40, 64, 65, 130, 300)
+
+
+@pytest.mark.parametrize("N,K,G", LSHAPES)
+def test_linear_a4_plain(mq, N, K, G):
+    W = _layer(N, K, N + K)
+    p = mq.mq_pack(to_dev(W), G, 0.0)
+    Wt = oracle.dequant(oracle.pack(W, G, 0.0))
+    _linear_cases(mq, p, Wt, K, G, MS, f"plain N={N} K={K} G={G}")
+
+
+@pytest.mark.parametrize("N,K,G,beta", [(200, 384, 64, 0.3), (300, 4160, 64, 0.1), (96, 256, 32, 1.0),
+                                        (520, 4096, 128, 0.05), (48, 1024, 128, 0.5)])
+def test_linear_a4_blocks(mq, N, K, G, beta):
+    W = _layer(N, K, 3 * N + K)
+    rng = np.random.default_rng(N)
+    Xc = rng.standard_normal((32, K)).astype(np.float16)
+    Xc[:, rng.choice(K, 4, replace=False)] *= 50
+    h = ob.hessian_diag(Xc)
+    p = mq.mq_pack_blocks(to_dev(W), G, beta, to_dev(h))
+    ref = ob.pack_blocks(W, G, beta, h)
+    assert p.nblk == ref["blk"].size
+    Wt = ob.dequant_blocks(ref)
+    _linear_cases(mq, p, Wt, K, G, MS, f"blocks N={N} K={K} G={G} beta={beta}")
+
+
+def test_linear_a4_rejects_element_residual(mq):
+    W = _layer(32, 256, 5)
+    p = mq.mq_pack(to_dev(W), 128, 0.01)
+    xq, xm = mq.mq_quantize_activations(to_dev(_acts(2, 256, 2)), 128)
+    with pytest.raises(mq.MQError) as ei:
+        mq.mq_linear_a4(xq, xm, p)
+    assert "UNSUPPORTED" in str(ei.value)
+
+
+def test_linear_a4_graph_replay(mq):
+    # quantizer + linear captured in a HIP graph (the split-K workspace becomes
+    # a graph allocation), replayed with fresh activations between replays
+    import torch
+    N, K, G = 300, 4096, 128
+    W = _layer(N, K, 11)
+    rng = np.random.default_rng(3)
+    Xc = rng.standard_normal((32, K)).astype(np.float16)
+    p = mq.mq_pack_blocks(to_dev(W), G, 0.1, to_dev(ob.hessian_diag(Xc)))
+    ref = ob.pack_blocks(W, G, 0.1, ob.hessian_diag(Xc))
+    Wt = ob.dequant_blocks(ref)
+    for M in (4, 64, 300):
+        Xd = to_dev(_acts(M, K, M))
+        xq, xm = mq.mq_quantize_activations(Xd, G)
+        Yd = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            mq.mq_quantize_activations(Xd, G, xq, xm, stream=s)
+            mq.mq_linear_a4(xq, xm, p, Yd, stream=s)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            mq.mq_quantize_activations(Xd, G, xq, xm, stream=torch.cuda.current_stream())
+            mq.mq_linear_a4(xq, xm, p, Yd, stream=torch.cuda.current_stream())
+        for rep in range(3):
+            X = _acts(M, K, 50 * M + rep)
+            Xd.copy_(torch.from_numpy(X))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            qx, sx = oa.quantize_activations(X, G)
+            check_linear(Yd.cpu().numpy(), oa.dequant_activations(qx, sx, G), Wt, f"graph M={M} replay {rep}")
