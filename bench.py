@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP16_PEAK_TFLOPS = 2516.6      # MI355X dense fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (5.0 PFLOP/s)
 MALL_BYTES = 256 << 20
 METRIC = "fused W4+sparse-residual linear: GB/s (decode) & TFLOP/s (prefill), % roofline"
 
@@ -50,8 +51,8 @@ def parse():
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-extra", action="store_true",
-                    help="skip the transformer-block, residual-sweep, block-residual and migration legs")
-    ap.add_argument("--only", choices=["decode", "prefill", "copy", "blocks", "migration"], default=None,
+                    help="skip the transformer-block, residual-sweep, block-residual, migration and W4A4 legs")
+    ap.add_argument("--only", choices=["decode", "prefill", "copy", "blocks", "migration", "w4a4"], default=None,
                     help="run one leg only (profiling runs); 'copy' runs the plain device copy that "
                          "calibrates the HBM byte counters")
     ap.add_argument("--no-warm", action="store_true",
@@ -507,6 +508,100 @@ def bench_migration(args, mq, synth, torch):
     return out
 
 
+def bench_w4a4(args, mq, synth, torch):
+    """4-bit activations. Prefill on the 28672x8192 layer at M = 512, 2048 and
+    4096: mq_quantize_activations + mq_linear_a4 (the quantization stage is
+    part of the step) and the W4A4 GEMM alone, against the fp16-activation
+    GEMM (mq_linear) on the same handle; plain W4 and 10 % residual blocks.
+    TFLOP/s count 2 M N K. Decode time at M = 1 and 16 on the 11008x4096
+    layer (rotated copies, graph replay). Output distortion ||Y - X W^T||^2 on
+    the held-out activations of that layer (4 hot channels x50): W4A16 and
+    W4A4, plain and with blocks, without and with outlier migration."""
+    res = {}
+    pl = synth.WORKLOADS["prefill-28672x8192"].layers[0]
+    Wp = torch.from_numpy(pl.W()).cuda()
+    hp = (torch.from_numpy(pl.calibration(256, 4)).cuda().float() ** 2).sum(0)
+    pre = {}
+    for name, make in (("plain_w4", lambda: mq.mq_pack(Wp, pl.group, 0.0)),
+                       ("blocks_0.1", lambda: mq.mq_pack_blocks(Wp, pl.group, 0.1, hp))):
+        p = make()
+        pre[name] = {}
+        for M in (512, 2048, 4096):
+            X = torch.from_numpy(pl.X(M)).cuda()
+            Y = torch.empty((M, pl.N), dtype=torch.float16, device="cuda")
+            xq, xm = mq.mq_quantize_activations(X, pl.group)
+
+            def step(i, X=X, Y=Y, p=p, xq=xq, xm=xm):
+                mq.mq_quantize_activations(X, pl.group, xq, xm)
+                mq.mq_linear_a4(xq, xm, p, Y)
+
+            def gemm(i, Y=Y, p=p, xq=xq, xm=xm):
+                mq.mq_linear_a4(xq, xm, p, Y)
+
+            def a16(i, X=X, Y=Y, p=p):
+                mq.mq_linear(X, p, Y)
+            e = {}
+            for tag, fn in (("w4a4_step", step), ("w4a4_gemm", gemm), ("w4a16_gemm", a16)):
+                time_events(fn, 3)
+                us = time_events(fn, 10) / 10 * 1e3
+                e[tag] = {"us": round(us, 1), "TFLOPs": round(2.0 * M * pl.N * pl.K / us / 1e6, 1)}
+            e["w4a4_gemm"]["frac_fp8_peak"] = round(e["w4a4_gemm"]["TFLOPs"] / FP8_PEAK_TFLOPS, 4)
+            e["speedup_step_vs_w4a16"] = round(e["w4a16_gemm"]["us"] / e["w4a4_step"]["us"], 3)
+            pre[name][str(M)] = e
+        p.free()
+    del Wp
+    res["prefill_28672x8192"] = pre
+
+    layer = synth.WORKLOADS["decode-11008x4096"].layers[0]
+    N, K, G = layer.N, layer.K, layer.group
+    W = torch.from_numpy(layer.W()).cuda()
+    dec = {}
+    for M in (1, 16):
+        X = torch.from_numpy(layer.X(M)).cuda()
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        p0 = mq.mq_pack(W, G, 0.0)
+        ncopy = max(2, math.ceil(2 * MALL_BYTES / p0.device_bytes))
+        copies = [p0] + [mq.mq_pack(W, G, 0.0) for _ in range(ncopy - 1)]
+        xq, xm = mq.mq_quantize_activations(X, G)
+
+        def a4(i, X=X, Y=Y, xq=xq, xm=xm):
+            mq.mq_quantize_activations(X, G, xq, xm)
+            mq.mq_linear_a4(xq, xm, copies[i % ncopy], Y)
+
+        def a16(i, X=X, Y=Y):
+            mq.mq_linear(X, copies[i % ncopy], Y)
+        dec[str(M)] = {"w4a4_step_us": round(replay_spread(torch, a4, 4, 40, reps=5)[0] * 1e3, 2),
+                       "w4a16_us": round(replay_spread(torch, a16, 4, 40, reps=5)[0] * 1e3, 2)}
+        for c in copies:
+            c.free()
+    res["decode_11008x4096_plain"] = dec
+
+    Xcal = torch.from_numpy(layer.calibration(256, 4)).cuda()
+    Xev = torch.from_numpy(layer.calibration(256, 4, held_out=True)).cuda()
+    Yref = Xev.float() @ W.float().t()
+    amax = Xcal.float().abs().amax(0)
+    Wm, e = mq.mq_smooth_weights(W, amax)
+    dist = {}
+    for tag, Wx, Xe, Xc in (("without_migration", W, Xev, Xcal),
+                            ("with_migration", Wm, mq.mq_smooth_activations(Xev, e),
+                             mq.mq_smooth_activations(Xcal, e))):
+        h = (Xc.float() ** 2).sum(0)
+        d = {}
+        for name, make in (("plain_w4", lambda: mq.mq_pack(Wx, G, 0.0)),
+                           ("blocks_0.1", lambda: mq.mq_pack_blocks(Wx, G, 0.1, h))):
+            p = make()
+            d[name + "_a16"] = float(((mq.mq_linear(Xe, p).float() - Yref) ** 2).sum())
+            xq, xm = mq.mq_quantize_activations(Xe, G)
+            d[name + "_a4"] = float(((mq.mq_linear_a4(xq, xm, p).float() - Yref) ** 2).sum())
+            p.free()
+        dist[tag] = d
+    base = dist["without_migration"]["plain_w4_a16"]
+    res["distortion_11008x4096"] = {
+        "workload": "decode-11008x4096", "held_out_tokens": 256,
+        "relative_to_w4a16_plain": {t: {k: round(v / base, 4) for k, v in d.items()} for t, d in dist.items()}}
+    return res
+
+
 def cpu_baseline(layer, Ms, min_seconds=10.0, max_steps=60):
     """The oracle, as it stands, on the same decode layer: one step is its
     dequantisation plus the float64 linear for M = 1, 4, 16 (packing by the
@@ -574,6 +669,9 @@ def main():
     if args.only == "migration":
         print(json.dumps({"migration": bench_migration(args, mq, synth, torch)}), flush=True)
         return
+    if args.only == "w4a4":
+        print(json.dumps({"w4a4": bench_w4a4(args, mq, synth, torch)}), flush=True)
+        return
     d = bench_decode(args, mq, synth, torch)
     value = d["bytes_step"] / (d["ms_per_step"] * 1e-3) / 1e9
     # dominant kernel: the decode launch with the longest average duration
@@ -608,6 +706,7 @@ def main():
             line["residual_sweep"] = bench_sweep(args, mq, synth, torch)
             line["block_residual"] = bench_blocks(args, mq, synth, torch)
             line["migration"] = bench_migration(args, mq, synth, torch)
+            line["w4a4"] = bench_w4a4(args, mq, synth, torch)
         if not args.skip_cpu:
             line["cpu_baseline"] = cpu_baseline(d["layer"], [1, 4, 16])
     print(json.dumps(line), flush=True)

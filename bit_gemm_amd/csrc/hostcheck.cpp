@@ -13,3 +13,5 @@ HC_API uint32_t mqh_fp32_div7(uint64_t Mx, uint64_t* m, int* Q) { return mq::fp3
 HC_API int mqh_quant7(int64_t a, uint64_t S) { return mq::quant7(a, S); }
 HC_API int mqh_quant7_scaled(int64_t e, uint64_t m, int Q) { return mq::quant7_scaled(e, m, Q); }
 HC_API uint64_t mqh_err_key(uint64_t abs_e) { return mq::err_key(abs_e); }
+HC_API uint32_t mqh_fp16_div7_h(uint32_t h) { return mq::fp16_div7_h(h); }
+HC_API int mqh_quant7_f(float x, float s) { return mq::quant7_f(x, s); }

@@ -129,6 +129,53 @@ MQ_HD int quant7_scaled(int64_t e, uint64_t m, int Q) {
   return quant7(e * (int64_t)(1ull << (-Q)), m);
 }
 
+// fp16 bits of fp16_rne(a / 7) for a finite fp16 magnitude a given by its
+// bit pattern h (sign clear), in 32-bit integers (the activation quantizer's
+// form of fp16_div7). a = m 2^E with m the significand; m 2^16 / 7 = t +
+// rem / 7 holds 14..27 bits, rounded to 11 significant bits, or to the 2^-24
+// quantum below the normal range, with rem as the sticky part.
+MQ_HD uint32_t fp16_div7_h(uint32_t h) {
+  if (h == 0u) return 0u;
+  const uint32_t e5 = h >> 10, m10 = h & 1023u;
+  const uint32_t m = e5 ? (1024u | m10) : m10;
+  const int E = (int)(e5 ? e5 : 1u) - 25;
+  const uint32_t n = m << 16;
+  const uint32_t t = n / 7u, rem = n - 7u * t;
+  const int L = 32 - __builtin_clz(t);
+  int sh = L - 11;
+  if (-8 - E > sh) sh = -8 - E;          // keeps the result's quantum >= 2^-24 (sh <= 16)
+  uint32_t r = t >> sh;
+  const uint32_t low = t & ((1u << sh) - 1u), half = 1u << (sh - 1);
+  if (low > half || (low == half && (rem != 0u || (r & 1u)))) ++r;
+  int F = sh + E - 16;                    // result = r 2^F
+  if (r == 2048u) {
+    r = 1024u;
+    ++F;
+  }
+  return r >= 1024u ? (((uint32_t)(F + 25) << 10) | (r - 1024u)) : r;   // normal, or subnormal at F = -24
+}
+
+// clamp(rne(x / s), -7, 7) for fp16 values held as floats, s >= 0 (0 when
+// s == 0). The estimate |x| (1 / s) is within one of the answer; the
+// decision itself compares 2 |x| with (2 n +- 1) s, products of at most 15
+// significant bits and so exact in fp32 (ties go to the even code).
+MQ_HD int quant7_f(float x, float s) {
+  if (!(s > 0.0f)) return 0;
+  const float ax = x < 0.0f ? -x : x;
+  const float a2 = 2.0f * ax;
+  int n = (int)(ax * (1.0f / s) + 0.5f);
+  if (n > 7) n = 7;
+  if (n > 0) {
+    const float b = (float)(2 * n - 1) * s;
+    if (a2 < b || (a2 == b && (n & 1))) --n;
+  }
+  if (n < 7) {
+    const float b = (float)(2 * n + 1) * s;
+    if (a2 > b || (a2 == b && (n & 1))) ++n;
+  }
+  return x < 0.0f ? -n : n;
+}
+
 // Order-preserving 64-bit key of |e| (|e| in units, < 2^41): the bits of the
 // exact double. The low 12 bits are always zero.
 MQ_HD uint64_t err_key(uint64_t abs_e) {

@@ -7,7 +7,8 @@
 //
 // Activations are quantized like the base weights, per token and per group of
 // G input columns: sx = fp16(max |x| / 7), qx = clamp(rne(x / sx), -7, 7),
-// decided exactly in integers (quant_exact.h).
+// decided exactly with 32-bit arithmetic (fp16_div7_h, quant7_f in
+// quant_exact.h).
 //
 // Matrix cores. gfx950's 16x16x128 fp8 MFMA multiplies 32 bytes per lane of
 // each operand and accumulates in fp32; on 4-bit integers its products and
@@ -89,13 +90,13 @@ __global__ __launch_bounds__(256) void k_quant_a4(const uint16_t* __restrict__ X
   if (NG == 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
   // a group with a non-finite entry gets a NaN scale (its outputs become NaN) and zero codes
   const bool finite = amax < 0x7C00u;
-  uint64_t S = 0;
-  const uint32_t sbits = finite ? fp16_div7((uint64_t)fp16_units(amax), &S) : 0x7E00u;
+  const uint32_t sbits = finite ? fp16_div7_h(amax) : 0x7E00u;
+  const float sf = finite ? h_to_f(sbits) : 0.0f;
   int q[8];
   int sum = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    q[i] = finite ? quant7(fp16_units(h[i]), S) : 0;
+    q[i] = quant7_f(h_to_f(h[i]), sf);
     sum += q[i];
   }
   const uint32_t lo = e4m3_code(q[0]) | (e4m3_code(q[4]) << 8) | (e4m3_code(q[1]) << 16) | (e4m3_code(q[5]) << 24);
@@ -124,11 +125,14 @@ struct CfgA4 {
   static constexpr int kBm = 16 * MS_ * NWM_;
   static constexpr int kChunks = kBm * 8;                          // 16-byte chunks of a staged activation tile
   static constexpr int kXr = (kChunks + kThreads - 1) / kThreads;   // chunks per thread
+  static constexpr int kMinBlocks = 2;                              // workgroups per CU
   static_assert(16 % NWN_ == 0 && MS_ >= 1, "workgroup shape");
 };
-using CfgA4Wide = CfgA4<4, 2, 4>;     // 256 x 128, waves of 64 x 64
-using CfgA4Mid = CfgA4<8, 1, 4>;      // 256 x 64, waves of 32 x 64
-using CfgA4Narrow = CfgA4<8, 1, 1>;   // 256 x 16, waves of 32 x 16
+// 256 x 64 with waves of 32 x 64 (up to 128 VGPRs, so two workgroups share a
+// CU: a larger tile of 8 waves leaves one wave's MFMA-to-VALU dependencies
+// exposed, and the second workgroup's waves fill them); 256 x 16 for decode.
+using CfgA4Mid = CfgA4<8, 1, 4>;
+using CfgA4Narrow = CfgA4<8, 1, 1>;
 
 template <int NG, int BM>
 struct StageA4 {
@@ -319,9 +323,6 @@ __device__ __forceinline__ void tile_math(float4_t (&acc)[C::kMs][C::kRb], const
         acc[i][j] += d * (sv * sw[j][gi]);
       }
     }
-#ifdef MQ_A4_SB
-    __builtin_amdgcn_sched_barrier(0);
-#endif
   }
   if constexpr (DR) {
     pin_acc<MS, RB>(acc);
@@ -390,16 +391,30 @@ __device__ __forceinline__ void store_act(const ActRegs<C, NG>& A, uint8_t* st, 
   }
 }
 
-// Tile index of workgroup b: consecutive workgroups go to the 8 XCDs in
-// turn, so each XCD gets a contiguous range of tiles (shared token slices in
-// its L2).
-__device__ __forceinline__ int xcd_tile_a4(int b, int T) {
+// Output tile of workgroup b. The hardware deals workgroups to the 8 XCDs in
+// turn; index i = xcd_index(b) makes each XCD's share a contiguous range.
+// That range is walked in groups of GM token slices, feature slices outer
+// and token slices inner, so the ~32 workgroups an XCD runs at once cover
+// about 4 feature x 8 token slices: their weight and activation tiles are
+// shared through its L2 instead of each bringing a weight slice of its own.
+constexpr int kGroupM = 8;
+
+__device__ __forceinline__ int xcd_index(int b, int T) {
   const int per = T >> 3, rem = T & 7, x = b & 7, local = b >> 3;
   return x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
 }
+__device__ __forceinline__ void tile_of(int b, int MT, int NT, int& mt, int& nt) {
+  const int i = xcd_index(b, MT * NT);
+  const int per_group = kGroupM * NT;
+  const int grp = i / per_group, first = grp * kGroupM;
+  const int gm = min(MT - first, kGroupM);
+  const int r = i - grp * per_group;
+  nt = r / gm;
+  mt = first + (r - nt * gm);
+}
 
 template <class C, int NG, bool DR>
-__global__ __launch_bounds__(C::kThreads, 1) void k_gemm_a4(WArrays warr, const uint8_t* __restrict__ xq,
+__global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void k_gemm_a4(WArrays warr, const uint8_t* __restrict__ xq,
                                                          const uint32_t* __restrict__ xmeta,
                                                          uint16_t* __restrict__ Y, float* __restrict__ part, int M,
                                                          int N, int Kt, int Nb, int NT, int T, int kt_per_split,
@@ -410,9 +425,9 @@ __global__ __launch_bounds__(C::kThreads, 1) void k_gemm_a4(WArrays warr, const 
   uint8_t* const st0 = lds_a4;
   uint8_t* const st1 = lds_a4 + S::kBytes;
 
-  const int tile = xcd_tile_a4(blockIdx.x, T);
+  int mt, nt;
+  tile_of(blockIdx.x, T / NT, NT, mt, nt);
   const int kt0 = blockIdx.y * kt_per_split, kt1 = min(Kt, kt0 + kt_per_split);
-  const int mt = tile / NT, nt = tile - mt * NT;
   const int rb0 = nt * (kBn / kRowsPerBlock), m0 = mt * BM;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, tid = threadIdx.x;
   const int wn = wave % C::kNwn, wm = wave / C::kNwn;
@@ -574,8 +589,7 @@ hipError_t quantize_a4(const uint16_t* X, int64_t M, int64_t K, int G, uint8_t* 
 hipError_t launch_gemm_a4(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, int64_t M, uint16_t* Y,
                           hipStream_t s) {
   if (M <= 16) return launch_a4_d<CfgA4Narrow>(p, xq, xmeta, M, Y, s);
-  if (M <= 64) return launch_a4_d<CfgA4Mid>(p, xq, xmeta, M, Y, s);
-  return launch_a4_d<CfgA4Wide>(p, xq, xmeta, M, Y, s);
+  return launch_a4_d<CfgA4Mid>(p, xq, xmeta, M, Y, s);
 }
 
 }  // namespace mq

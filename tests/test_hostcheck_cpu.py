@@ -36,6 +36,10 @@ def hc():
     h.mqh_quant7_scaled.restype = ctypes.c_int
     h.mqh_err_key.argtypes = [u64]
     h.mqh_err_key.restype = u64
+    h.mqh_fp16_div7_h.argtypes = [ctypes.c_uint32]
+    h.mqh_fp16_div7_h.restype = ctypes.c_uint32
+    h.mqh_quant7_f.argtypes = [ctypes.c_float, ctypes.c_float]
+    h.mqh_quant7_f.restype = ctypes.c_int
     return h
 
 
@@ -120,3 +124,51 @@ def test_err_key_preserves_order(hc):
     keys = [hc.mqh_err_key(int(x)) for x in v.tolist()]
     assert keys == sorted(keys)
     assert all((k & 0xFFF) == 0 for k in keys)
+
+
+def test_fp16_div7_h_matches_the_oracle_scale_for_every_fp16(hc):
+    # the activation quantizer's 32-bit scale rule, for every finite fp16
+    # magnitude, against the oracle's fp16(a / 7) and exact rational rounding
+    mags = all_finite_fp16()
+    mags = np.unique(np.abs(mags))
+    want = oracle.to_fp16_rne(mags.astype(np.float64) / 7).view(np.uint16)
+    bits = mags.astype(np.float16).view(np.uint16)
+    got = np.array([hc.mqh_fp16_div7_h(int(b)) for b in bits.tolist()], dtype=np.uint16)
+    assert np.array_equal(got, want)
+    for v in mags[::97].tolist():
+        assert Fraction(float(np.uint16(hc.mqh_fp16_div7_h(_bits16(v))).view(np.float16))) == \
+            fp16_exact(Fraction(v) / 7)
+
+
+def test_quant7_f_matches_the_oracle_codes(hc):
+    # random fp16 pairs over the whole range, every scale's ties (x = (n + 1/2) s)
+    # and values just beside them, against clamp(rint(x / s)) in float64
+    rng = np.random.default_rng(5)
+    s = np.abs(rng.standard_normal(4000) * np.exp2(rng.integers(-26, 14, 4000))).astype(np.float16)
+    s = s[(s > 0) & np.isfinite(s)]
+    xs, ss = [], []
+    ties = 0
+    for sv in s[:600].tolist():
+        for n in range(8):
+            t = np.float64(sv) * (n + 0.5)
+            h = np.float16(t)
+            if not np.isfinite(h):
+                continue
+            cands = [np.nextafter(h, np.float16(np.inf)), np.nextafter(h, np.float16(0))]
+            if np.float64(h) == t:                      # the midpoint itself is an fp16 value: a tie
+                cands.append(h)
+                ties += 1
+            for x in cands:
+                if np.isfinite(x):
+                    xs.append(x); ss.append(sv)
+    assert ties > 300
+    x = np.concatenate([np.array(xs, dtype=np.float16),
+                        (rng.standard_normal(20000) * 7 * np.repeat(s[:200], 100)[:20000]).astype(np.float16)])
+    sv = np.concatenate([np.array(ss, dtype=np.float16), np.repeat(s[:200], 100)[:20000]])
+    ok = np.isfinite(x)
+    x, sv = x[ok], sv[ok]
+    x = np.where(np.random.default_rng(1).random(x.size) < 0.5, -x, x).astype(np.float16)
+    want = np.clip(np.rint(x.astype(np.float64) / sv.astype(np.float64)), -7, 7).astype(int)
+    got = np.array([hc.mqh_quant7_f(float(a), float(b)) for a, b in zip(x.tolist(), sv.tolist())])
+    assert np.array_equal(got, want)
+    assert hc.mqh_quant7_f(3.0, 0.0) == 0
