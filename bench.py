@@ -639,6 +639,11 @@ def cpu_baseline(layer, Ms, min_seconds=10.0, max_steps=60):
             "seconds": round(t_lin, 3), "steps": steps, "pack_seconds": round(t_pack, 2)}
 
 
+def progress(leg):
+    """One line on stderr per finished leg (the JSON line stays alone on stdout)."""
+    print(f"[bench] {leg} done at {time.strftime('%H:%M:%S')}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -698,17 +703,20 @@ def main():
         "pack": {"workload": "decode-11008x4096", "gpu_ms": round(d["pack_ms"], 3),
                  "wall_ms_first_call": round(d["pack_wall_ms"], 3)},
     }
+    legs = []
     if args.only != "decode":
         if not args.skip_prefill:
-            line["prefill"] = bench_prefill(args, mq, synth, torch)
+            legs.append(("prefill", bench_prefill))
         if not args.skip_extra:
-            line["block_4096h_m16"] = bench_block(args, mq, synth, torch)
-            line["residual_sweep"] = bench_sweep(args, mq, synth, torch)
-            line["block_residual"] = bench_blocks(args, mq, synth, torch)
-            line["migration"] = bench_migration(args, mq, synth, torch)
-            line["w4a4"] = bench_w4a4(args, mq, synth, torch)
-        if not args.skip_cpu:
-            line["cpu_baseline"] = cpu_baseline(d["layer"], [1, 4, 16])
+            legs += [("block_4096h_m16", bench_block), ("residual_sweep", bench_sweep),
+                     ("block_residual", bench_blocks), ("migration", bench_migration), ("w4a4", bench_w4a4)]
+    progress("decode")
+    for name, fn in legs:
+        line[name] = fn(args, mq, synth, torch)
+        progress(name)
+    if args.only != "decode" and not args.skip_cpu:
+        line["cpu_baseline"] = cpu_baseline(d["layer"], [1, 4, 16])
+        progress("cpu_baseline")
     print(json.dumps(line), flush=True)
 
 
