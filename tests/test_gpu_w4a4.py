@@ -9,7 +9,9 @@ oracle (oracle/w4a4.py).
   dequantized weights of the oracle's packing (the 4-bit products are exact
   on the matrix cores; what remains is fp32 scaling and accumulation and the
   fp16 output rounding), for plain handles and block-residual handles, over
-  the three workgroup shapes, split K and ragged N, M and K.
+  both workgroup shapes (M <= 16 and above), split K and ragged N, M and K;
+  and at the benchmark's full size (28672 x 8192; M = 512, 2048, 4096) on
+  sampled outputs.
 """
 import numpy as np
 import pytest
@@ -183,3 +185,49 @@ def test_linear_a4_graph_replay(mq):
             torch.cuda.synchronize()
             qx, sx = oa.quantize_activations(X, G)
             check_linear(Yd.cpu().numpy(), oa.dequant_activations(qx, sx, G), Wt, f"graph M={M} replay {rep}")
+
+
+def _sampled_a4(mq, p, X16, G, Wt, what, n_feat=192, n_tok=6, seed=0):
+    """mq_quantize_activations + mq_linear_a4 on all of X, then every token at
+    n_feat output features (always the first and last 16) and every feature at
+    n_tok tokens (always the first and last) against the oracle."""
+    import torch
+    M, N = X16.shape[0], Wt.shape[0]
+    xq, xm = mq.mq_quantize_activations(to_dev(X16), G)
+    Y = mq.mq_linear_a4(xq, xm, p)
+    torch.cuda.synchronize()
+    Y = Y.cpu().numpy()
+    qx, sx = oa.quantize_activations(X16, G)
+    Xh = oa.dequant_activations(qx, sx, G)
+    rng = np.random.default_rng(seed)
+    feats = np.unique(np.concatenate([np.arange(16), np.arange(N - 16, N),
+                                      rng.choice(N, min(N, n_feat), replace=False)]))
+    toks = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, n_tok), replace=False)]))
+    check_linear(Y[:, feats], Xh, Wt[feats], f"{what} features {feats.size} x all tokens")
+    check_linear(Y[toks, :], Xh[toks], Wt, f"{what} tokens {toks.tolist()} x all features")
+
+
+@pytest.mark.timeout(600)
+def test_linear_a4_prefill_layer_full_size(mq):
+    # the 28672 x 8192 layer as the benchmark runs it: plain W4 and 10 % of the
+    # blocks, at M = 512, 2048 and 4096, on sampled outputs
+    from bit_gemm_amd import synth
+    layer = synth.WORKLOADS["prefill-28672x8192"].layers[0]
+    G = layer.group
+    W = layer.W()
+    h = ob.hessian_diag(layer.calibration(128, 4))
+    print("[a4 full size] pack blocks beta=0.1", flush=True)
+    p = mq.mq_pack_blocks(to_dev(W), G, 0.1, to_dev(h))
+    ref = ob.pack_blocks(W, G, 0.1, h)
+    assert np.array_equal(mq.export_blocks(p)["blk"], ref["blk"])
+    Wt = ob.dequant_blocks(ref)
+    del ref
+    for M in (512, 2048, 4096):
+        print(f"[a4 full size] blocks M={M}", flush=True)
+        _sampled_a4(mq, p, layer.X(M), G, Wt, f"a4 prefill blocks M={M}", seed=M)
+    p.free()
+    print("[a4 full size] plain W4 M=2048", flush=True)
+    p = mq.mq_pack(to_dev(W), G, 0.0)
+    Wt = oracle.dequant(oracle.pack(W, G, 0.0))
+    _sampled_a4(mq, p, layer.X(2048), G, Wt, "a4 prefill plain M=2048", seed=7)
+    p.free()
