@@ -130,9 +130,9 @@ struct CfgA4 {
 };
 // 256 x 64 with waves of 32 x 64 (up to 128 VGPRs, so two workgroups share a
 // CU: a larger tile of 8 waves leaves one wave's MFMA-to-VALU dependencies
-// exposed, and the second workgroup's waves fill them); 256 x 16 for decode.
+// exposed, and the second workgroup's waves fill them). Up to 16 tokens run
+// the decode kernel below instead.
 using CfgA4Mid = CfgA4<8, 1, 4>;
-using CfgA4Narrow = CfgA4<8, 1, 1>;
 
 template <int NG, int BM>
 struct StageA4 {
@@ -511,6 +511,22 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void k_gemm_a4(WArrays 
   }
 }
 
+// the handle's arrays for the kernels' buffer resources
+template <bool DR>
+WArrays weight_arrays(const mq_packed* p) {
+  WArrays w;
+  w.tiles = p->tiles;
+  w.tiles_b = (int)(p->Nb * p->Kt * kTileBytes);
+  w.scales = p->scales;
+  w.scales_b = (int)(p->Nb * kRowsPerBlock * p->sstride * 2);
+  w.sstride_b = (uint32_t)(p->sstride * 2);
+  w.rtiles = DR ? (const void*)p->rt_tiles : (const void*)p->tiles;
+  w.rtiles_b = DR ? (int)((p->nblk + 1) * kTileBytes) : 0;
+  w.rscale = DR ? (const void*)p->bscale : (const void*)p->tiles;
+  w.rscale_b = DR ? (int)((p->nblk + 1) * kRowsPerBlock * 4) : 0;
+  return w;
+}
+
 template <class C, int NG, bool DR>
 hipError_t launch_a4(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, int64_t M, uint16_t* Y,
                      hipStream_t s) {
@@ -538,16 +554,7 @@ hipError_t launch_a4(const mq_packed* p, const uint8_t* xq, const uint32_t* xmet
   }
   const DenseA4 dr = DR ? DenseA4{p->rt_slot, reinterpret_cast<const uint4*>(p->rt_tiles), p->bscale, (int)p->nblk}
                         : DenseA4{nullptr, nullptr, nullptr, 0};
-  WArrays warr;
-  warr.tiles = p->tiles;
-  warr.tiles_b = (int)(p->Nb * Kt * kTileBytes);
-  warr.scales = p->scales;
-  warr.scales_b = (int)(p->Nb * kRowsPerBlock * p->sstride * 2);
-  warr.sstride_b = (uint32_t)(p->sstride * 2);
-  warr.rtiles = DR ? (const void*)p->rt_tiles : (const void*)p->tiles;
-  warr.rtiles_b = DR ? (int)((p->nblk + 1) * kTileBytes) : 0;
-  warr.rscale = DR ? (const void*)p->bscale : (const void*)p->tiles;
-  warr.rscale_b = DR ? (int)((p->nblk + 1) * kRowsPerBlock * 4) : 0;
+  const WArrays warr = weight_arrays<DR>(p);
   k_gemm_a4<C, NG, DR><<<dim3((unsigned)T, (unsigned)S), dim3(C::kThreads), kLds, s>>>(
       warr, xq, xmeta, Y, part, (int)M, (int)p->N, Kt, (int)p->Nb, NT, T, per, dr);
   hipError_t e = hipGetLastError();
@@ -574,6 +581,184 @@ hipError_t launch_a4_d(const mq_packed* p, const uint8_t* xq, const uint32_t* xm
                                     : launch_a4_g<C, false>(p, xq, xmeta, M, Y, s);
 }
 
+// ------------------------------------------------------------- W4A4 decode
+
+// Decode (M <= 16): one workgroup per RBW row blocks with the full K; its 8
+// waves split the column tiles, so no partial sums leave the workgroup (no
+// workspace, no second kernel). Each wave requests the codes, scales and
+// residual tiles of up to 4 of its tiles (2 when G < 128) for all RBW row
+// blocks, and their
+// activation codes and metadata, before any math; the 8 partial sums of
+// each row block meet in LDS and are added in wave order.
+template <int NG>
+constexpr int dec_tiles() { return NG == 1 ? 4 : 2; }   // tiles a wave loads ahead (fewer registers for G < 128)
+constexpr int64_t kDecMaxM = 16;   // tokens of one 16-row MFMA operand
+
+template <int NG, int RBW>
+struct DecRegs {
+  static constexpr int T = dec_tiles<NG>();
+  uint4 code[T][RBW];
+  typename WRegs<RBW, NG>::SrawT sraw[T][RBW];
+  uint4 rcode[T][RBW];
+  float rsc[T][RBW];
+  int slot[T][RBW];
+  uint4 a0[T], a1[T];        // the lane's 32 activation bytes (token l % 16) of each tile
+  uint32_t meta[T][4][NG];   // metadata of tokens 4 (l / 16) + 0..3 of each tile
+};
+
+template <int NG, bool DR, int RBW>
+__global__ __launch_bounds__(512) void k_gemv_a4(WArrays warr, const uint8_t* __restrict__ xq,
+                                                 const uint32_t* __restrict__ xmeta, uint16_t* __restrict__ Y,
+                                                 int M, int N, int Kt, int Nb, DenseA4 dr) {
+  __shared__ float4_t red[RBW][8][64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int rb0 = blockIdx.x * RBW;
+  const int kt0 = (Kt * wave) / 8, kt1 = (Kt * (wave + 1)) / 8;
+  const WSrc src = make_wsrc(warr);
+  const int Kp = Kt * kTileCols, ngt = Kt * NG;
+  // tokens past M read as zero codes and zero metadata
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(xq), 0, M * Kp, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t mrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(xmeta), 0, M * ngt * 4, kBufferFlags);
+  const uint32_t vcode = 16u * (uint32_t)lane, vscale = (uint32_t)r * src.sstride_b, vrs = 4u * (uint32_t)r;
+  const uint32_t va = (uint32_t)(r * Kp + 32 * g);
+
+  float4_t acc[RBW];
+#pragma unroll
+  for (int j = 0; j < RBW; ++j) acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int T = dec_tiles<NG>();
+  for (int base = kt0; base < kt1; base += T) {
+    DecRegs<NG, RBW> D;
+    // every load of the batch first (tiles past kt1 are clamped; their math is skipped)
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int kt = min(base + t, Kt - 1);
+      const auto a0 = __builtin_amdgcn_raw_buffer_load_b128(xrs, va, kt * kTileCols, 0);
+      const auto a1 = __builtin_amdgcn_raw_buffer_load_b128(xrs, va, kt * kTileCols + 16, 0);
+      D.a0[t] = make_uint4(a0[0], a0[1], a0[2], a0[3]);
+      D.a1[t] = make_uint4(a1[0], a1[1], a1[2], a1[3]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+          D.meta[t][q][gi] =
+              __builtin_amdgcn_raw_buffer_load_b32(mrs, (uint32_t)(((4 * g + q) * ngt + kt * NG + gi) * 4), 0, 0);
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) {
+        const int rb = min(rb0 + j, Nb - 1);
+        const auto c = __builtin_amdgcn_raw_buffer_load_b128(src.tiles, vcode, (rb * Kt + kt) * kTileBytes, 0);
+        D.code[t][j] = make_uint4(c[0], c[1], c[2], c[3]);
+        const int srow = rb * kRowsPerBlock * (int)src.sstride_b;
+        if constexpr (NG == 1) {
+          D.sraw[t][j] = __builtin_amdgcn_raw_buffer_load_b32(src.scales, vscale, srow + 4 * (kt >> 1), 0);
+        } else if constexpr (NG == 2) {
+          D.sraw[t][j] = __builtin_amdgcn_raw_buffer_load_b32(src.scales, vscale, srow + 4 * kt, 0);
+        } else {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(src.scales, vscale, srow + 8 * kt, 0);
+          D.sraw[t][j] = make_uint2(v[0], v[1]);
+        }
+        if constexpr (DR) {
+          const int sl = __builtin_amdgcn_readfirstlane(dr.slot[(int64_t)rb * Kt + kt]);
+          D.slot[t][j] = sl;
+          const auto rc = __builtin_amdgcn_raw_buffer_load_b128(src.rtiles, vcode, sl * kTileBytes, 0);
+          D.rcode[t][j] = make_uint4(rc[0], rc[1], rc[2], rc[3]);
+          D.rsc[t][j] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(src.rscale, vrs, sl * kRowsPerBlock * 4, 0));
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int kt = base + t;
+      if (kt >= kt1) break;   // wave-uniform
+      i32x8_t a;
+      a[0] = (int32_t)D.a0[t].x; a[1] = (int32_t)D.a0[t].y; a[2] = (int32_t)D.a0[t].z; a[3] = (int32_t)D.a0[t].w;
+      a[4] = (int32_t)D.a1[t].x; a[5] = (int32_t)D.a1[t].y; a[6] = (int32_t)D.a1[t].z; a[7] = (int32_t)D.a1[t].w;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        i32x8_t ag = a;
+        if constexpr (NG > 1) {
+          constexpr int W = 8 / NG;
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (k / W != gi) ag[k] = 0;
+        }
+        float4_t cv, sv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t mv = D.meta[t][q][gi];
+          sv[q] = h_to_f(mv & 0xFFFFu) * 512.0f;
+          cv[q] = (float)(int16_t)(uint16_t)(mv >> 16) * -0.015625f;
+        }
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) {
+          const float sw = group_scale<NG>(D.sraw[t][j], kt, gi);
+          const float4_t d = mfma_fp8(ag, split_nibbles(D.code[t][j]), cv);
+          acc[j] += d * (sv * sw);
+          if constexpr (DR) {
+            if (D.slot[t][j] != dr.nblk) {   // wave-uniform
+              const float4_t e = mfma_fp8(ag, split_nibbles(D.rcode[t][j]), cv);
+              acc[j] += e * (sv * D.rsc[t][j]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < RBW; ++j) red[j][wave][lane] = acc[j];
+  __syncthreads();
+  if (wave < RBW && rb0 + wave < Nb) {   // wave j adds row block j's 8 partials in wave order
+    float4_t sum = red[wave][0][lane];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) sum += red[wave][w][lane];
+    const int n = (rb0 + wave) * kRowsPerBlock + r;
+    if (n < N) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = 4 * g + q;
+        if (m < M) Y[m * N + n] = f32_to_h(sum[q]);
+      }
+    }
+  }
+}
+
+template <int NG, bool DR, int RBW>
+hipError_t launch_dec(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, int64_t M, uint16_t* Y,
+                      hipStream_t s) {
+  const WArrays warr = weight_arrays<DR>(p);
+  const DenseA4 dr = DR ? DenseA4{p->rt_slot, reinterpret_cast<const uint4*>(p->rt_tiles), p->bscale, (int)p->nblk}
+                        : DenseA4{nullptr, nullptr, nullptr, 0};
+  const unsigned grid = (unsigned)((p->Nb + RBW - 1) / RBW);
+  k_gemv_a4<NG, DR, RBW><<<dim3(grid), dim3(512), 0, s>>>(warr, xq, xmeta, Y, (int)M, (int)p->N, (int)p->Kt,
+                                                          (int)p->Nb, dr);
+  return hipGetLastError();
+}
+
+// row blocks per workgroup: enough that one round of workgroups covers the
+// layer on 256 CUs, at most 4
+template <int NG, bool DR>
+hipError_t launch_dec_r(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, int64_t M, uint16_t* Y,
+                        hipStream_t s) {
+  const int64_t rbw = std::min<int64_t>(4, std::max<int64_t>(1, (p->Nb + 255) / 256));
+  if (rbw == 1) return launch_dec<NG, DR, 1>(p, xq, xmeta, M, Y, s);
+  if (rbw == 2) return launch_dec<NG, DR, 2>(p, xq, xmeta, M, Y, s);
+  if (rbw == 3) return launch_dec<NG, DR, 3>(p, xq, xmeta, M, Y, s);
+  return launch_dec<NG, DR, 4>(p, xq, xmeta, M, Y, s);
+}
+
+template <bool DR>
+hipError_t launch_dec_g(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, int64_t M, uint16_t* Y,
+                        hipStream_t s) {
+  if (p->G == 128) return launch_dec_r<1, DR>(p, xq, xmeta, M, Y, s);
+  if (p->G == 64) return launch_dec_r<2, DR>(p, xq, xmeta, M, Y, s);
+  return launch_dec_r<4, DR>(p, xq, xmeta, M, Y, s);
+}
+
 }  // namespace
 
 hipError_t quantize_a4(const uint16_t* X, int64_t M, int64_t K, int G, uint8_t* xq, uint32_t* xmeta, hipStream_t s) {
@@ -588,7 +773,10 @@ hipError_t quantize_a4(const uint16_t* X, int64_t M, int64_t K, int G, uint8_t* 
 
 hipError_t launch_gemm_a4(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, int64_t M, uint16_t* Y,
                           hipStream_t s) {
-  if (M <= 16) return launch_a4_d<CfgA4Narrow>(p, xq, xmeta, M, Y, s);
+  if (M <= kDecMaxM) {
+    return (p->blocks && p->nblk > 0) ? launch_dec_g<true>(p, xq, xmeta, M, Y, s)
+                                      : launch_dec_g<false>(p, xq, xmeta, M, Y, s);
+  }
   return launch_a4_d<CfgA4Mid>(p, xq, xmeta, M, Y, s);
 }
 
