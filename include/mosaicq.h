@@ -324,9 +324,10 @@ mq_status mq_quantize_activations(const void* X_dev_fp16, int64_t M, int64_t K, 
  *   hip_stream      stream to enqueue on (no synchronisation)
  *
  * The products run on the fp8 matrix cores exactly (4-bit integers) and each
- * group's sum is scaled and added in fp32. Like mq_linear's GEMM it splits K
- * when the output tiles are few, with a stream-ordered fp32 workspace of at
- * most 64 MiB (MQ_ERR_OUT_OF_MEMORY if it cannot be had). Deterministic.
+ * group's sum is scaled and added in fp32. Up to 16 tokens one kernel runs
+ * with no workspace; above that, like mq_linear's GEMM, it splits K when the
+ * output tiles are few, with a stream-ordered fp32 workspace of at most
+ * 16 MiB (MQ_ERR_OUT_OF_MEMORY if it cannot be had). Deterministic.
  * Errors: MQ_ERR_BAD_HANDLE, MQ_ERR_INVALID_ARG, MQ_ERR_UNSUPPORTED (a
  * handle with single residual entries: their per-entry scale cannot join the
  * integer sum; pack with mq_pack_blocks instead; or base codes of 2 GiB or
