@@ -52,9 +52,11 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-extra", action="store_true",
                     help="skip the transformer-block, residual-sweep, block-residual, migration and W4A4 legs")
-    ap.add_argument("--only", choices=["decode", "prefill", "copy", "blocks", "migration", "w4a4"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "copy", "stream", "blocks", "migration", "w4a4"],
+                    default=None,
                     help="run one leg only (profiling runs); 'copy' runs the plain device copy that "
-                         "calibrates the HBM byte counters")
+                         "calibrates the HBM byte counters; 'stream' times a plain streaming read of a "
+                         "decode layer's size (the HBM read ceiling of the decode kernels)")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the warm single-copy decode leg (keeps per-kernel profiles all-cold)")
     return ap.parse_args()
@@ -128,10 +130,14 @@ def replay_spread(torch, fn, warmup, steps, reps=9):
     return float(np.median(out)), float(np.percentile(out, 10)), float(np.percentile(out, 90))
 
 
-def source_digest():
-    """sha256 of the decode kernel sources (counters are only valid for these)."""
+DECODE_SOURCES = ("gemv.hip", "kernel_common.h", "mq_internal.h")
+GEMM_SOURCES = ("gemm.hip", "kernel_common.h", "mq_internal.h")
+
+
+def source_digest(files=DECODE_SOURCES):
+    """sha256 of kernel sources: a profile summary is only valid for these."""
     h = hashlib.sha256()
-    for f in ("gemv.hip", "kernel_common.h", "mq_internal.h"):
+    for f in files:
         with open(os.path.join(ROOT, "bit_gemm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -141,19 +147,76 @@ def counted_traffic(kernel_tag):
     """HBM bytes per launch that rocprofv3 counted for `kernel_tag`, from the
     committed counter summary, or None when the summary is missing or was
     taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", "decode_hbm_counters.txt")
+    v = profile_values("decode_hbm_counters.txt", DECODE_SOURCES).get(f"hbm_bytes_per_launch[{kernel_tag}]")
+    return float(v) if v else None
+
+
+def profile_values(name, sources):
+    """key: value lines of a committed rocprofv3 summary under profiles/, or
+    {} when the file is missing or its `source_sha256` differs from the
+    current sources of the kernel it describes (then its figures are stale)."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
-        return None
+        return {}
     vals = {}
     with open(path) as fh:
         for line in fh:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("source_sha256") != source_digest():
+    if vals.get("source_sha256") != source_digest(sources):
+        return {}
+    return vals
+
+
+class ClockSampler:
+    """Samples the shader clock the driver reports (the active DPM level of
+    pp_dpm_sclk) every few ms while a timed region runs; None where the
+    file is not readable."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period, self.samples = period_s, []
+        self._stop = threading.Event()
+        self._thr = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for p in self.paths:
+            try:
+                with open(p) as fh:
+                    for line in fh:
+                        if line.rstrip().endswith("*"):
+                            return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+            except (OSError, ValueError, IndexError):
+                continue
         return None
-    v = vals.get(f"hbm_bytes_per_launch[{kernel_tag}]")
-    return float(v) if v else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._thr.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.paths:
+            self._thr.join()
+
+    def summary(self):
+        import numpy as np
+        if not self.samples:
+            return None
+        a = np.array(self.samples)
+        return {"samples": int(a.size), "median_MHz": float(np.median(a)), "max_MHz": float(a.max()),
+                "min_MHz": float(a.min())}
 
 
 def bench_decode(args, mq, synth, torch):
@@ -180,9 +243,11 @@ def bench_decode(args, mq, synth, torch):
     Ys = {M: torch.empty((M, layer.N), dtype=torch.float16, device="cuda") for M in Ms}
 
     def step(i):
-        p = copies[i % ncopy]
-        for M in Ms:
-            mq.mq_linear_with(Xs[M], p, mq.KERNEL_GEMV, Ys[M])
+        # every launch of the step reads its own packed copy (the copies are
+        # dealt in launch order), so no launch finds the weights that the
+        # launch before it pulled into the Infinity Cache
+        for j, M in enumerate(Ms):
+            mq.mq_linear_with(Xs[M], copies[(len(Ms) * i + j) % ncopy], mq.KERNEL_GEMV, Ys[M])
 
     ms = time_graphs(torch, step, args.warmup, args.steps)
     bytes_step = sum(decode_bytes(first, M) for M in Ms)
@@ -255,11 +320,22 @@ def bench_prefill(args, mq, synth, torch):
         def run(i):
             mq.mq_linear_with(X, p, mq.KERNEL_GEMM, Y)
         time_events(run, max(2, args.warmup // 4))
-        ms = time_events(run, n) / n
+        with ClockSampler() as clk:
+            ms = time_events(run, n) / n
         tflops = 2.0 * M * layer.N * layer.K / (ms * 1e-3) / 1e12
         out["M"][str(M)] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tflops, 1),
-                            "frac_mfma_peak": round(tflops / FP16_PEAK_TFLOPS, 4)}
+                            "frac_mfma_peak": round(tflops / FP16_PEAK_TFLOPS, 4), "sclk": clk.summary()}
     p.free()
+    # roofline of the GEMM at the largest M: achieved TFLOP/s against the
+    # dense fp16 MFMA peak, with the matrix-core busy fraction and the clock
+    # that the committed rocprofv3 counter summary measured for this kernel
+    mtop = str(max(wl.batch))
+    cnt = profile_values("prefill_mfma_counters.txt", GEMM_SOURCES)
+    out["roofline"] = {"bound": "mfma", "achieved": out["M"][mtop]["TFLOPs"], "peak": FP16_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": out["M"][mtop]["frac_mfma_peak"], "M": int(mtop),
+                       "flops_per_launch": 2 * int(mtop) * layer.N * layer.K,
+                       "profile_mfma_busy": float(cnt[f"mfma_busy[M={mtop}]"]) if f"mfma_busy[M={mtop}]" in cnt else None,
+                       "profile_clock_GHz": float(cnt[f"clock_GHz[M={mtop}]"]) if f"clock_GHz[M={mtop}]" in cnt else None}
     # the same layer without residual (rho = 0): t(rho) / t(0)
     W = torch.from_numpy(layer.W()).cuda()
     p0 = mq.mq_pack(W, layer.group, 0.0)
@@ -602,6 +678,28 @@ def bench_w4a4(args, mq, synth, torch):
     return res
 
 
+def bench_stream(args, mq, torch, nbytes=24 << 20):
+    """Read ceiling: mq_stream_read over `nbytes` (the decode layer's packed
+    size), every launch on another buffer (rotated over more than twice the
+    Infinity Cache), back-to-back launches in a graph, at several grid sizes.
+    Per-launch period from HIP events, as for the decode kernels."""
+    nbuf = max(2, math.ceil(2 * MALL_BYTES / nbytes))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255) for _ in range(nbuf)]
+    out = {"bytes": nbytes, "buffers": nbuf, "by_workgroups": {}}
+    for wg in (384, 768, 1536, 3072, 6144):   # 16, 8, 4, 2, 1 loads per thread
+        sink = torch.empty(wg, dtype=torch.int32, device="cuda")
+
+        def rd(i, wg=wg, sink=sink):
+            mq.mq_stream_read(bufs[i % nbuf], wg, sink)
+        med, p10, p90 = replay_spread(torch, rd, max(2, args.warmup // 4), max(20, args.steps // 2), reps=5)
+        out["by_workgroups"][str(wg)] = {"us": round(med * 1e3, 3), "p10_us": round(p10 * 1e3, 3),
+                                         "p90_us": round(p90 * 1e3, 3),
+                                         "GBps": round(nbytes / (med * 1e-3) / 1e9, 1)}
+    best = min(out["by_workgroups"].values(), key=lambda v: v["us"])
+    out["best"] = best
+    return out
+
+
 def cpu_baseline(layer, Ms, min_seconds=10.0, max_steps=60):
     """The oracle, as it stands, on the same decode layer: one step is its
     dequantisation plus the float64 linear for M = 1, 4, 16 (packing by the
@@ -665,6 +763,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}), flush=True)
         return
+    if args.only == "stream":
+        print(json.dumps({"stream_read": bench_stream(args, mq, torch)}), flush=True)
+        return
     if args.only == "prefill":
         print(json.dumps({"prefill": bench_prefill(args, mq, synth, torch)}), flush=True)
         return
@@ -685,6 +786,12 @@ def main():
     achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
     tag = ("k_gemv_x" if int(mdom) <= 4 else "k_gemv_r") + f"@M={mdom}"
     traffic = counted_traffic(tag)
+    # the same kernel's average duration in the committed rocprofv3 kernel
+    # trace of `bench.py --only decode` (kernel time alone, without the
+    # dispatch gap that a graph replay's per-launch period includes)
+    trace = profile_values("decode_kernel_stats.txt", DECODE_SOURCES)
+    trace_us = float(trace[f"kernel_avg_us[{tag}]"]) if f"kernel_avg_us[{tag}]" in trace else None
+    period_us = float(trace[f"launch_period_us[{tag}]"]) if f"launch_period_us[{tag}]" in trace else None
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(d["ms_per_step"], 5),
@@ -692,10 +799,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode-11008x4096", "N": 11008, "K": 4096, "group": 128, "rho": 0.005,
                    "nnz": d["nnz"], "M": [1, 4, 16], "packed_copies": d["copies"],
-                   "timing": "hip graph replay"},
+                   "timing": "hip graph replay; every launch reads another packed copy"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": tag,
-                     "algorithmic_bytes_per_launch": dom["bytes"], "avg_launch_us": dom["us"]},
+                     "algorithmic_bytes_per_launch": dom["bytes"], "avg_launch_us": dom["us"],
+                     "time_basis": "live: HIP events around a graph of back-to-back launches of this kernel "
+                                   "(each on another packed copy) / launches = launch period, kernel + dispatch gap",
+                     "profile_launch_period_us": period_us, "profile_kernel_avg_us": trace_us,
+                     "frac_kernel_time": (round(dom["bytes"] / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                          if trace_us else None)},
         "decode_per_M": d["per_m"],
         "decode_residual_overhead_t_rho_over_t0": d["overhead"],
         "decode_unfused_two_kernels": d["unfused"],

@@ -364,6 +364,17 @@ MQ_API mq_status mq_linear_a4(const void* xq_dev_u8, const void* xmeta_dev_u32, 
                                      static_cast<uint16_t*>(Y_dev_fp16), static_cast<hipStream_t>(hip_stream)));
 }
 
+MQ_API mq_status mq_stream_read(const void* src_dev, int64_t bytes, int32_t workgroups, void* sink_dev_u32,
+                                void* hip_stream) {
+  if (!src_dev || !sink_dev_u32 || bytes <= 0 || workgroups <= 0) return MQ_ERR_INVALID_ARG;
+  if ((bytes & 15) != 0 || (reinterpret_cast<uintptr_t>(src_dev) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(sink_dev_u32) & 3u) != 0)
+    return MQ_ERR_INVALID_ARG;
+  if (bytes / 16 > (int64_t)workgroups * 256 * 16) return MQ_ERR_INVALID_ARG;   // at most 16 chunks per thread
+  return from_hip(mq::stream_read(src_dev, bytes, workgroups, static_cast<uint32_t*>(sink_dev_u32),
+                                  static_cast<hipStream_t>(hip_stream)));
+}
+
 MQ_API mq_status mq_packed_info(const mq_packed* p, int64_t* N, int64_t* K, int32_t* G, int64_t* nnz,
                                 size_t* bytes) {
   if (!is_live(p)) return MQ_ERR_BAD_HANDLE;

@@ -126,6 +126,10 @@ hipError_t quantize_a4(const uint16_t* X, int64_t M, int64_t K, int G, uint8_t* 
 hipError_t launch_gemm_a4(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, int64_t M, uint16_t* Y,
                           hipStream_t stream);
 
+// Streaming-read probe (probe.hip): reads bytes (a multiple of 16) of src
+// with 16-byte loads, one XOR word per workgroup into sink[workgroups].
+hipError_t stream_read(const void* src, int64_t bytes, int workgroups, uint32_t* sink, hipStream_t stream);
+
 constexpr int64_t kGemvMaxM = 64;       // the GEMV kernels accept up to 64 tokens
 constexpr int64_t kAutoGemvMaxM = 16;   // the automatic choice takes them up to 16
 

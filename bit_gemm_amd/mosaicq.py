@@ -24,7 +24,7 @@ GEMV_MAX_M = 64
 EXPORTED = ("mq_pack", "mq_linear", "mq_linear_with", "mq_residual_add", "mq_packed_info",
             "mq_export_canonical", "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks",
             "mq_smooth_weights", "mq_smooth_activations", "mq_quantize_activations", "mq_linear_a4",
-            "mq_free", "mq_status_string")
+            "mq_stream_read", "mq_free", "mq_status_string")
 
 
 class MQError(RuntimeError):
@@ -67,6 +67,8 @@ def _load():
     lib.mq_quantize_activations.restype = ctypes.c_int
     lib.mq_linear_a4.argtypes = [vp, vp, i64, vp, vp, vp]
     lib.mq_linear_a4.restype = ctypes.c_int
+    lib.mq_stream_read.argtypes = [vp, i64, i32, vp, vp]
+    lib.mq_stream_read.restype = ctypes.c_int
     lib.mq_free.argtypes = [vp]
     lib.mq_free.restype = None
     lib.mq_status_string.argtypes = [ctypes.c_int]
@@ -291,6 +293,19 @@ def mq_residual_add(X, packed: Packed, Y, stream=None):
         raise ValueError(f"Y must be [{M}, {packed.N}]")
     _check(lib.mq_residual_add(xp, M, packed.handle, yp, _stream_handle(stream)), "mq_residual_add")
     return Y
+
+
+def mq_stream_read(src, workgroups: int, sink, stream=None):
+    """Read every byte of the device tensor `src` once (measurement helper;
+    see mq_stream_read in include/mosaicq.h); sink: int32 [workgroups]."""
+    import torch
+    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous():
+        raise TypeError("src must be a contiguous GPU tensor")
+    if sink.dtype != torch.int32 or sink.numel() < workgroups or not sink.is_cuda:
+        raise TypeError(f"sink must be an int32 GPU tensor of at least {workgroups} elements")
+    nbytes = src.numel() * src.element_size()
+    _check(lib.mq_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, int(workgroups),
+                              ctypes.c_void_p(sink.data_ptr()), _stream_handle(stream)), "mq_stream_read")
 
 
 def mq_packed_info(packed: Packed) -> dict:

@@ -336,6 +336,20 @@ mq_status mq_quantize_activations(const void* X_dev_fp16, int64_t M, int64_t K, 
 mq_status mq_linear_a4(const void* xq_dev_u8, const void* xmeta_dev_u32, int64_t M, const mq_packed* p,
                        void* Y_dev_fp16, void* hip_stream);
 
+/*
+ * mq_stream_read -- measurement helper, not a step of the method: reads
+ * `bytes` of src_dev once with 16-byte loads (workgroups of 256 threads,
+ * each thread issuing all of its U = ceil(bytes / (16 * 256 * workgroups))
+ * loads before using any, U <= 16) and writes the XOR of what workgroup b
+ * read to sink_dev_u32[b]. Timed on a buffer of a decode layer's size, it
+ * gives the streaming HBM read rate the decode kernels are compared with.
+ * bytes > 0 and a multiple of 16, U <= 16, src 16-byte and sink 4-byte
+ * aligned, sink holds `workgroups` words; else MQ_ERR_INVALID_ARG.
+ * Enqueued only.
+ */
+mq_status mq_stream_read(const void* src_dev, int64_t bytes, int32_t workgroups, void* sink_dev_u32,
+                         void* hip_stream);
+
 /* mq_free -- release a handle and its device memory (NULL is accepted). The
  * caller must make sure no enqueued mq_linear still reads it. */
 void mq_free(mq_packed* p);

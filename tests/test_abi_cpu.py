@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
-        ["mq_pack", "mq_linear", "mq_linear_with", "mq_residual_add", "mq_packed_info", "mq_export_canonical",
+        ["mq_pack", "mq_linear", "mq_linear_with", "mq_residual_add", "mq_stream_read", "mq_packed_info", "mq_export_canonical",
          "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks", "mq_smooth_weights",
          "mq_smooth_activations", "mq_quantize_activations", "mq_linear_a4", "mq_free", "mq_status_string"])
 
@@ -136,3 +136,14 @@ def test_linear_a4_validation(lib):
     f = lib.mq_linear_a4
     assert f(FAKE, FAKE, 4, None, FAKE, None) == -6              # no handle
     assert f(FAKE, FAKE, 4, FAKE, FAKE, None) == -6              # not a live handle
+
+
+def test_stream_read_validation(lib):
+    f = lib.mq_stream_read
+    assert f(None, 1024, 4, FAKE, None) == -1
+    assert f(FAKE, 0, 4, FAKE, None) == -1
+    assert f(FAKE, 1000, 4, FAKE, None) == -1                       # not a multiple of 16
+    assert f(FAKE, 1024, 0, FAKE, None) == -1
+    assert f(ctypes.c_void_p((1 << 20) + 8), 1024, 4, FAKE, None) == -1
+    assert f(FAKE, 1024, 4, ctypes.c_void_p((1 << 20) + 2), None) == -1
+    assert f(FAKE, 16 * 256 * 16 + 16, 1, FAKE, None) == -1      # more than 16 loads per thread

@@ -46,6 +46,24 @@ def test_linear_small_layers_both_kernels(mq, N, K, G, rho):
             check_linear(Y, X, Wt, f"N={N} K={K} M={M} kernel={kern}")
 
 
+def test_linear_k65536_with_residual_in_every_window(mq):
+    """K = 65536: the residual stream's columns are stored mod 4096, so each
+    of the 16 column windows of a row block has its own segment; residual in
+    every window, both kernels, decode and GEMM batch sizes."""
+    N, K, G, rho = 40, 65536, 64, 0.004
+    W = _layer(N, K, seed=65536, outlier_cols=3)
+    p = mq.mq_pack(to_dev(W), G, rho)
+    ref = oracle.pack(W, G, rho)
+    assert np.unique(ref["col"].astype(np.int64) // 4096).size == 16, "every window holds residual entries"
+    Wt = oracle.dequant(ref)
+    for M in (1, 5, 16, 17, 64):
+        X = _x(M, K, seed=7 + M)
+        for kern in (mq.KERNEL_GEMV, mq.KERNEL_GEMM):
+            print(f"[linear parity] K=65536 rho={rho} M={M} kernel={kern}", flush=True)
+            Y = mq.mq_linear_with(to_dev(X), p, kern).cpu().numpy()
+            check_linear(Y, X, Wt, f"K=65536 M={M} kernel={kern}")
+
+
 def test_one_hot_rows_reproduce_the_dequantised_weights(mq):
     """P9: X rows = unit vectors e_j give Y[:, i] = W~[i, j] (to fp16), for
     every position of a tile, so any index mistake in either kernel shows."""
@@ -65,10 +83,11 @@ def test_one_hot_rows_reproduce_the_dequantised_weights(mq):
 
 
 # K = 4096 decode shapes: the up-to-4-token kernel (X slices in LDS) and the
-# several-row-blocks-per-workgroup kernel (1, 2 or 3 row blocks, the last
+# several-row-blocks-per-workgroup kernel (1, 2, 3 or 4 row blocks, the last
 # workgroup partly past the end), ragged N, no residual, and residual
 # densities whose chunks overflow the two prefetched per wave
-K4096 = [(40, 128, 0.3), (16, 128, 0.0), (4100, 64, 0.01), (8210, 32, 0.002), (1000, 128, 0.02)]
+K4096 = [(40, 128, 0.3), (16, 128, 0.0), (4100, 64, 0.01), (8210, 32, 0.002), (1000, 128, 0.02),
+         (11008, 128, 0.005), (14336, 128, 0.005), (12300, 64, 0.01)]
 
 
 @pytest.mark.parametrize("N,G,rho", K4096)

@@ -142,6 +142,47 @@ def test_linear_a4_blocks(mq, N, K, G, beta):
     _linear_cases(mq, p, Wt, K, G, MS, f"blocks N={N} K={K} G={G} beta={beta}")
 
 
+# Decode (M <= 16) takes ceil(Nb / 256) row blocks per workgroup, at most 4:
+# N = 4100 -> 2, 8200 -> 3, 12300 -> 4 (the last workgroup partly past the
+# end), plain and block handles, G = 128, 64 and 32
+DEC_RBW = [(4100, 512, 64, 0.0), (4100, 256, 32, 0.2), (8200, 384, 128, 0.0), (8200, 512, 64, 0.1),
+           (12300, 256, 128, 0.0), (12300, 512, 32, 0.05)]
+
+
+@pytest.mark.parametrize("N,K,G,beta", DEC_RBW)
+def test_linear_a4_decode_row_blocks_per_workgroup(mq, N, K, G, beta):
+    W = _layer(N, K, 7 * N + K)
+    if beta > 0:
+        rng = np.random.default_rng(N + G)
+        Xc = rng.standard_normal((32, K)).astype(np.float16)
+        Xc[:, rng.choice(K, 4, replace=False)] *= 50
+        h = ob.hessian_diag(Xc)
+        p = mq.mq_pack_blocks(to_dev(W), G, beta, to_dev(h))
+        ref = ob.pack_blocks(W, G, beta, h)
+        assert p.nblk == ref["blk"].size and p.nblk > 0
+        Wt = ob.dequant_blocks(ref)
+    else:
+        p = mq.mq_pack(to_dev(W), G, 0.0)
+        Wt = oracle.dequant(oracle.pack(W, G, 0.0))
+    _linear_cases(mq, p, Wt, K, G, (1, 5, 16), f"decode rbw N={N} K={K} G={G} beta={beta}")
+    p.free()
+
+
+def test_linear_a4_decode_layer_11008x4096(mq):
+    # the decode layer the benchmark times (3 row blocks per workgroup), plain
+    # and with 10 % of the blocks, at M = 1, 5 and 16, every output
+    from bit_gemm_amd import synth
+    layer = synth.WORKLOADS["decode-11008x4096"].layers[0]
+    W, G = layer.W(), layer.group
+    h = ob.hessian_diag(layer.calibration(128, 4))
+    for name, make, ref in (("plain", lambda: mq.mq_pack(to_dev(W), G, 0.0), lambda: oracle.dequant(oracle.pack(W, G, 0.0))),
+                            ("blocks", lambda: mq.mq_pack_blocks(to_dev(W), G, 0.1, to_dev(h)),
+                             lambda: ob.dequant_blocks(ob.pack_blocks(W, G, 0.1, h)))):
+        p = make()
+        _linear_cases(mq, p, ref(), layer.K, G, (1, 5, 16), f"decode 11008x4096 {name}")
+        p.free()
+
+
 def test_linear_a4_rejects_element_residual(mq):
     W = _layer(32, 256, 5)
     p = mq.mq_pack(to_dev(W), 128, 0.01)
