@@ -319,6 +319,21 @@ MQ_API mq_status mq_linear_with(const void* X_dev_fp16, int64_t M, const mq_pack
   return linear_impl(X_dev_fp16, M, p, Y_dev_fp16, hip_stream, kernel);
 }
 
+MQ_API mq_status mq_linear_noalloc(const void* X_dev_fp16, int64_t M, const mq_packed* p, void* Y_dev_fp16,
+                                   void* hip_stream) {
+  if (!is_live(p)) return MQ_ERR_BAD_HANDLE;
+  if (!X_dev_fp16 || !Y_dev_fp16 || M <= 0) return MQ_ERR_INVALID_ARG;
+  if (M > (int64_t(1) << 31) / p->K || M > (int64_t(1) << 31) / p->N) return MQ_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(X_dev_fp16) & 15u) != 0 || (reinterpret_cast<uintptr_t>(Y_dev_fp16) & 7u) != 0)
+    return MQ_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const uint16_t* X = static_cast<const uint16_t*>(X_dev_fp16);
+  uint16_t* Y = static_cast<uint16_t*>(Y_dev_fp16);
+  if (M <= mq::kAutoGemvMaxM) return from_hip(mq::launch_gemv(p, X, M, Y, s));   // no workspace on this path
+  if (mq::gemm_workspace_bytes(p, M) > mq::gemm_scratch_capacity()) return MQ_ERR_UNSUPPORTED;
+  return from_hip(mq::launch_gemm_noalloc(p, X, M, Y, s));
+}
+
 MQ_API mq_status mq_residual_add(const void* X_dev_fp16, int64_t M, const mq_packed* p, void* Y_dev_fp16,
                                  void* hip_stream) {
   if (!is_live(p)) return MQ_ERR_BAD_HANDLE;

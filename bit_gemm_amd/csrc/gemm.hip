@@ -26,6 +26,7 @@
 // the tile's residual codes with the row's residual scale and adds them to
 // the staged weights, instead of patching single entries.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "kernel_common.h"
@@ -530,8 +531,37 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   store4(Y + (int64_t)m * N + n0, sum, N - n0, (N & 3) == 0);
 }
 
+// Workspace of the entry point that allocates nothing (mq_linear_noalloc):
+// the split-K partial sums live in this array instead of a stream-ordered
+// allocation. Host code never names it directly: its device address comes
+// from hipGetSymbolAddress, once per device (each GPU has its own copy).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// split-K parts for a layer and token count (1 = no split)
+template <class C>
+int split_parts(const mq_packed* p, int64_t M, int* per_out) {
+  const int NT = (int)((p->Nb + (BN / kRowsPerBlock) - 1) / (BN / kRowsPerBlock));
+  const int MT = (int)((M + C::kBM - 1) / C::kBM);
+  const int T = NT * MT;
+  const int Kt = (int)p->Kt;
+  // Split K when the output tiles cannot fill the chip's 256 CUs: about one
+  // round of workgroups, at least 2 code tiles per split.
+  int S = 1;
+  if (T < kSplitTarget) S = std::max(1, std::min(kSplitTarget / T, Kt / 2));
+  const int per = (Kt + S - 1) / S;
+  if (per_out) *per_out = per;
+  return (Kt + per - 1) / per;
+}
+
+// ws: caller's workspace for the split-K partials (nullptr: allocate it on
+// the stream for this call)
 template <int GSH, bool KTAIL, class C, bool DR>
-hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
+hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s, float* ws) {
   constexpr int BM = C::kBM;
   static bool attr_set = false;
   if (!attr_set) {
@@ -544,16 +574,16 @@ hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y,
   const int MT = (int)((M + BM - 1) / BM);
   const int T = NT * MT;
   const int Kt = (int)p->Kt;
-  // Split K when the output tiles cannot fill the chip's 256 CUs: about one
-  // round of workgroups, at least 2 code tiles per split.
-  int S = 1;
-  if (T < kSplitTarget) S = std::max(1, std::min(kSplitTarget / T, Kt / 2));
-  const int per = (Kt + S - 1) / S;
-  S = (Kt + per - 1) / per;
+  int per = Kt;
+  const int S = split_parts<C>(p, M, &per);
   float* part = nullptr;
   if (S > 1) {
-    const hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&part), (size_t)S * M * p->N * sizeof(float), s);
-    if (e != hipSuccess) return e;
+    if (ws) {
+      part = ws;
+    } else {
+      const hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&part), (size_t)S * M * p->N * sizeof(float), s);
+      if (e != hipSuccess) return e;
+    }
   }
   const DenseGemm dr = DR ? DenseGemm{p->rt_slot, reinterpret_cast<const uint2*>(p->rt_tiles), p->bscale}
                           : DenseGemm{nullptr, nullptr, nullptr};
@@ -565,8 +595,10 @@ hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y,
     if (e == hipSuccess) {
       e = launch_splitk_reduce(part, Y, M, p->N, S, s);
     }
-    const hipError_t f = hipFreeAsync(part, s);
-    if (e == hipSuccess) e = f;
+    if (!ws) {
+      const hipError_t f = hipFreeAsync(part, s);
+      if (e == hipSuccess) e = f;
+    }
   }
   return e;
 }
@@ -574,21 +606,22 @@ hipError_t launch(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y,
 }  // namespace
 
 template <bool KTAIL, class C, bool DR>
-hipError_t launch_g(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
-  if (p->G == 128) return launch<0, KTAIL, C, DR>(p, X, M, Y, s);
-  if (p->G == 64) return launch<1, KTAIL, C, DR>(p, X, M, Y, s);
-  return launch<2, KTAIL, C, DR>(p, X, M, Y, s);
+hipError_t launch_g(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s, float* ws) {
+  if (p->G == 128) return launch<0, KTAIL, C, DR>(p, X, M, Y, s, ws);
+  if (p->G == 64) return launch<1, KTAIL, C, DR>(p, X, M, Y, s, ws);
+  return launch<2, KTAIL, C, DR>(p, X, M, Y, s, ws);
 }
 
 // handles from mq_pack_blocks carry their residual as code tiles (DR)
 template <bool KTAIL, class C>
-hipError_t launch_d(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
-  return p->blocks ? launch_g<KTAIL, C, true>(p, X, M, Y, s) : launch_g<KTAIL, C, false>(p, X, M, Y, s);
+hipError_t launch_d(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s, float* ws) {
+  return p->blocks ? launch_g<KTAIL, C, true>(p, X, M, Y, s, ws) : launch_g<KTAIL, C, false>(p, X, M, Y, s, ws);
 }
 
 template <bool KTAIL>
-hipError_t launch_k(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
-  return M <= kNarrowMaxM ? launch_d<KTAIL, CfgNarrow>(p, X, M, Y, s) : launch_d<KTAIL, CfgWide>(p, X, M, Y, s);
+hipError_t launch_k(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s, float* ws) {
+  return M <= kNarrowMaxM ? launch_d<KTAIL, CfgNarrow>(p, X, M, Y, s, ws)
+                          : launch_d<KTAIL, CfgWide>(p, X, M, Y, s, ws);
 }
 
 hipError_t launch_splitk_reduce(const float* part, uint16_t* Y, int64_t M, int64_t N, int S, hipStream_t s) {
@@ -598,7 +631,39 @@ hipError_t launch_splitk_reduce(const float* part, uint16_t* Y, int64_t M, int64
 }
 
 hipError_t launch_gemm(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
-  return (p->K % kTileCols) != 0 ? launch_k<true>(p, X, M, Y, s) : launch_k<false>(p, X, M, Y, s);
+  return (p->K % kTileCols) != 0 ? launch_k<true>(p, X, M, Y, s, nullptr) : launch_k<false>(p, X, M, Y, s, nullptr);
 }
+
+size_t gemm_workspace_bytes(const mq_packed* p, int64_t M) {
+  const int S = M <= kNarrowMaxM ? split_parts<CfgNarrow>(p, M, nullptr) : split_parts<CfgWide>(p, M, nullptr);
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)p->N * sizeof(float) : 0;
+}
+
+hipError_t scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {   // first use on this device (it is current): its copy of the array
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = a;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_gemm_noalloc(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
+  if (gemm_workspace_bytes(p, M) > kScratchBytes) return hipErrorInvalidValue;   // rejected by the caller first
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  float* w = static_cast<float*>(ws);
+  return (p->K % kTileCols) != 0 ? launch_k<true>(p, X, M, Y, s, w) : launch_k<false>(p, X, M, Y, s, w);
+}
+
+size_t gemm_scratch_capacity() { return kScratchBytes; }
 
 }  // namespace mq

@@ -111,6 +111,14 @@ hipError_t launch_gemv(const mq_packed* p, const uint16_t* X, int64_t M, uint16_
 // Prefill kernel (gemm.hip): any M >= 1.
 hipError_t launch_gemm(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
 
+// mq_linear's GEMM path with the split-K partials in the library's static
+// scratch array instead of a stream-ordered allocation (gemm.hip): no
+// allocation at all. gemm_workspace_bytes: the partials' size for (p, M);
+// gemm_scratch_capacity: the array's size.
+hipError_t launch_gemm_noalloc(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
+size_t gemm_workspace_bytes(const mq_packed* p, int64_t M);
+size_t gemm_scratch_capacity();
+
 // Separate residual kernel (residual.hip): Y <- fp16(Y + X R^T) from the
 // canonical CSR, for the unfused comparison.
 hipError_t launch_residual(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);

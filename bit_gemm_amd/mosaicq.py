@@ -21,7 +21,7 @@ STATUS = {
 KERNEL_AUTO, KERNEL_GEMV, KERNEL_GEMM = 0, 1, 2
 GEMV_MAX_M = 64
 
-EXPORTED = ("mq_pack", "mq_linear", "mq_linear_with", "mq_residual_add", "mq_packed_info",
+EXPORTED = ("mq_pack", "mq_linear", "mq_linear_with", "mq_linear_noalloc", "mq_residual_add", "mq_packed_info",
             "mq_export_canonical", "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks",
             "mq_smooth_weights", "mq_smooth_activations", "mq_quantize_activations", "mq_linear_a4",
             "mq_stream_read", "mq_free", "mq_status_string")
@@ -44,6 +44,8 @@ def _load():
     lib.mq_linear.restype = ctypes.c_int
     lib.mq_linear_with.argtypes = [vp, i64, vp, vp, vp, i32]
     lib.mq_linear_with.restype = ctypes.c_int
+    lib.mq_linear_noalloc.argtypes = [vp, i64, vp, vp, vp]
+    lib.mq_linear_noalloc.restype = ctypes.c_int
     lib.mq_residual_add.argtypes = [vp, i64, vp, vp, vp]
     lib.mq_residual_add.restype = ctypes.c_int
     lib.mq_packed_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i32),
@@ -279,6 +281,20 @@ def mq_linear_with(X, packed: Packed, kernel: int = KERNEL_AUTO, Y=None, stream=
 
 def mq_linear(X, packed: Packed, Y=None, stream=None):
     return mq_linear_with(X, packed, KERNEL_AUTO, Y, stream)
+
+
+def mq_linear_noalloc(X, packed: Packed, Y, stream=None):
+    """mq_linear without any device allocation (see mq_linear_noalloc in
+    include/mosaicq.h): Y must be given. Enqueued on `stream` (no sync)."""
+    xp = _dev_fp16(X, "X")
+    if X.dim() != 2 or X.shape[1] != packed.K:
+        raise ValueError(f"X must be [M, {packed.K}]")
+    M = X.shape[0]
+    yp = _dev_fp16(Y, "Y")
+    if tuple(Y.shape) != (M, packed.N):
+        raise ValueError(f"Y must be [{M}, {packed.N}]")
+    _check(lib.mq_linear_noalloc(xp, M, packed.handle, yp, _stream_handle(stream)), "mq_linear_noalloc")
+    return Y
 
 
 def mq_residual_add(X, packed: Packed, Y, stream=None):

@@ -96,6 +96,25 @@ mq_status mq_pack(const void* W_dev_fp16, int64_t N, int64_t K, int32_t group_si
 mq_status mq_linear(const void* X_dev_fp16, int64_t M, const mq_packed* p,
                     void* Y_dev_fp16, void* hip_stream);
 
+/*
+ * mq_linear_noalloc -- mq_linear for callers that cannot allocate device
+ * memory during the call (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, kernels, results (bit for
+ * bit) and errors as mq_linear, but it allocates nothing: where mq_linear
+ * splits K across workgroups (M > 16 on layers with fewer than 256 output
+ * tiles) and takes the fp32 partial sums from a stream-ordered allocation,
+ * this entry point puts them in a workspace array the library holds on each
+ * GPU for the life of the process (64 MiB, set up on the first call on that
+ * device). The split rule bounds the partials at 64 MiB, so every call fits;
+ * a call that would need more returns MQ_ERR_UNSUPPORTED. All calls on one
+ * GPU share that array: calls that overlap in time on one GPU (different
+ * streams, or graphs replayed concurrently) race and must be ordered by the
+ * caller. Every partial is written before it is read, so the array needs no
+ * clearing between calls.
+ */
+mq_status mq_linear_noalloc(const void* X_dev_fp16, int64_t M, const mq_packed* p, void* Y_dev_fp16,
+                            void* hip_stream);
+
 /* Kernel choice for mq_linear_with. */
 typedef enum { MQ_KERNEL_AUTO = 0, MQ_KERNEL_GEMV = 1, MQ_KERNEL_GEMM = 2 } mq_kernel;
 

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
-        ["mq_pack", "mq_linear", "mq_linear_with", "mq_residual_add", "mq_stream_read", "mq_packed_info", "mq_export_canonical",
+        ["mq_pack", "mq_linear", "mq_linear_with", "mq_linear_noalloc", "mq_residual_add", "mq_stream_read", "mq_packed_info", "mq_export_canonical",
          "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks", "mq_smooth_weights",
          "mq_smooth_activations", "mq_quantize_activations", "mq_linear_a4", "mq_free", "mq_status_string"])
 
@@ -107,6 +107,7 @@ def test_bad_handles_are_rejected(lib):
     assert lib.mq_linear(FAKE, 1, None, FAKE, None) == -6
     assert lib.mq_linear(FAKE, 1, bogus, FAKE, None) == -6
     assert lib.mq_linear_with(FAKE, 1, bogus, FAKE, None, mosaicq.KERNEL_GEMV) == -6
+    assert lib.mq_linear_noalloc(FAKE, 1, bogus, FAKE, None) == -6
     assert lib.mq_residual_add(FAKE, 1, bogus, FAKE, None) == -6
     n = ctypes.c_int64()
     assert lib.mq_packed_info(bogus, ctypes.byref(n), None, None, None, None) == -6
