@@ -214,7 +214,6 @@ MQ_API mq_status mq_pack_blocks(const void* W_dev_fp16, int64_t N, int64_t K, in
                 {(void**)&p->scales, (size_t)(p->Nb * mq::kRowsPerBlock * p->sstride) * sizeof(uint16_t)},
                 {(void**)&p->tile_ptr, (n_tiles + 1) * sizeof(uint32_t)},
                 {(void**)&p->entries, sz_ent},
-                {(void**)&p->wpatch, sz_ent},
                 {(void**)&p->blk, nb1 * sizeof(int32_t)},
                 {(void**)&p->bscale, nb1 * mq::kRowsPerBlock * sizeof(float)},
                 {(void**)&p->bcodes, nb1 * mq::kRowsPerBlock * (mq::kTileCols / 2)},

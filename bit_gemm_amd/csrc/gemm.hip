@@ -77,6 +77,17 @@ using CfgNarrow = Cfg<64, 8, 1, 4>;
 #endif
 constexpr int64_t kNarrowMaxM = MQ_GEMM_NARROW_MAX_M;   // token counts up to this use the narrow shape
 
+// Widened weights are stored as this type: it may alias anything, so the
+// compiler keeps the patches' atomic XORs on the same LDS words after them.
+typedef uint32_t lds_u32x4_t __attribute__((ext_vector_type(4), __may_alias__));
+
+// XOR v into the 16-bit LDS element `half` of the stage buffer (an atomic on
+// its dword: two patches may share one)
+__device__ __forceinline__ void xor_half(_Float16* Ws, uint32_t half, uint32_t v) {
+  (void)__hip_atomic_fetch_xor(reinterpret_cast<uint32_t*>(Ws) + (half >> 1), v << (16 * (half & 1u)),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // v_perm_b32 selectors: the low / high fp16 of a dword in both halves
 constexpr uint32_t kSelLo = 0x05040100u, kSelHi = 0x07060302u;
 __device__ __forceinline__ half2_t splat_sel(uint32_t dword, uint32_t sel) {
@@ -239,8 +250,8 @@ __device__ __forceinline__ void write_w(const HalfRegs<RB>& H, _Float16* Ws, _Fl
       w0 += dequant_dword(H.rcode[j].x, srs, vmask, vmask4, vmagic);
       w1 += dequant_dword(H.rcode[j].y, srs, vmask, vmask4, vmagic);
     }
-    *reinterpret_cast<half8_t*>(dst) = w0;
-    *reinterpret_cast<half8_t*>(dst + 32) = w1;
+    *reinterpret_cast<lds_u32x4_t*>(dst) = __builtin_bit_cast(lds_u32x4_t, w0);
+    *reinterpret_cast<lds_u32x4_t*>(dst + 32) = __builtin_bit_cast(lds_u32x4_t, w1);
   }
   if constexpr (DR) return;
 #pragma unroll
@@ -251,7 +262,7 @@ __device__ __forceinline__ void write_w(const HalfRegs<RB>& H, _Float16* Ws, _Fl
     // both offsets are positive: the dummy slots follow the two stage buffers
     const uint32_t real = (uint32_t)(((lrb0 + j) * kRowsPerBlock + (int)ent_row(v)) * LDW) + (v & 63u);
     const uint32_t idle = (uint32_t)(dummy - Ws) + (uint32_t)lane;
-    reinterpret_cast<uint16_t*>(Ws)[idle ^ ((real ^ idle) & okm)] = (uint16_t)(v >> 16);
+    xor_half(Ws, idle ^ ((real ^ idle) & okm), v >> 16);
   }
 }
 
@@ -269,7 +280,7 @@ __device__ __forceinline__ void patch_rest(const uint32_t* __restrict__ tile_ptr
       const uint32_t v = wpatch[e];
       if ((v & kPatchValid) == 0u || ((v >> 6) & 1u) != (uint32_t)h) continue;
       const int row = (lrb0 + j) * kRowsPerBlock + (int)ent_row(v);
-      *reinterpret_cast<uint16_t*>(Ws + row * LDW + (v & 63u)) = (uint16_t)(v >> 16);
+      xor_half(Ws, (uint32_t)(row * LDW) + (v & 63u), v >> 16);
     }
   }
 }
@@ -631,10 +642,12 @@ hipError_t launch_splitk_reduce(const float* part, uint16_t* Y, int64_t M, int64
 }
 
 hipError_t launch_gemm(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
+  if (M <= kGemmMidMaxM) return launch_gemm_mid(p, X, M, Y, s);
   return (p->K % kTileCols) != 0 ? launch_k<true>(p, X, M, Y, s, nullptr) : launch_k<false>(p, X, M, Y, s, nullptr);
 }
 
 size_t gemm_workspace_bytes(const mq_packed* p, int64_t M) {
+  if (M <= kGemmMidMaxM) return 0;   // the mid-size kernel splits K inside its workgroups
   const int S = M <= kNarrowMaxM ? split_parts<CfgNarrow>(p, M, nullptr) : split_parts<CfgWide>(p, M, nullptr);
   return S > 1 ? (size_t)S * (size_t)M * (size_t)p->N * sizeof(float) : 0;
 }
@@ -656,6 +669,7 @@ hipError_t scratch_address(void** ptr) {
 }
 
 hipError_t launch_gemm_noalloc(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
+  if (M <= kGemmMidMaxM) return launch_gemm_mid(p, X, M, Y, s);   // no workspace
   if (gemm_workspace_bytes(p, M) > kScratchBytes) return hipErrorInvalidValue;   // rejected by the caller first
   void* ws = nullptr;
   const hipError_t e = scratch_address(&ws);

@@ -10,13 +10,12 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// D = (a & m) | o in one VALU op; m and o must already sit in VGPRs (a VOP3
-// instruction on this target takes neither two SGPRs nor a literal).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(m), "v"(o));
-  return d;
-}
+// D = (a & m) | o, one v_and_or_b32 when m and o already sit in VGPRs (a
+// VOP3 instruction on this target takes at most one scalar operand). Plain C
+// rather than inline asm: the compiler's hazard checks do not see into an asm
+// block, and a VGPR written by one while an MFMA still reads it as its
+// accumulator input would corrupt that MFMA.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) { return (a & m) | o; }
 
 // The 8 codes of one dword as exact fp16 q = u - 8 (no scale). Pairs (0,1)
 // and (4,5) sit in nibbles 0/4 of the dword and of the dword shifted right

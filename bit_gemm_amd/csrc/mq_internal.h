@@ -59,7 +59,9 @@ struct mq_packed {
   float* rscale;        // [N]
   uint32_t* tile_ptr;   // [Nb*Kt + 1]
   uint32_t* entries;    // [nstream + kEntryPad]: residual stream, row blocks padded to 32 entries
-  uint32_t* wpatch;     // [nstream + kEntryPad]: the same entries carrying the patched weight fp16(s q + sr qr)
+  uint32_t* wpatch;     // [nstream + kEntryPad]: the same entries as patches of the GEMM kernels' widened
+                        // weights: bits 0-6 column mod 128, 11 valid, 12-15 row mod 16, 16-31
+                        // fp16(s q + fp16(sr qr)) XOR fp16(s q); element-wise handles only
   int64_t nstream;      // entries in the stream incl. the per-row-block zero padding
   int64_t stream_cap;   // allocated stream length (excluding the trailing zero pad)
   size_t bytes;
@@ -108,8 +110,13 @@ hipError_t export_codes(const mq_packed* p, uint8_t* codes, hipStream_t stream);
 // Decode kernel (gemv.hip): M <= 64.
 hipError_t launch_gemv(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
 
-// Prefill kernel (gemm.hip): any M >= 1.
+// Prefill kernel (gemm.hip): any M >= 1 (up to 64 tokens it runs the
+// mid-size kernel below).
 hipError_t launch_gemm(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
+
+// Mid-size batch kernel (gemm_mid.hip): M <= 64, no workspace.
+hipError_t launch_gemm_mid(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
+constexpr int64_t kGemmMidMaxM = 64;
 
 // mq_linear's GEMM path with the split-K partials in the library's static
 // scratch array instead of a stream-ordered allocation (gemm.hip): no

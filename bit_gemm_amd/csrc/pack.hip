@@ -397,15 +397,19 @@ __global__ __launch_bounds__(kWave) void k_row_emit(const uint16_t* __restrict__
         const _Float16 dh = (_Float16)dres;
         entries[ps] = ((uint32_t)__builtin_bit_cast(uint16_t, dh) << 16) | ((uint32_t)r << 12) |
                       ((uint32_t)j & (kColWindow - 1));
-        // Patched weight for kernels that overwrite the dequantized base
-        // weight in place: fp16(s q + fp16(sr qr)), one fused multiply-add
-        // and one rounding. Column c of the lane's 32 sits in dword lane / 16
-        // of lane r + 16 (c / 8) of the tile, at nibble nib_pos(c % 8).
+        // Patch for the GEMM kernels, which widen the base weight to
+        // fp16(s q) (the exact product, rounded once, as their packed
+        // multiply forms it): the patched weight fp16(s q + fp16(sr qr)) (one
+        // fused multiply-add, one rounding) XOR fp16(s q), so that one XOR
+        // turns the widened weight into the patched one. Column c of the
+        // lane's 32 sits in dword lane / 16 of lane r + 16 (c / 8) of the
+        // tile, at nibble nib_pos(c % 8).
         const uint32_t dw = tw[(r + 16 * (c >> 3)) * 4 + (lane >> 4)];
         const int q = (int)((dw >> (4 * nib_pos(c & 7))) & 0xFu) - 8;
         const _Float16 wv = (_Float16)fmaf(sbase, (float)q, (float)dh);
-        wpatch[ps] = ((uint32_t)__builtin_bit_cast(uint16_t, wv) << 16) | ((uint32_t)r << 12) | kPatchValid |
-                     ((uint32_t)j & (kTileCols - 1));
+        const _Float16 wb = (_Float16)(sbase * (float)q);
+        wpatch[ps] = ((uint32_t)(__builtin_bit_cast(uint16_t, wv) ^ __builtin_bit_cast(uint16_t, wb)) << 16) |
+                     ((uint32_t)r << 12) | kPatchValid | ((uint32_t)j & (kTileCols - 1));
         ++pc;
         ++ps;
       }

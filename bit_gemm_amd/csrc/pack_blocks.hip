@@ -261,8 +261,8 @@ __global__ __launch_bounds__(kWave) void k_block_emit(const uint16_t* __restrict
                                                       const uint32_t* __restrict__ row_cnt,
                                                       const uint32_t* __restrict__ tile_ptr,
                                                       const uint8_t* __restrict__ tiles,
-                                                      uint32_t* __restrict__ entries, uint32_t* __restrict__ wpatch,
-                                                      int64_t stream_cap, SelState* flags) {
+                                                      uint32_t* __restrict__ entries, int64_t stream_cap,
+                                                      SelState* flags) {
   const int n = blockIdx.x, b = blk[n], rb = b / Kt, kt = b - (b / Kt) * Kt;
   const int lane = threadIdx.x, r = lane & 15, kq = lane >> 4;
   BlockLane L;
@@ -286,8 +286,6 @@ __global__ __launch_bounds__(kWave) void k_block_emit(const uint16_t* __restrict
   row_lanes(nz, lane, &ex, &tot);
   if (!L.t.valid || nz == 0) return;
   uint32_t ps = tile_ptr[b] + (incl - rc) + ex;
-  const float sbase = (float)__builtin_bit_cast(_Float16, scales[(int64_t)L.t.row * sstride + L.t.c0 / G]);
-  const uint32_t* tw = reinterpret_cast<const uint32_t*>(tiles) + (int64_t)b * (kWave * 4);
   for (int c = 0; c < 32; ++c) {
     if (qr[c] == 0) continue;
     if ((int64_t)ps >= stream_cap) {   // counts disagree: never write out of bounds
@@ -299,11 +297,6 @@ __global__ __launch_bounds__(kWave) void k_block_emit(const uint16_t* __restrict
     const _Float16 dh = (_Float16)ldexpf((float)((int64_t)L.sm * qr[c]), L.sQ - 24);
     entries[ps] = ((uint32_t)__builtin_bit_cast(uint16_t, dh) << 16) | ((uint32_t)r << 12) |
                   ((uint32_t)j & (kColWindow - 1));
-    const uint32_t dw = tw[(r + 16 * (c >> 3)) * 4 + kq];
-    const int q = (int)((dw >> (4 * nib_pos(c & 7))) & 0xFu) - 8;
-    const _Float16 wv = (_Float16)fmaf(sbase, (float)q, (float)dh);
-    wpatch[ps] = ((uint32_t)__builtin_bit_cast(uint16_t, wv) << 16) | ((uint32_t)r << 12) | kPatchValid |
-                 ((uint32_t)j & (kTileCols - 1));
     ++ps;
   }
 }
@@ -334,7 +327,6 @@ hipError_t pack_blocks_on_device(const uint16_t* W, const float* h, mq_packed* p
   MQ_TRY(hipMemsetAsync(p->scales, 0, (size_t)Nb * kRowsPerBlock * p->sstride * sizeof(uint16_t), stream));
   MQ_TRY(hipMemsetAsync(p->tile_ptr, 0, (size_t)(ntiles + 1) * sizeof(uint32_t), stream));
   MQ_TRY(hipMemsetAsync(p->entries, 0, (size_t)(p->stream_cap + kEntryPad) * sizeof(uint32_t), stream));
-  MQ_TRY(hipMemsetAsync(p->wpatch, 0, (size_t)(p->stream_cap + kEntryPad) * sizeof(uint32_t), stream));
   MQ_TRY(launch_pack_base(W, p, st, stream));
   // the all-zero block slot nblk: block 0's column tile, scales 0, codes 8 (q = 0)
   MQ_TRY(hipMemsetAsync(p->blk + nsel, 0, sizeof(int32_t), stream));
@@ -372,7 +364,7 @@ hipError_t pack_blocks_on_device(const uint16_t* W, const float* h, mq_packed* p
     MQ_TRY(launch_scan_tiles(tcnt, ntiles, p->tile_ptr, stream));
     k_block_emit<<<dim3((unsigned)nsel), dim3(kWave), 0, stream>>>(W, p->scales, N, K, G, Kt, p->sstride, p->blk,
                                                                    rcnt, p->tile_ptr, p->tiles, p->entries,
-                                                                   p->wpatch, p->stream_cap, st);
+                                                                   p->stream_cap, st);
     MQ_TRY(hipGetLastError());
   }
   SelState fin;
