@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-extra", action="store_true",
                     help="skip the transformer-block, residual-sweep, block-residual, migration and W4A4 legs")
-    ap.add_argument("--only", choices=["decode", "prefill", "copy", "stream", "blocks", "migration", "w4a4"],
+    ap.add_argument("--only", choices=["decode", "prefill", "copy", "stream", "mid", "blocks", "migration", "w4a4"],
                     default=None,
                     help="run one leg only (profiling runs); 'copy' runs the plain device copy that "
                          "calibrates the HBM byte counters; 'stream' times a plain streaming read of a "
@@ -132,6 +132,7 @@ def replay_spread(torch, fn, warmup, steps, reps=9):
 
 DECODE_SOURCES = ("gemv.hip", "kernel_common.h", "mq_internal.h")
 GEMM_SOURCES = ("gemm.hip", "kernel_common.h", "mq_internal.h")
+MID_SOURCES = ("gemm_mid.hip", "kernel_common.h", "mq_internal.h")
 
 
 def source_digest(files=DECODE_SOURCES):
@@ -448,6 +449,38 @@ def bench_sweep(args, mq, synth, torch):
         out[mode] = per
         del W
     return {"workload": "sweep-14336x4096", "N": 14336, "K": 4096, "group": 128, "by_placement": out}
+
+
+def bench_mid(args, mq, synth, torch):
+    """Mid-size batches on the 14336x4096 sweep layer (columns placement):
+    16, 32, 48 and 64 tokens through mq_linear (the mid-size kernel), at
+    rho = 0 and 0.005, rotated copies, graph replay. Bytes: the packed layer
+    as stored plus X and Y; FLOPs: 2 M N K."""
+    layer = synth.sweep_layer("columns", 0.0)
+    W = torch.from_numpy(layer.W()).cuda()
+    Ms = (16, 32, 48, 64)
+    Xs = {M: torch.from_numpy(layer.X(M)).cuda() for M in Ms}
+    Ys = {M: torch.empty((M, layer.N), dtype=torch.float16, device="cuda") for M in Ms}
+    out = {}
+    for rho in (0.0, 0.005):
+        p = mq.mq_pack(W, layer.group, rho)
+        ncopy = max(2, math.ceil(2 * MALL_BYTES / p.device_bytes))
+        copies = [p] + [mq.mq_pack(W, layer.group, rho) for _ in range(ncopy - 1)]
+        per = {}
+        for M in Ms:
+            def one(i, M=M):
+                mq.mq_linear(Xs[M], copies[i % ncopy], Ys[M])
+            med, p10, p90 = replay_spread(torch, one, max(2, args.warmup // 4), max(20, args.steps // 2), reps=5)
+            nbytes = p.canonical_bytes() + 2 * M * layer.K + 2 * M * layer.N
+            per[str(M)] = {"us": round(med * 1e3, 2), "p10_us": round(p10 * 1e3, 2), "p90_us": round(p90 * 1e3, 2),
+                           "GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
+                           "TFLOPs": round(2.0 * M * layer.N * layer.K / (med * 1e-3) / 1e12, 1)}
+        for c in copies:
+            c.free()
+        out[str(rho)] = {"nnz": p.nnz, "per_M": per}
+    del W
+    return {"workload": "sweep-14336x4096 (columns)", "N": layer.N, "K": layer.K, "group": layer.group,
+            "kernel": "k_gemm_mid", "by_rho": out}
 
 
 def bench_blocks(args, mq, synth, torch):
@@ -769,6 +802,9 @@ def main():
     if args.only == "prefill":
         print(json.dumps({"prefill": bench_prefill(args, mq, synth, torch)}), flush=True)
         return
+    if args.only == "mid":
+        print(json.dumps({"mid_batch": bench_mid(args, mq, synth, torch)}), flush=True)
+        return
     if args.only == "blocks":
         print(json.dumps({"block_residual": bench_blocks(args, mq, synth, torch)}), flush=True)
         return
@@ -820,7 +856,7 @@ def main():
         if not args.skip_prefill:
             legs.append(("prefill", bench_prefill))
         if not args.skip_extra:
-            legs += [("block_4096h_m16", bench_block), ("residual_sweep", bench_sweep),
+            legs += [("mid_batch", bench_mid), ("block_4096h_m16", bench_block), ("residual_sweep", bench_sweep),
                      ("block_residual", bench_blocks), ("migration", bench_migration), ("w4a4", bench_w4a4)]
     progress("decode")
     for name, fn in legs:

@@ -157,7 +157,7 @@ static mq_status linear_impl(const void* X, int64_t M, const mq_packed* p, void*
   if (kernel < MQ_KERNEL_AUTO || kernel > MQ_KERNEL_GEMM) return MQ_ERR_INVALID_ARG;
   bool gemv;
   if (kernel == MQ_KERNEL_AUTO)
-    gemv = M <= mq::kAutoGemvMaxM;
+    gemv = mq::auto_gemv(p, M);
   else if (kernel == MQ_KERNEL_GEMV) {
     if (M > mq::kGemvMaxM) return MQ_ERR_UNSUPPORTED;
     gemv = true;
@@ -328,7 +328,7 @@ MQ_API mq_status mq_linear_noalloc(const void* X_dev_fp16, int64_t M, const mq_p
   const hipStream_t s = static_cast<hipStream_t>(hip_stream);
   const uint16_t* X = static_cast<const uint16_t*>(X_dev_fp16);
   uint16_t* Y = static_cast<uint16_t*>(Y_dev_fp16);
-  if (M <= mq::kAutoGemvMaxM) return from_hip(mq::launch_gemv(p, X, M, Y, s));   // no workspace on this path
+  if (mq::auto_gemv(p, M)) return from_hip(mq::launch_gemv(p, X, M, Y, s));   // no workspace on this path
   if (mq::gemm_workspace_bytes(p, M) > mq::gemm_scratch_capacity()) return MQ_ERR_UNSUPPORTED;
   return from_hip(mq::launch_gemm_noalloc(p, X, M, Y, s));
 }

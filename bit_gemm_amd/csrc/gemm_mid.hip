@@ -9,12 +9,12 @@
 //     tokens of its slice; the waves split K (wave w takes code tiles w,
 //     w + 8, ...), so the code tiles of a workgroup are read once, by one
 //     wave each;
-//   * a wave loads its code tiles straight into registers and widens them
-//     there to fp16(s q): the tile layout is the A operand of the 16x16x32
-//     fp16 MFMA as stored. X comes in one tile ahead of its use, with loads
-//     in which every 4 adjacent lanes read 64 contiguous bytes of one token
-//     row, and passes through a small per-wave LDS slot into the B-operand
-//     layout (tokens as columns). Loading the B layout directly would have
+//   * a wave loads its code tiles straight into registers, a tile ahead of
+//     their use, and widens them there to fp16(s q): the tile layout is the
+//     A operand of the 16x16x32 fp16 MFMA as stored. X comes in with the
+//     code tiles, with loads in which every 4 adjacent lanes read 64
+//     contiguous bytes of one token row, and passes through a small per-wave
+//     LDS slot into the B-operand layout (tokens as columns). Loading the B layout directly would have
 //     each 4 adjacent lanes read 4 different token rows, which the L2-to-CU
 //     path serves at well under half the rate, and every workgroup reads
 //     all of X;
@@ -40,6 +40,7 @@ constexpr int kPlaneStrideM = 40;   // patch plane: halves per lane (80 B: 4 k-s
                                     // on distinct banks)
 constexpr int kBufferFlagsM = 0x00020000;   // buffer descriptor word 3: 32-bit data format, raw addressing
 constexpr int kXSlotBytes = 4096;           // per wave: one token block's X for one code tile (16 x 128 fp16)
+constexpr int kRingM = 2;   // register sets in a wave's load ring (deeper rings measured slower at every shape)
 
 enum { kPlainM = 0, kElemM = 1, kBlocksM = 2 };
 
@@ -62,31 +63,60 @@ struct DenseMid {
   const float* scale;
 };
 
-// Segment bounds (kElemM) or residual slot (kBlocksM) of one code tile for
-// the workgroup's row blocks: wave-uniform scalars, loaded a tile ahead of
-// the vector loads that use them.
+// Segment bounds (kElemM) or residual slot (kBlocksM) of the wave's code
+// tiles, for the workgroup's row blocks: lane l holds those of the wave's
+// tile l (wave + 8 l; a wave has at most 64 tiles as K <= 65536), loaded with
+// one vector load per row block at the start. A step takes its tile's values
+// out with readlane, so the loop issues no scalar loads: those share a
+// completion counter with the LDS operations and return out of order, so
+// every LDS wait would also wait for the scalar load just issued.
+template <int R>
+struct MidTab {
+  uint32_t a[R], b[R];
+};
+
+template <int MODE, int R>
+__device__ __forceinline__ void mid_table(MidTab<R>& tab, const uint32_t* __restrict__ tile_ptr,
+                                          const DenseMid& dr, int Kt, int Nb, int rb0, int wave, int lane) {
+  const int kl = min(wave + kWavesM * lane, Kt - 1);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int64_t t = (int64_t)min(rb0 + j, Nb - 1) * Kt + kl;
+    if constexpr (MODE == kBlocksM) {
+      tab.a[j] = (uint32_t)dr.slot[t];
+      tab.b[j] = 0u;
+    } else if constexpr (MODE == kElemM) {
+      tab.a[j] = tile_ptr[t];
+      tab.b[j] = tile_ptr[t + 1];
+    } else {
+      tab.a[j] = tab.b[j] = 0u;
+    }
+  }
+}
+
+// The values of one tile (kt, the wave's tile idx): wave-uniform. Past the
+// last tile the segment is empty and the slot that of the last tile.
 template <int R>
 struct MidPtrs {
   uint32_t p0[R], cnt[R];
 };
 
 template <int MODE, int R>
-__device__ __forceinline__ void mid_ptrs(MidPtrs<R>& P, const uint32_t* __restrict__ tile_ptr, const DenseMid& dr,
-                                         int Kt, int Nb, int rb0, int kt) {
+__device__ __forceinline__ void mid_ptrs(MidPtrs<R>& P, const MidTab<R>& tab, int Kt, int Nb, int rb0, int kt,
+                                         int idx) {
+  const int l = min(idx, 63);
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    const bool ok = rb0 + j < Nb && kt < Kt;
-    const int64_t t = (int64_t)min(rb0 + j, Nb - 1) * Kt + min(kt, Kt - 1);
-    if constexpr (MODE == kBlocksM) {
-      P.p0[j] = (uint32_t)dr.slot[t];
-      P.cnt[j] = 0u;
-    } else if constexpr (MODE == kElemM) {
-      const uint32_t p0 = tile_ptr[t], p1 = tile_ptr[t + 1];
-      P.p0[j] = p0;
-      P.cnt[j] = ok ? p1 - p0 : 0u;
+    if constexpr (MODE == kPlainM) {
+      P.p0[j] = P.cnt[j] = 0u;
     } else {
-      P.p0[j] = 0u;
-      P.cnt[j] = 0u;
+      P.p0[j] = (uint32_t)__builtin_amdgcn_readlane((int)tab.a[j], l);
+      if constexpr (MODE == kElemM) {
+        const uint32_t p1 = (uint32_t)__builtin_amdgcn_readlane((int)tab.b[j], l);
+        P.cnt[j] = rb0 + j < Nb && kt < Kt ? p1 - P.p0[j] : 0u;
+      } else {
+        P.cnt[j] = 0u;
+      }
     }
   }
 }
@@ -99,7 +129,7 @@ struct MidTile {
   uint4 code[R];
   uint32_t sraw[R][GSH == 2 ? 2 : 1];   // the aligned scale word(s) of the lane's row holding the tile's scale(s)
   uint32_t ent[R];                      // kElemM: entry p0 + lane; kBlocksM: fp32 residual row scale
-  uint32_t cnt[R];
+  uint32_t p0[R], cnt[R];               // kElemM: the tile's segment of the patch stream
   uint4 rcode[R];                       // kBlocksM
   u32x4_t x[NTB][4];                    // X as loaded: token block tb, load u (see mid_load)
 };
@@ -120,12 +150,11 @@ __device__ __forceinline__ uint32_t x_read_pos(int lane, int t) {
   return (uint32_t)(64 * (n >> 2) + 16 * (n & 3) + 4 * (t ^ (n >> 2)) + (g ^ (n & 3)));
 }
 
-template <int GSH, int MODE, int NTB, int R, bool KTAIL>
-__device__ __forceinline__ void mid_load(MidTile<GSH, MODE, NTB, R>& T, const MidPtrs<R>& P,
-                                         const uint4* __restrict__ tiles, const uint16_t* __restrict__ scales,
-                                         int64_t sstride, const uint32_t* __restrict__ wpatch, const DenseMid& dr,
-                                         __amdgpu_buffer_rsrc_t xrs, const uint32_t (&xoff)[4], int K, int Kt,
-                                         int Nb, int rb0, int kt, int lane) {
+template <int GSH, int MODE, int NTB, int R>
+__device__ __forceinline__ void mid_load_base(MidTile<GSH, MODE, NTB, R>& T, const uint4* __restrict__ tiles,
+                                              const uint16_t* __restrict__ scales, int64_t sstride,
+                                              __amdgpu_buffer_rsrc_t xrs, const uint32_t (&xoff)[4], int K, int Kt,
+                                              int Nb, int rb0, int kt, int lane) {
   const int r = lane & 15;
   const int ktc = min(kt, Kt - 1);
 #pragma unroll
@@ -142,18 +171,13 @@ __device__ __forceinline__ void mid_load(MidTile<GSH, MODE, NTB, R>& T, const Mi
       T.sraw[j][0] = v.x;
       T.sraw[j][1] = v.y;
     }
-    if constexpr (MODE == kElemM) {
-      T.ent[j] = wpatch[P.p0[j] + lane];   // 1024 zero entries follow the stream: always readable
-      T.cnt[j] = P.cnt[j];
-    } else if constexpr (MODE == kBlocksM) {
-      T.rcode[j] = dr.tiles[(int64_t)P.p0[j] * 64 + lane];
-      T.ent[j] = __builtin_bit_cast(uint32_t, dr.scale[(int64_t)P.p0[j] * kRowsPerBlock + r]);
-    }
   }
   // The whole X offset (token row and column) goes into the per-lane offset,
-  // which the buffer's range check covers (reads past the workgroup's last
-  // row return zero).
-  const uint32_t coff = (uint32_t)ktc * (kTileCols * 2);
+  // which the buffer's range check covers: reads past the workgroup's last
+  // row return zero, and so does all of X for a tile past the last (the
+  // offset 2^30 is past any X range, and the sum cannot wrap), so such a tile
+  // adds exactly zero.
+  const uint32_t coff = kt < Kt ? (uint32_t)ktc * (kTileCols * 2) : (1u << 30);
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -161,6 +185,25 @@ __device__ __forceinline__ void mid_load(MidTile<GSH, MODE, NTB, R>& T, const Mi
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff[u] + coff + (uint32_t)tb * 32u * K, 0, 0);
       T.x[tb][u] = u32x4_t{v[0], v[1], v[2], v[3]};
     }
+}
+
+// The tile's residual: its patch entries (kElemM) or residual code tile and
+// row scale (kBlocksM).
+template <int GSH, int MODE, int NTB, int R>
+__device__ __forceinline__ void mid_load_res(MidTile<GSH, MODE, NTB, R>& T, const MidPtrs<R>& P,
+                                             const uint32_t* __restrict__ wpatch, const DenseMid& dr, int lane) {
+  const int r = lane & 15;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if constexpr (MODE == kElemM) {
+      T.ent[j] = wpatch[P.p0[j] + lane];   // 1024 zero entries follow the stream: always readable
+      T.p0[j] = P.p0[j];
+      T.cnt[j] = P.cnt[j];
+    } else if constexpr (MODE == kBlocksM) {
+      T.rcode[j] = dr.tiles[(int64_t)P.p0[j] * 64 + lane];
+      T.ent[j] = __builtin_bit_cast(uint32_t, dr.scale[(int64_t)P.p0[j] * kRowsPerBlock + r]);
+    }
+  }
 }
 
 // Element-wise residual of one row block's tile, applied to the widened A
@@ -196,7 +239,7 @@ __device__ __forceinline__ void mid_patch(half8_t (&a)[4], uint32_t v, uint32_t 
 
 template <int GSH, int MODE, int NTB, int R, bool KTAIL>
 __device__ __forceinline__ void mid_compute(float4_t (&acc)[R][NTB], const MidTile<GSH, MODE, NTB, R>& T,
-                                            const MidPtrs<R>& P, const uint32_t* __restrict__ wpatch, int kt,
+                                            const uint32_t* __restrict__ wpatch, int kt,
                                             uint16_t* plane, plane_u32x4_t* xslot, const uint32_t (&xpos)[4],
                                             int K, int Kt, int lane, uint32_t vmask, uint32_t vmask4,
                                             uint32_t vmagic) {
@@ -252,7 +295,7 @@ __device__ __forceinline__ void mid_compute(float4_t (&acc)[R][NTB], const MidTi
       a[2] += dequant_dword(T.rcode[j].z, srs, vmask, vmask4, vmagic);
       a[3] += dequant_dword(T.rcode[j].w, srs, vmask, vmask4, vmagic);
     } else if constexpr (MODE == kElemM) {
-      if (T.cnt[j] != 0u) mid_patch(a, T.ent[j], T.cnt[j], P.p0[j], wpatch, plane, lane);
+      if (T.cnt[j] != 0u) mid_patch(a, T.ent[j], T.cnt[j], T.p0[j], wpatch, plane, lane);
     }
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb)
@@ -311,31 +354,37 @@ __global__ __launch_bounds__(kThreadsM, 1) void k_gemm_mid(const uint4* __restri
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) acc[j][tb] = float4_t{z, z, z, z};
 
-  // tiles wave, wave + 8, ...: two register sets in turn, each loaded a tile
-  // ahead of its use; segment bounds two tiles ahead
-  MidTile<GSH, MODE, NTB, R> TA, TB;
-  MidPtrs<R> PA, PB, PC;
-  const int kt0 = wave;
-  mid_ptrs<MODE, R>(PA, tile_ptr, dr, Kt, Nb, rb0, kt0);
-  mid_ptrs<MODE, R>(PB, tile_ptr, dr, Kt, Nb, rb0, kt0 + kWavesM);
-  mid_load<GSH, MODE, NTB, R, KTAIL>(TA, PA, tiles, scales, sstride, wpatch, dr, xrs, xoff, K, Kt, Nb, rb0,
-                                     kt0, lane);
-  for (int kt = kt0; kt < Kt; kt += 2 * kWavesM) {
-    mid_ptrs<MODE, R>(PC, tile_ptr, dr, Kt, Nb, rb0, kt + 2 * kWavesM);
-    mid_load<GSH, MODE, NTB, R, KTAIL>(TB, PB, tiles, scales, sstride, wpatch, dr, xrs, xoff, K, Kt, Nb, rb0,
-                                       kt + kWavesM, lane);
-    mid_compute<GSH, MODE, NTB, R, KTAIL>(acc, TA, PA, wpatch, kt, plane, xslot, xpos, K, Kt, lane, vmask, vmask4,
-                                          vmagic);
-    if (kt + kWavesM >= Kt) break;   // the same in every lane of the wave
-    mid_ptrs<MODE, R>(PA, tile_ptr, dr, Kt, Nb, rb0, kt + 3 * kWavesM);
-    mid_load<GSH, MODE, NTB, R, KTAIL>(TA, PC, tiles, scales, sstride, wpatch, dr, xrs, xoff, K, Kt, Nb, rb0,
-                                       kt + 2 * kWavesM, lane);
-    mid_compute<GSH, MODE, NTB, R, KTAIL>(acc, TB, PB, wpatch, kt + kWavesM, plane, xslot, xpos, K, Kt, lane,
-                                          vmask, vmask4, vmagic);
-    // rotate the segment bounds: PA <- tile kt + 2 * 8 (PC), PB <- tile kt + 3 * 8 (PA)
-    const MidPtrs<R> t = PA;
-    PA = PC;
-    PB = t;
+  // Tiles wave, wave + 8, ...: a ring of kRingM register sets, each loaded kRingM - 1
+  // tiles ahead of its use, in whole turns of the ring with no branch inside
+  // (one costs registers): the steps past the wave's last tile compute on
+  // zero X. The segment table is requested first; the first tiles' residual
+  // loads, which need it, follow their code tiles.
+  MidTab<R> tab;
+  mid_table<MODE, R>(tab, tile_ptr, dr, Kt, Nb, rb0, wave, lane);
+  MidTile<GSH, MODE, NTB, R> T[kRingM];
+#pragma unroll
+  for (int u = 0; u + 1 < kRingM; ++u)
+    mid_load_base<GSH, MODE, NTB, R>(T[u], tiles, scales, sstride, xrs, xoff, K, Kt, Nb, rb0, wave + kWavesM * u,
+                                     lane);
+#pragma unroll
+  for (int u = 0; u + 1 < kRingM; ++u) {
+    MidPtrs<R> P;
+    mid_ptrs<MODE, R>(P, tab, Kt, Nb, rb0, wave + kWavesM * u, u);
+    mid_load_res<GSH, MODE, NTB, R>(T[u], P, wpatch, dr, lane);
+  }
+  const int nt = (Kt - wave + kWavesM - 1) / kWavesM;   // tiles of this wave
+  for (int i = 0; i < nt; i += kRingM) {
+#pragma unroll
+    for (int u = 0; u < kRingM; ++u) {
+      const int kt = wave + kWavesM * (i + u), kn = kt + kWavesM * (kRingM - 1);
+      MidPtrs<R> P;
+      mid_ptrs<MODE, R>(P, tab, Kt, Nb, rb0, kn, i + u + kRingM - 1);
+      mid_load_base<GSH, MODE, NTB, R>(T[(u + kRingM - 1) % kRingM], tiles, scales, sstride, xrs, xoff, K, Kt, Nb, rb0, kn,
+                                       lane);
+      mid_load_res<GSH, MODE, NTB, R>(T[(u + kRingM - 1) % kRingM], P, wpatch, dr, lane);
+      mid_compute<GSH, MODE, NTB, R, KTAIL>(acc, T[u], wpatch, kt, plane, xslot, xpos, K, Kt, lane, vmask, vmask4,
+                                            vmagic);
+    }
   }
 
   // The 8 partial sums of each (row block, token block) meet in LDS (the
@@ -384,11 +433,12 @@ hipError_t launch_mid(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t
 
 // Row blocks per workgroup: enough that one round of workgroups covers the
 // layer on 256 CUs (fewer row blocks per workgroup would make a second
-// round, each reading all of its X again), at most 4, and fewer where the
-// registers of a tile and the next (64 tokens of X each) would not fit.
+// round, each reading all of its X again), at most 4; with 64 tokens 2 for
+// the element-wise residual or a K tail and 3 for a block residual with
+// G = 32, where more would not fit the registers.
 template <int GSH, int MODE, int NTB, bool KTAIL>
 hipError_t launch_mid_r(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
-  constexpr int64_t rmax = NTB < 4 ? 4 : (MODE == kElemM || KTAIL) ? 2 : MODE == kBlocksM ? 3 : 4;
+  constexpr int64_t rmax = NTB < 4 ? 4 : (MODE == kElemM || KTAIL) ? 2 : MODE == kBlocksM && GSH == 2 ? 3 : 4;
   const int64_t r = std::min<int64_t>(rmax, std::max<int64_t>(1, (p->Nb + 255) / 256));
   if (r == 1) return launch_mid<GSH, MODE, NTB, 1, KTAIL>(p, X, M, Y, s);
   if (r == 2 || rmax == 2) return launch_mid<GSH, MODE, NTB, 2, KTAIL>(p, X, M, Y, s);

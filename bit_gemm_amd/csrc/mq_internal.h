@@ -146,6 +146,11 @@ hipError_t launch_gemm_a4(const mq_packed* p, const uint8_t* xq, const uint32_t*
 hipError_t stream_read(const void* src, int64_t bytes, int workgroups, uint32_t* sink, hipStream_t stream);
 
 constexpr int64_t kGemvMaxM = 64;       // the GEMV kernels accept up to 64 tokens
-constexpr int64_t kAutoGemvMaxM = 16;   // the automatic choice takes them up to 16
+
+// The automatic choice: the GEMV kernels up to 16 tokens when K <= 4096 (X
+// whole in LDS), else up to 3 (with X from global memory they lose to the
+// mid-size kernel from about 4 tokens on); the GEMM path (the mid-size kernel
+// up to 64 tokens) otherwise.
+inline bool auto_gemv(const mq_packed* p, int64_t M) { return M <= (p->K <= 4096 ? 16 : 3); }
 
 }  // namespace mq

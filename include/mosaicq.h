@@ -83,15 +83,18 @@ mq_status mq_pack(const void* W_dev_fp16, int64_t N, int64_t K, int32_t group_si
  *   Y_dev_fp16   [M, N] fp16 output (device, caller-owned, fully overwritten)
  *   hip_stream   stream to enqueue on; the call returns without synchronising
  *
- * Up to 16 tokens (decode) a GEMV-style kernel streams the 4-bit tiles from
- * HBM; above that an MFMA GEMM runs. Both are deterministic. When the GEMM's
- * output tiles are too few to fill the GPU (M times N small against K), it
- * splits K: the parts write fp32 partial sums to a workspace that the call
- * takes from the stream-ordered allocator (hipMallocAsync / hipFreeAsync on
- * hip_stream, so it also works under stream capture, where it becomes a
- * graph allocation), and a second kernel adds the parts in a fixed order.
- * The workspace holds at most 256 x 256 x 256 fp32 values (64 MiB); if it
- * cannot be allocated the call returns MQ_ERR_OUT_OF_MEMORY.
+ * Decode batches (up to 16 tokens with K <= 4096, up to 3 tokens for larger
+ * K) run a GEMV-style kernel that streams the 4-bit tiles from HBM; up to 64
+ * tokens a mid-size MFMA kernel that splits K among the waves of each
+ * workgroup; above that the MFMA GEMM. All are deterministic. When the
+ * GEMM's output tiles are too few to fill the GPU (M times N small against
+ * K), it splits K across workgroups: the parts write fp32 partial sums to a
+ * workspace that the call takes from the stream-ordered allocator
+ * (hipMallocAsync / hipFreeAsync on hip_stream, so it also works under
+ * stream capture, where it becomes a graph allocation), and a second kernel
+ * adds the parts in a fixed order. The workspace holds at most
+ * 256 x 256 x 256 fp32 values (64 MiB); if it cannot be allocated the call
+ * returns MQ_ERR_OUT_OF_MEMORY. Up to 64 tokens no workspace is used.
  */
 mq_status mq_linear(const void* X_dev_fp16, int64_t M, const mq_packed* p,
                     void* Y_dev_fp16, void* hip_stream);
@@ -101,7 +104,7 @@ mq_status mq_linear(const void* X_dev_fp16, int64_t M, const mq_packed* p,
  * memory during the call (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc). Same arguments, kernels, results (bit for
  * bit) and errors as mq_linear, but it allocates nothing: where mq_linear
- * splits K across workgroups (M > 16 on layers with fewer than 256 output
+ * splits K across workgroups (M > 64 on layers with fewer than 256 output
  * tiles) and takes the fp32 partial sums from a stream-ordered allocation,
  * this entry point puts them in a workspace array the library holds on each
  * GPU for the life of the process (64 MiB, set up on the first call on that

@@ -119,6 +119,25 @@ def test_linear_workload_layers(mq, name):
             check_linear(Y, X, Wt, f"{name} M={M} kernel={kern}")
 
 
+def test_automatic_choice_follows_the_documented_rule(mq):
+    """mq_linear picks the GEMV kernels up to 16 tokens when K <= 4096 and up
+    to 3 tokens for larger K, else the GEMM path: its output is bit-identical
+    to that kernel's, and within the oracle bound."""
+    for N, K, G, rho in ((300, 4096, 128, 0.01), (260, 8320, 64, 0.01), (40, 640, 32, 0.05)):
+        W = _layer(N, K, seed=K + 1)
+        p = mq.mq_pack(to_dev(W), G, rho)
+        Wt = oracle.dequant(oracle.pack(W, G, rho))
+        for M in (1, 3, 4, 8, 16, 17, 64, 65):
+            X = _x(M, K, seed=M + 11)
+            Xd = to_dev(X)
+            want = mq.KERNEL_GEMV if M <= (16 if K <= 4096 else 3) else mq.KERNEL_GEMM
+            print(f"[auto] N={N} K={K} M={M} expect kernel={want}", flush=True)
+            Ya = mq.mq_linear(Xd, p).cpu().numpy()
+            Yk = mq.mq_linear_with(Xd, p, want).cpu().numpy()
+            assert np.array_equal(Ya.view(np.uint16), Yk.view(np.uint16)), (N, K, M)
+            check_linear(Ya, X, Wt, f"auto N={N} K={K} M={M}")
+
+
 def test_linear_is_deterministic(mq):
     layer = synth.WORKLOADS["tiny-1024x1024"].layers[0]
     p = mq.mq_pack(to_dev(layer.W()), 128, 0.05)
