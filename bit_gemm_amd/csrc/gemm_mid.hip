@@ -42,7 +42,16 @@ constexpr int kBufferFlagsM = 0x00020000;   // buffer descriptor word 3: 32-bit 
 constexpr int kXSlotBytes = 4096;           // per wave: one token block's X for one code tile (16 x 128 fp16)
 constexpr int kRingM = 2;   // register sets in a wave's load ring (deeper rings measured slower at every shape)
 
-enum { kPlainM = 0, kElemM = 1, kBlocksM = 2 };
+// Residual of the handle: none; element-wise, either branch-free (kElemFlat1M
+// + e - 1 when no tile's segment of the patch stream exceeds 64 e entries,
+// e <= 3: each lane applies up to e entries per tile, all at once) or in
+// rounds of 64 entries in a loop (kElemM, longer segments: the loop ties up
+// enough registers that a workgroup takes at most 2 row blocks with 64
+// tokens); or blocks of 4-bit codes.
+enum { kPlainM = 0, kElemM = 1, kBlocksM = 2, kElemFlat1M = 3, kElemFlat3M = 5 };
+constexpr bool is_flat(int mode) { return mode >= kElemFlat1M && mode <= kElemFlat3M; }
+constexpr bool is_elem(int mode) { return mode == kElemM || is_flat(mode); }
+constexpr int flat_entries(int mode) { return is_flat(mode) ? mode - kElemFlat1M + 1 : 1; }
 
 // Reads of the patch plane, which is written 16 bits at a time, and its
 // clearing: the type may alias anything, so the compiler keeps them in
@@ -63,7 +72,7 @@ struct DenseMid {
   const float* scale;
 };
 
-// Segment bounds (kElemM) or residual slot (kBlocksM) of the wave's code
+// Segment bounds (element-wise) or residual slot (kBlocksM) of the wave's code
 // tiles, for the workgroup's row blocks: lane l holds those of the wave's
 // tile l (wave + 8 l; a wave has at most 64 tiles as K <= 65536), loaded with
 // one vector load per row block at the start. A step takes its tile's values
@@ -85,7 +94,7 @@ __device__ __forceinline__ void mid_table(MidTab<R>& tab, const uint32_t* __rest
     if constexpr (MODE == kBlocksM) {
       tab.a[j] = (uint32_t)dr.slot[t];
       tab.b[j] = 0u;
-    } else if constexpr (MODE == kElemM) {
+    } else if constexpr (is_elem(MODE)) {
       tab.a[j] = tile_ptr[t];
       tab.b[j] = tile_ptr[t + 1];
     } else {
@@ -111,7 +120,7 @@ __device__ __forceinline__ void mid_ptrs(MidPtrs<R>& P, const MidTab<R>& tab, in
       P.p0[j] = P.cnt[j] = 0u;
     } else {
       P.p0[j] = (uint32_t)__builtin_amdgcn_readlane((int)tab.a[j], l);
-      if constexpr (MODE == kElemM) {
+      if constexpr (is_elem(MODE)) {
         const uint32_t p1 = (uint32_t)__builtin_amdgcn_readlane((int)tab.b[j], l);
         P.cnt[j] = rb0 + j < Nb && kt < Kt ? p1 - P.p0[j] : 0u;
       } else {
@@ -128,8 +137,8 @@ template <int GSH, int MODE, int NTB, int R>
 struct MidTile {
   uint4 code[R];
   uint32_t sraw[R][GSH == 2 ? 2 : 1];   // the aligned scale word(s) of the lane's row holding the tile's scale(s)
-  uint32_t ent[R];                      // kElemM: entry p0 + lane; kBlocksM: fp32 residual row scale
-  uint32_t p0[R], cnt[R];               // kElemM: the tile's segment of the patch stream
+  uint32_t ent[R][flat_entries(MODE)];  // element-wise: entries p0 + lane + 64 e; kBlocksM: [0] fp32 row scale
+  uint32_t p0[R], cnt[R];               // element-wise: the tile's segment of the patch stream
   uint4 rcode[R];                       // kBlocksM
   u32x4_t x[NTB][4];                    // X as loaded: token block tb, load u (see mid_load)
 };
@@ -187,7 +196,7 @@ __device__ __forceinline__ void mid_load_base(MidTile<GSH, MODE, NTB, R>& T, con
     }
 }
 
-// The tile's residual: its patch entries (kElemM) or residual code tile and
+// The tile's residual: its patch entries (element-wise) or residual code tile and
 // row scale (kBlocksM).
 template <int GSH, int MODE, int NTB, int R>
 __device__ __forceinline__ void mid_load_res(MidTile<GSH, MODE, NTB, R>& T, const MidPtrs<R>& P,
@@ -195,46 +204,83 @@ __device__ __forceinline__ void mid_load_res(MidTile<GSH, MODE, NTB, R>& T, cons
   const int r = lane & 15;
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    if constexpr (MODE == kElemM) {
-      T.ent[j] = wpatch[P.p0[j] + lane];   // 1024 zero entries follow the stream: always readable
+    if constexpr (is_elem(MODE)) {
+#pragma unroll
+      for (int e = 0; e < flat_entries(MODE); ++e)   // 1024 zero entries follow the stream: always readable
+        T.ent[j][e] = wpatch[P.p0[j] + lane + 64 * e];
       T.p0[j] = P.p0[j];
       T.cnt[j] = P.cnt[j];
     } else if constexpr (MODE == kBlocksM) {
       T.rcode[j] = dr.tiles[(int64_t)P.p0[j] * 64 + lane];
-      T.ent[j] = __builtin_bit_cast(uint32_t, dr.scale[(int64_t)P.p0[j] * kRowsPerBlock + r]);
+      T.ent[j][0] = __builtin_bit_cast(uint32_t, dr.scale[(int64_t)P.p0[j] * kRowsPerBlock + r]);
     }
   }
 }
 
 // Element-wise residual of one row block's tile, applied to the widened A
-// operands. Entry bits (the patched-weight stream): 0-6 column mod 128,
-// 11 valid, 12-15 row, 16-31 fp16(s q + sr qr) XOR fp16(s q). Its plane
-// position is that of the weight in the A operands: lane r + 16 ((j % 32) /
-// 8), k-step j / 32, element j % 8. Every lane writes (lanes without an
-// entry to an unused part of their own slot), so the reads that follow see
-// every lane's write; entries past the first 64 of a segment take further
-// rounds.
+// operands, one round of up to 64 entries (entries base .. base + 63 of the
+// segment, entry base + lane in v). Entry bits (the patched-weight stream):
+// 0-6 column mod 128, 11 valid, 12-15 row, 16-31 fp16(s q + sr qr) XOR
+// fp16(s q). Its plane position is that of the weight in the A operands:
+// lane r + 16 ((j % 32) / 8), k-step j / 32, element j % 8. Every lane writes
+// (lanes without an entry to an unused part of their own slot), so the reads
+// that follow see every lane's write.
+__device__ __forceinline__ void mid_patch_round(half8_t (&a)[4], uint32_t v, uint32_t cnt, uint32_t base,
+                                                uint16_t* plane, int lane) {
+  const uint32_t c = v & 127u, row = (v >> 12) & 15u;
+  uint32_t okm = 0u - (((uint32_t)lane + base < cnt) & ((v >> 11) & 1u));
+  asm("" : "+v"(okm));
+  const uint32_t real = (row + 16u * ((c >> 3) & 3u)) * kPlaneStrideM + 8u * (c >> 5) + (c & 7u);
+  const uint32_t idle = (uint32_t)(lane * kPlaneStrideM + 32);
+  const uint32_t tgt = idle ^ ((real ^ idle) & okm);
+  plane[tgt] = (uint16_t)(v >> 16);
+  const plane_u32x4_t* src = reinterpret_cast<const plane_u32x4_t*>(plane + lane * kPlaneStrideM);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const u32x4_t p = src[ks];
+    a[ks] = __builtin_bit_cast(half8_t, __builtin_bit_cast(u32x4_t, a[ks]) ^ p);
+  }
+  plane[tgt] = 0;
+}
+
+// A segment of any length: rounds of 64 entries.
 __device__ __forceinline__ void mid_patch(half8_t (&a)[4], uint32_t v, uint32_t cnt, uint32_t e0,
                                           const uint32_t* __restrict__ wpatch, uint16_t* plane, int lane) {
   for (uint32_t base = 0;;) {
-    const uint32_t c = v & 127u, row = (v >> 12) & 15u;
-    uint32_t okm = 0u - (((uint32_t)lane + base < cnt) & ((v >> 11) & 1u));
-    asm("" : "+v"(okm));
-    const uint32_t real = (row + 16u * ((c >> 3) & 3u)) * kPlaneStrideM + 8u * (c >> 5) + (c & 7u);
-    const uint32_t idle = (uint32_t)(lane * kPlaneStrideM + 32);
-    const uint32_t tgt = idle ^ ((real ^ idle) & okm);
-    plane[tgt] = (uint16_t)(v >> 16);
-    const plane_u32x4_t* src = reinterpret_cast<const plane_u32x4_t*>(plane + lane * kPlaneStrideM);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const u32x4_t p = src[ks];
-      a[ks] = __builtin_bit_cast(half8_t, __builtin_bit_cast(u32x4_t, a[ks]) ^ p);
-    }
-    plane[tgt] = 0;
+    mid_patch_round(a, v, cnt, base, plane, lane);
     base += 64;
     if (base >= cnt) break;   // wave-uniform
     v = wpatch[e0 + base + lane];
   }
+}
+
+// A segment of up to 64 E entries, branch-free: lane l scatters entries
+// l, l + 64, ... (each to its position, or to its own unused half past the
+// end of the segment), then every lane reads its slice back once and the
+// entries are cleared. Two entries never share a position (each names one
+// weight).
+template <int E>
+__device__ __forceinline__ void mid_patch_flat(half8_t (&a)[4], const uint32_t (&v)[E], uint32_t cnt,
+                                               uint16_t* plane, int lane) {
+  const uint32_t idle = (uint32_t)(lane * kPlaneStrideM + 32);
+  uint32_t tgt[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t c = v[e] & 127u, row = (v[e] >> 12) & 15u;
+    uint32_t okm = 0u - (((uint32_t)(lane + 64 * e) < cnt) & ((v[e] >> 11) & 1u));
+    asm("" : "+v"(okm));
+    const uint32_t real = (row + 16u * ((c >> 3) & 3u)) * kPlaneStrideM + 8u * (c >> 5) + (c & 7u);
+    tgt[e] = idle ^ ((real ^ idle) & okm);
+    plane[tgt[e]] = (uint16_t)(v[e] >> 16);
+  }
+  const plane_u32x4_t* src = reinterpret_cast<const plane_u32x4_t*>(plane + lane * kPlaneStrideM);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const u32x4_t p = src[ks];
+    a[ks] = __builtin_bit_cast(half8_t, __builtin_bit_cast(u32x4_t, a[ks]) ^ p);
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) plane[tgt[e]] = 0;
 }
 
 template <int GSH, int MODE, int NTB, int R, bool KTAIL>
@@ -288,14 +334,16 @@ __device__ __forceinline__ void mid_compute(float4_t (&acc)[R][NTB], const MidTi
     a[2] = dequant_dword(T.code[j].z, s[2], vmask, vmask4, vmagic);
     a[3] = dequant_dword(T.code[j].w, s[3], vmask, vmask4, vmagic);
     if constexpr (MODE == kBlocksM) {
-      const _Float16 sr = (_Float16)__builtin_bit_cast(float, T.ent[j]);
+      const _Float16 sr = (_Float16)__builtin_bit_cast(float, T.ent[j][0]);
       const half2_t srs = {sr, sr};
       a[0] += dequant_dword(T.rcode[j].x, srs, vmask, vmask4, vmagic);
       a[1] += dequant_dword(T.rcode[j].y, srs, vmask, vmask4, vmagic);
       a[2] += dequant_dword(T.rcode[j].z, srs, vmask, vmask4, vmagic);
       a[3] += dequant_dword(T.rcode[j].w, srs, vmask, vmask4, vmagic);
+    } else if constexpr (is_flat(MODE)) {
+      mid_patch_flat<flat_entries(MODE)>(a, T.ent[j], T.cnt[j], plane, lane);
     } else if constexpr (MODE == kElemM) {
-      if (T.cnt[j] != 0u) mid_patch(a, T.ent[j], T.cnt[j], T.p0[j], wpatch, plane, lane);
+      if (T.cnt[j] != 0u) mid_patch(a, T.ent[j][0], T.cnt[j], T.p0[j], wpatch, plane, lane);
     }
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb)
@@ -321,9 +369,9 @@ __global__ __launch_bounds__(kThreadsM, 1) void k_gemm_mid(const uint4* __restri
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int rb0 = blockIdx.x * R, m0 = blockIdx.y * 16 * NTB;
   uint16_t* const plane = reinterpret_cast<uint16_t*>(lds_mid) + wave * 64 * kPlaneStrideM;
-  constexpr int xbase = MODE == kElemM ? kWavesM * 64 * kPlaneStrideM * 2 : 0;   // the X slots follow the planes
+  constexpr int xbase = is_elem(MODE) ? kWavesM * 64 * kPlaneStrideM * 2 : 0;   // the X slots follow the planes
   plane_u32x4_t* const xslot = reinterpret_cast<plane_u32x4_t*>(lds_mid + xbase + wave * kXSlotBytes);
-  if constexpr (MODE == kElemM) {
+  if constexpr (is_elem(MODE)) {
     // LDS holds whatever a previous kernel left: each lane zeroes the 32
     // halves of its slot that the patches XOR in
     plane_u32x4_t* dst = reinterpret_cast<plane_u32x4_t*>(plane + lane * kPlaneStrideM);
@@ -354,8 +402,8 @@ __global__ __launch_bounds__(kThreadsM, 1) void k_gemm_mid(const uint4* __restri
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb) acc[j][tb] = float4_t{z, z, z, z};
 
-  // Tiles wave, wave + 8, ...: a ring of kRingM register sets, each loaded kRingM - 1
-  // tiles ahead of its use, in whole turns of the ring with no branch inside
+  // Tiles wave, wave + 8, ...: a ring of kRingM register sets, each loaded
+  // kRingM - 1 tiles ahead of its use, in whole turns of the ring with no branch inside
   // (one costs registers): the steps past the wave's last tile compute on
   // zero X. The segment table is requested first; the first tiles' residual
   // loads, which need it, follow their code tiles.
@@ -379,9 +427,9 @@ __global__ __launch_bounds__(kThreadsM, 1) void k_gemm_mid(const uint4* __restri
       const int kt = wave + kWavesM * (i + u), kn = kt + kWavesM * (kRingM - 1);
       MidPtrs<R> P;
       mid_ptrs<MODE, R>(P, tab, Kt, Nb, rb0, kn, i + u + kRingM - 1);
-      mid_load_base<GSH, MODE, NTB, R>(T[(u + kRingM - 1) % kRingM], tiles, scales, sstride, xrs, xoff, K, Kt, Nb, rb0, kn,
-                                       lane);
-      mid_load_res<GSH, MODE, NTB, R>(T[(u + kRingM - 1) % kRingM], P, wpatch, dr, lane);
+      MidTile<GSH, MODE, NTB, R>& Tn = T[(u + kRingM - 1) % kRingM];
+      mid_load_base<GSH, MODE, NTB, R>(Tn, tiles, scales, sstride, xrs, xoff, K, Kt, Nb, rb0, kn, lane);
+      mid_load_res<GSH, MODE, NTB, R>(Tn, P, wpatch, dr, lane);
       mid_compute<GSH, MODE, NTB, R, KTAIL>(acc, T[u], wpatch, kt, plane, xslot, xpos, K, Kt, lane, vmask, vmask4,
                                             vmagic);
     }
@@ -411,7 +459,7 @@ __global__ __launch_bounds__(kThreadsM, 1) void k_gemm_mid(const uint4* __restri
 
 template <int GSH, int MODE, int NTB, int R, bool KTAIL>
 hipError_t launch_mid(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
-  constexpr size_t work_bytes = (MODE == kElemM ? (size_t)kWavesM * 64 * kPlaneStrideM * 2 : 0) +
+  constexpr size_t work_bytes = (is_elem(MODE) ? (size_t)kWavesM * 64 * kPlaneStrideM * 2 : 0) +
                                 (size_t)kWavesM * kXSlotBytes;
   constexpr size_t red_bytes = (size_t)R * NTB * kWavesM * 64 * sizeof(float4_t);
   constexpr size_t lds = work_bytes > red_bytes ? work_bytes : red_bytes;
@@ -434,11 +482,15 @@ hipError_t launch_mid(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t
 // Row blocks per workgroup: enough that one round of workgroups covers the
 // layer on 256 CUs (fewer row blocks per workgroup would make a second
 // round, each reading all of its X again), at most 4; with 64 tokens 2 for
-// the element-wise residual or a K tail and 3 for a block residual with
-// G = 32, where more would not fit the registers.
+// the looping element-wise residual or a K tail, and 3 with G = 32 for a
+// block residual or 3 patch entries per lane, where more would not fit the
+// registers.
 template <int GSH, int MODE, int NTB, bool KTAIL>
 hipError_t launch_mid_r(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
-  constexpr int64_t rmax = NTB < 4 ? 4 : (MODE == kElemM || KTAIL) ? 2 : MODE == kBlocksM && GSH == 2 ? 3 : 4;
+  constexpr int64_t rmax = NTB < 4                                                  ? 4
+                           : (MODE == kElemM || KTAIL)                               ? 2
+                           : (MODE == kBlocksM || MODE == kElemFlat3M) && GSH == 2 ? 3
+                                                                                     : 4;
   const int64_t r = std::min<int64_t>(rmax, std::max<int64_t>(1, (p->Nb + 255) / 256));
   if (r == 1) return launch_mid<GSH, MODE, NTB, 1, KTAIL>(p, X, M, Y, s);
   if (r == 2 || rmax == 2) return launch_mid<GSH, MODE, NTB, 2, KTAIL>(p, X, M, Y, s);
@@ -468,7 +520,11 @@ hipError_t launch_mid_m(const mq_packed* p, const uint16_t* X, int64_t M, uint16
   if (p->blocks) {
     return p->nblk > 0 ? launch_mid_g<kBlocksM, KTAIL>(p, X, M, Y, s) : launch_mid_g<kPlainM, KTAIL>(p, X, M, Y, s);
   }
-  return p->nnz > 0 ? launch_mid_g<kElemM, KTAIL>(p, X, M, Y, s) : launch_mid_g<kPlainM, KTAIL>(p, X, M, Y, s);
+  if (p->nnz == 0) return launch_mid_g<kPlainM, KTAIL>(p, X, M, Y, s);
+  if (p->max_seg <= 64) return launch_mid_g<kElemFlat1M, KTAIL>(p, X, M, Y, s);
+  if (p->max_seg <= 128) return launch_mid_g<kElemFlat1M + 1, KTAIL>(p, X, M, Y, s);
+  if (p->max_seg <= 192) return launch_mid_g<kElemFlat3M, KTAIL>(p, X, M, Y, s);
+  return launch_mid_g<kElemM, KTAIL>(p, X, M, Y, s);
 }
 
 }  // namespace

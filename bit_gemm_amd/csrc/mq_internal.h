@@ -26,7 +26,7 @@ struct SelState {
   uint64_t prefix;   // bits of the threshold key found so far (key = bits of |e| as a double)
   uint64_t krem;     // entries still to take among keys equal to the current prefix
   uint32_t flags;    // kFlag* bits raised by the kernels
-  uint32_t pad;
+  uint32_t max_seg;  // the longest per-tile segment of the residual stream (entries, padding included)
 };
 constexpr uint32_t kFlagNonFinite = 1u;
 constexpr uint32_t kFlagScaleOverflow = 2u;
@@ -59,6 +59,7 @@ struct mq_packed {
   float* rscale;        // [N]
   uint32_t* tile_ptr;   // [Nb*Kt + 1]
   uint32_t* entries;    // [nstream + kEntryPad]: residual stream, row blocks padded to 32 entries
+  uint32_t max_seg;     // the longest per-tile segment of the stream (entries, padding included)
   uint32_t* wpatch;     // [nstream + kEntryPad]: the same entries as patches of the GEMM kernels' widened
                         // weights: bits 0-6 column mod 128, 11 valid, 12-15 row mod 16, 16-31
                         // fp16(s q + fp16(sr qr)) XOR fp16(s q); element-wise handles only
@@ -93,7 +94,8 @@ hipError_t pack_blocks_on_device(const uint16_t* W, const float* h, mq_packed* p
 
 // Pieces of the element-wise pipeline the block packer reuses (pack.hip).
 hipError_t launch_pack_base(const uint16_t* W, mq_packed* p, SelState* st, hipStream_t stream);
-hipError_t launch_scan_tiles(const uint32_t* tile_cnt, int64_t ntiles, uint32_t* tile_ptr, hipStream_t stream);
+hipError_t launch_scan_tiles(const uint32_t* tile_cnt, int64_t ntiles, uint32_t* tile_ptr, SelState* st,
+                             hipStream_t stream);
 
 // Outlier migration (migrate.hip): e_j and W^ = W 2^e (W_out may be W);
 // synchronises; *flags_out != 0 when an activation maximum is negative or not

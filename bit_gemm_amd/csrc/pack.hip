@@ -302,15 +302,20 @@ __global__ __launch_bounds__(kWave) void k_row_select(const uint16_t* __restrict
   }
 }
 
-// One block of 1024 threads: exclusive scan of the per-tile entry counts.
+// One block of 1024 threads: exclusive scan of the per-tile entry counts,
+// and their maximum into st->max_seg.
 __global__ __launch_bounds__(1024) void k_scan_tiles(const uint32_t* __restrict__ tile_cnt, int64_t ntiles,
-                                                     uint32_t* __restrict__ tile_ptr) {
+                                                     uint32_t* __restrict__ tile_ptr, SelState* st) {
   __shared__ uint64_t wave_tot[16];
   __shared__ uint64_t tot;
+  __shared__ uint32_t seg_max;
+  if (threadIdx.x == 0) seg_max = 0u;
   uint64_t carry = 0;
+  uint32_t mx = 0u;
   for (int64_t base = 0; base < ntiles; base += blockDim.x) {
     const int64_t i = base + threadIdx.x;
     const uint64_t v = (i < ntiles) ? tile_cnt[i] : 0u;
+    mx = max(mx, (uint32_t)v);
     const uint64_t incl = block_scan_incl(v, wave_tot);
     if (i < ntiles) tile_ptr[i] = (uint32_t)(carry + incl - v);
     if (threadIdx.x == blockDim.x - 1) tot = incl;
@@ -318,7 +323,12 @@ __global__ __launch_bounds__(1024) void k_scan_tiles(const uint32_t* __restrict_
     carry += tot;
     __syncthreads();
   }
-  if (threadIdx.x == 0) tile_ptr[ntiles] = (uint32_t)carry;
+  atomicMax(&seg_max, mx);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    tile_ptr[ntiles] = (uint32_t)carry;
+    st->max_seg = seg_max;
+  }
 }
 
 // ------------------------------------------------- 5. emit CSR and stream
@@ -512,7 +522,7 @@ hipError_t pack_on_device(const uint16_t* W, mq_packed* p, hipStream_t stream, u
     k_row_select<<<dim3(Nb), dim3(kWave), 0, stream>>>(W, p->scales, N, K, G, Kt, p->sstride, st, eb, p->rscale,
                                                        crt, tcnt);
     MQ_TRY(hipGetLastError());
-    k_scan_tiles<<<dim3(1), dim3(1024), 0, stream>>>(tcnt, ntiles, p->tile_ptr);
+    k_scan_tiles<<<dim3(1), dim3(1024), 0, stream>>>(tcnt, ntiles, p->tile_ptr, st);
     MQ_TRY(hipGetLastError());
     k_row_emit<<<dim3(Nb), dim3(kWave), 0, stream>>>(W, p->scales, N, K, G, Kt, p->sstride, st, eb, p->row_ptr,
                                                      p->rscale, crt, p->tile_ptr, p->tiles, p->col,
@@ -528,6 +538,7 @@ hipError_t pack_on_device(const uint16_t* W, mq_packed* p, hipStream_t stream, u
   MQ_TRY(hipStreamSynchronize(stream));
   *flags_out = fin.flags;
   p->nstream = nstream;
+  p->max_seg = fin.max_seg;
   if ((int64_t)nstream > p->stream_cap) *flags_out |= kFlagCountMismatch;
   return hipSuccess;
 }
@@ -539,8 +550,9 @@ hipError_t launch_pack_base(const uint16_t* W, mq_packed* p, SelState* st, hipSt
   return hipGetLastError();
 }
 
-hipError_t launch_scan_tiles(const uint32_t* tile_cnt, int64_t ntiles, uint32_t* tile_ptr, hipStream_t stream) {
-  k_scan_tiles<<<dim3(1), dim3(1024), 0, stream>>>(tile_cnt, ntiles, tile_ptr);
+hipError_t launch_scan_tiles(const uint32_t* tile_cnt, int64_t ntiles, uint32_t* tile_ptr, SelState* st,
+                             hipStream_t stream) {
+  k_scan_tiles<<<dim3(1), dim3(1024), 0, stream>>>(tile_cnt, ntiles, tile_ptr, st);
   return hipGetLastError();
 }
 

@@ -361,7 +361,7 @@ hipError_t pack_blocks_on_device(const uint16_t* W, const float* h, mq_packed* p
     MQ_TRY(hipGetLastError());
     k_block_pad<<<dim3((unsigned)((Nb + 255) / 256)), dim3(256), 0, stream>>>(tcnt, Nb, Kt);
     MQ_TRY(hipGetLastError());
-    MQ_TRY(launch_scan_tiles(tcnt, ntiles, p->tile_ptr, stream));
+    MQ_TRY(launch_scan_tiles(tcnt, ntiles, p->tile_ptr, st, stream));
     k_block_emit<<<dim3((unsigned)nsel), dim3(kWave), 0, stream>>>(W, p->scales, N, K, G, Kt, p->sstride, p->blk,
                                                                    rcnt, p->tile_ptr, p->tiles, p->entries,
                                                                    p->stream_cap, st);

@@ -119,6 +119,45 @@ def test_linear_workload_layers(mq, name):
             check_linear(Y, X, Wt, f"{name} M={M} kernel={kern}")
 
 
+def _longest_segment(ref, N, K):
+    """Entries in the longest (row block, code tile) segment of the patch
+    stream, from the oracle's CSR: per-tile counts, each row block padded to
+    whole 32-entry chunks in its last tile."""
+    rp, col = ref["row_ptr"].astype(np.int64), ref["col"].astype(np.int64)
+    Nb, Kt = -(-N // 16), -(-K // 128)
+    rows = np.repeat(np.arange(N), np.diff(rp))
+    cnt = np.bincount((rows // 16) * Kt + col // 128, minlength=Nb * Kt).reshape(Nb, Kt)
+    cnt[:, -1] += (-cnt.sum(1)) % 32
+    return int(cnt.max())
+
+
+@pytest.mark.parametrize("nnz,bucket", [(200, 1), (440, 2), (640, 3), (1100, 4)])
+def test_mid_kernel_patch_segment_lengths(mq, nnz, bucket):
+    """The mid-size kernel applies a tile's element-wise patches branch-free
+    when no segment exceeds 64, 128 or 192 entries (1, 2 or 3 per lane) and in
+    a loop of 64-entry rounds beyond. Outliers in 16 columns of one code tile
+    inflate its group scales, so most selected entries fall in that tile; the
+    densities put the longest segment (56, 120, 165, 283 entries) in each
+    case."""
+    N, K, G = 64, 1024, 128
+    rng = np.random.default_rng(16)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, 256 + np.arange(16) * 5] *= 40
+    W = W.astype(np.float16)
+    rho = nnz / (N * K)   # exact: N K is a power of two
+    ref = oracle.pack(W, G, rho)
+    seg = _longest_segment(ref, N, K)
+    assert min(-(-seg // 64), 4) == bucket, seg
+    p = mq.mq_pack(to_dev(W), G, rho)
+    assert p.nnz == nnz
+    Wt = oracle.dequant(ref)
+    for M in (5, 16, 33, 64):
+        X = _x(M, K, seed=100 + M)
+        print(f"[mid patch segments] longest={seg} M={M}", flush=True)
+        Y = mq.mq_linear_with(to_dev(X), p, mq.KERNEL_GEMM).cpu().numpy()
+        check_linear(Y, X, Wt, f"longest segment {seg} M={M}")
+
+
 def test_automatic_choice_follows_the_documented_rule(mq):
     """mq_linear picks the GEMV kernels up to 16 tokens when K <= 4096 and up
     to 3 tokens for larger K, else the GEMM path: its output is bit-identical
