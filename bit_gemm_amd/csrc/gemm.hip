@@ -315,14 +315,6 @@ __device__ __forceinline__ void mfma_stage(float16_t (&acc)[IB][JB], const _Floa
   }
 }
 
-// Tile index of workgroup b: the hardware deals workgroups to the 8 XCDs in
-// turn, so the tiles of XCD x are made a contiguous range (one or a few
-// token slices, all their feature tiles).
-__device__ __forceinline__ int xcd_tile(int b, int T) {
-  const int per = T >> 3, rem = T & 7, x = b & 7, local = b >> 3;
-  return x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
-}
-
 template <int GSH, bool KTAIL, class C, bool DR>
 __global__ __launch_bounds__(C::kThreads, 1) void k_gemm(const uint4* __restrict__ tiles,
                                                       const uint16_t* __restrict__ scales, int64_t sstride,
@@ -643,11 +635,13 @@ hipError_t launch_splitk_reduce(const float* part, uint16_t* Y, int64_t M, int64
 
 hipError_t launch_gemm(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
   if (M <= kGemmMidMaxM) return launch_gemm_mid(p, X, M, Y, s);
+  if (gemm_rw_takes(p, M)) return launch_gemm_rw(p, X, M, Y, s);
   return (p->K % kTileCols) != 0 ? launch_k<true>(p, X, M, Y, s, nullptr) : launch_k<false>(p, X, M, Y, s, nullptr);
 }
 
 size_t gemm_workspace_bytes(const mq_packed* p, int64_t M) {
   if (M <= kGemmMidMaxM) return 0;   // the mid-size kernel splits K inside its workgroups
+  if (gemm_rw_takes(p, M)) return 0;
   const int S = M <= kNarrowMaxM ? split_parts<CfgNarrow>(p, M, nullptr) : split_parts<CfgWide>(p, M, nullptr);
   return S > 1 ? (size_t)S * (size_t)M * (size_t)p->N * sizeof(float) : 0;
 }
@@ -670,6 +664,7 @@ hipError_t scratch_address(void** ptr) {
 
 hipError_t launch_gemm_noalloc(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
   if (M <= kGemmMidMaxM) return launch_gemm_mid(p, X, M, Y, s);   // no workspace
+  if (gemm_rw_takes(p, M)) return launch_gemm_rw(p, X, M, Y, s);
   if (gemm_workspace_bytes(p, M) > kScratchBytes) return hipErrorInvalidValue;   // rejected by the caller first
   void* ws = nullptr;
   const hipError_t e = scratch_address(&ws);

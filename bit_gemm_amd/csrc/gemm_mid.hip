@@ -143,22 +143,6 @@ struct MidTile {
   u32x4_t x[NTB][4];                    // X as loaded: token block tb, load u (see mid_load)
 };
 
-// Lane l = 16 a + j of load u of token block tb reads 8 columns of token row
-// 16 tb + 4 u + a: chunk 4 ((j / 4) ^ u) + ((j % 4) ^ a) of the tile's 16
-// chunks of 8 columns. The 4 lanes of a quad read one 64-byte run, and
-// written to the slot in lane order the 4 loads put token row c, chunk h at
-// 16-byte position 64 (c / 4) + 16 (c % 4) + 4 ((h / 4) ^ (c / 4)) +
-// ((h % 4) ^ (c % 4)). The B operand of k-step t in lane n + 16 g is row n,
-// chunk 4 t + g; for fixed t and g the 16 lanes n read 16 distinct 16-byte
-// bank groups.
-__device__ __forceinline__ uint32_t x_load_chunk(int lane, int u) {
-  return 4u * (uint32_t)(((lane & 15) >> 2) ^ u) + (uint32_t)((lane & 3) ^ (lane >> 4));
-}
-__device__ __forceinline__ uint32_t x_read_pos(int lane, int t) {
-  const int n = lane & 15, g = lane >> 4;
-  return (uint32_t)(64 * (n >> 2) + 16 * (n & 3) + 4 * (t ^ (n >> 2)) + (g ^ (n & 3)));
-}
-
 template <int GSH, int MODE, int NTB, int R>
 __device__ __forceinline__ void mid_load_base(MidTile<GSH, MODE, NTB, R>& T, const uint4* __restrict__ tiles,
                                               const uint16_t* __restrict__ scales, int64_t sstride,

@@ -84,6 +84,34 @@ __device__ __forceinline__ uint32_t ent_col(uint32_t e) { return e & 0xFFFu; }
 __device__ __forceinline__ uint32_t ent_row(uint32_t e) { return (e >> 12) & 15u; }
 __device__ __forceinline__ uint32_t ent_delta(uint32_t e) { return e >> 16; }
 
+// Tile index of workgroup b: the hardware deals workgroups to the 8 XCDs in
+// turn, so the tiles of XCD x are made a contiguous range (one or a few
+// token slices, all their feature tiles).
+__device__ __forceinline__ int xcd_tile(int b, int T) {
+  const int per = T >> 3, rem = T & 7, x = b & 7, local = b >> 3;
+  return x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
+}
+
+// X of one token block (16 token rows) for one code tile (128 columns) as a
+// 4 KiB LDS block in the B-operand order of the 16x16x32 fp16 MFMA, filled
+// by 4 loads of 64 lanes x 16 bytes written in lane order (registers stored
+// in lane order, or direct copies into LDS): lane l = 16 a + j of load u
+// reads 8 columns of token row 4 u + a, chunk 4 ((j / 4) ^ u) + ((j % 4) ^ a)
+// of the tile's 16 chunks of 8 columns. The 4 lanes of a quad read one
+// 64-byte run (loading the B order directly would have each quad read 4
+// token rows, which the L2-to-CU path serves at well under half the rate),
+// and the loads put token row c, chunk h at 16-byte position
+// 64 (c / 4) + 16 (c % 4) + 4 ((h / 4) ^ (c / 4)) + ((h % 4) ^ (c % 4)).
+// The B operand of k-step t in lane n + 16 g is row n, chunk 4 t + g; for
+// fixed t and g the 16 lanes n read 16 distinct 16-byte bank groups.
+__device__ __forceinline__ uint32_t x_load_chunk(int lane, int u) {
+  return 4u * (uint32_t)(((lane & 15) >> 2) ^ u) + (uint32_t)((lane & 3) ^ (lane >> 4));
+}
+__device__ __forceinline__ uint32_t x_read_pos(int lane, int t) {
+  const int n = lane & 15, g = lane >> 4;
+  return (uint32_t)(64 * (n >> 2) + 16 * (n & 3) + 4 * (t ^ (n >> 2)) + (g ^ (n & 3)));
+}
+
 // fp32 -> fp16 bits, round to nearest even.
 __device__ __forceinline__ uint16_t f32_to_h(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);

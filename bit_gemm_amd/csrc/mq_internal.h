@@ -116,6 +116,11 @@ hipError_t launch_gemv(const mq_packed* p, const uint16_t* X, int64_t M, uint16_
 // mid-size kernel below).
 hipError_t launch_gemm(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
 
+// Prefill kernel with the weights widened in registers (gemm_rw.hip), for
+// the handles and shapes gemm_rw_takes accepts.
+bool gemm_rw_takes(const mq_packed* p, int64_t M);
+hipError_t launch_gemm_rw(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
+
 // Mid-size batch kernel (gemm_mid.hip): M <= 64, no workspace.
 hipError_t launch_gemm_mid(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
 constexpr int64_t kGemmMidMaxM = 64;
