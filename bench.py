@@ -286,6 +286,10 @@ def bench_decode(args, mq, synth, torch):
         mr = replay_spread(torch, res, args.warmup, args.steps)[0]
         unfused[str(M)] = {"us": round(m2 * 1e3, 3), "residual_kernel_us": round(mr * 1e3, 3),
                            "over_fused": round(m2 * 1e3 / per_m[str(M)]["us"], 3)}
+    handle = {"plain_w4_bytes": plain[0].device_bytes, "elementwise_bytes": first.device_bytes,
+              "over_plain_w4": round(first.device_bytes / plain[0].device_bytes, 4),
+              "bits_per_weight": round(8.0 * first.device_bytes / (layer.N * layer.K), 4),
+              "plain_w4_bits_per_weight": round(8.0 * plain[0].device_bytes / (layer.N * layer.K), 4)}
     for p in plain:
         p.free()
     # warm, single copy (weights can stay in the Infinity Cache): context only
@@ -296,7 +300,7 @@ def bench_decode(args, mq, synth, torch):
         "layer": layer, "first": first, "ms_per_step": ms / args.steps, "bytes_step": bytes_step,
         "launches_per_step": len(Ms), "per_m": per_m, "pack_ms": pack_ms, "pack_wall_ms": pack_wall_ms,
         "copies": ncopy, "warm_us_m1": warm_ms * 1e3, "nnz": first.nnz, "overhead": overhead,
-        "unfused": unfused,
+        "unfused": unfused, "handle": handle,
     }
 
 
@@ -521,8 +525,10 @@ def bench_blocks(args, mq, synth, torch):
 
     base = mq.mq_pack(W, layer.group, 0.0)
     D0 = distortion(base)
+    plain_bytes = base.device_bytes
     res = {"workload": "decode-11008x4096", "block": "16x128", "calibration_tokens": 256,
-           "D_base": D0, "base_us": decode_us(lambda: mq.mq_pack(W, layer.group, 0.0)), "by_fraction": {}}
+           "D_base": D0, "base_us": decode_us(lambda: mq.mq_pack(W, layer.group, 0.0)),
+           "plain_w4_device_bytes": plain_bytes, "by_fraction": {}}
     base.free()
     for beta in (0.01, 0.05, 0.1, 0.2):
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -532,6 +538,8 @@ def bench_blocks(args, mq, synth, torch):
         torch.cuda.synchronize()
         rbytes = p.nblk * (16 * 64 + 16 * 4)             # 4-bit codes + fp32 scale per block row
         entry = {"nblk": p.nblk, "entries": p.nnz, "pack_ms": round(ev0.elapsed_time(ev1), 3),
+                 "device_bytes": p.device_bytes, "over_plain_w4": round(p.device_bytes / plain_bytes, 4),
+                 "bits_per_weight": round(8.0 * p.device_bytes / (N * K), 4),
                  "residual_bytes": rbytes, "recovered": round(1.0 - distortion(p) / D0, 4),
                  "us": decode_us(lambda: mq.mq_pack_blocks(W, layer.group, beta, h))}
         p.free()
@@ -848,6 +856,7 @@ def main():
         "decode_residual_overhead_t_rho_over_t0": d["overhead"],
         "decode_unfused_two_kernels": d["unfused"],
         "decode_warm_single_copy_us_M1": None if args.no_warm else round(d["warm_us_m1"], 3),
+        "handle_device_bytes": d["handle"],
         "pack": {"workload": "decode-11008x4096", "gpu_ms": round(d["pack_ms"], 3),
                  "wall_ms_first_call": round(d["pack_wall_ms"], 3)},
     }

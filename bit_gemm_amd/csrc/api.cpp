@@ -35,7 +35,7 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 void release(mq_packed* p) {
   void* bufs[] = {p->tiles,    p->scales,  p->row_ptr, p->col,    p->rcodes, p->rscale,  p->tile_ptr,
-                  p->entries, p->wpatch,  p->blk,     p->bscale, p->bcodes, p->rt_ptr, p->rt_tiles,
+                  p->entries, p->wpatch,  p->blk,     p->bscale, p->rt_ptr, p->rt_tiles,
                   p->rt_slot};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
@@ -201,22 +201,20 @@ MQ_API mq_status mq_pack_blocks(const void* W_dev_fp16, int64_t N, int64_t K, in
   int64_t nsel = (int64_t)std::floor(block_fraction * (double)nblocks);   // one float64 product, then floor
   if (nsel > nblocks) nsel = nblocks;
   p->nblk = nsel;
-  // every entry of a selected block may carry a nonzero code; row blocks pad to 32 entries
-  p->stream_cap = nsel * mq::kRowsPerBlock * mq::kTileCols + (int64_t)(mq::kChunk - 1) * p->Nb;
 
+  // The handle holds what the kernels read: base tiles and scales, and the
+  // residual blocks as code tiles with a scale per row, located by the
+  // blocks' slot per tile and first block per row block. (The canonical
+  // block codes are derived from the code tiles on export.)
   const size_t n_tiles = (size_t)nblocks;
-  const size_t sz_ent = (size_t)(p->stream_cap + mq::kEntryPad) * sizeof(uint32_t);
   const size_t nb1 = (size_t)nsel + 1;   // one more all-zero block slot
   struct {
     void** dst;
     size_t n;
   } allocs[] = {{(void**)&p->tiles, n_tiles * mq::kTileBytes},
                 {(void**)&p->scales, (size_t)(p->Nb * mq::kRowsPerBlock * p->sstride) * sizeof(uint16_t)},
-                {(void**)&p->tile_ptr, (n_tiles + 1) * sizeof(uint32_t)},
-                {(void**)&p->entries, sz_ent},
                 {(void**)&p->blk, nb1 * sizeof(int32_t)},
                 {(void**)&p->bscale, nb1 * mq::kRowsPerBlock * sizeof(float)},
-                {(void**)&p->bcodes, nb1 * mq::kRowsPerBlock * (mq::kTileCols / 2)},
                 {(void**)&p->rt_ptr, (size_t)(p->Nb + 1) * sizeof(uint32_t)},
                 {(void**)&p->rt_tiles, nb1 * mq::kTileBytes},
                 {(void**)&p->rt_slot, n_tiles * sizeof(int32_t)}};
@@ -275,8 +273,9 @@ MQ_API mq_status mq_export_blocks(const mq_packed* p, void* blk_i32, void* rscal
   if (blk_i32) e = hipMemcpyAsync(blk_i32, p->blk, n * sizeof(int32_t), hipMemcpyDefault, s);
   if (e == hipSuccess && rscale_f32)
     e = hipMemcpyAsync(rscale_f32, p->bscale, n * mq::kRowsPerBlock * sizeof(float), hipMemcpyDefault, s);
-  if (e == hipSuccess && rcodes_u8)
-    e = hipMemcpyAsync(rcodes_u8, p->bcodes, n * mq::kRowsPerBlock * (mq::kTileCols / 2), hipMemcpyDefault, s);
+  if (e == hipSuccess && rcodes_u8)   // block n as a 16-row, 128-column layer of one tile per row block
+    e = mq::export_tile_codes(p->rt_tiles, (int64_t)n * mq::kRowsPerBlock, mq::kTileCols,
+                              static_cast<uint8_t*>(rcodes_u8), s);
   return from_hip(e);
 }
 
@@ -440,6 +439,7 @@ MQ_API mq_status mq_export_canonical(const mq_packed* p, void* codes_u8, void* s
 MQ_API mq_status mq_export_tiled(const mq_packed* p, void* tiles_u8, void* tile_ptr_u32, void* entries_u32,
                                  void* hip_stream) {
   if (!is_live(p)) return MQ_ERR_BAD_HANDLE;
+  if (p->blocks && (tile_ptr_u32 || entries_u32)) return MQ_ERR_UNSUPPORTED;   // no element-wise stream
   const hipStream_t s = static_cast<hipStream_t>(hip_stream);
   const size_t n_tiles = (size_t)(p->Nb * p->Kt);
   hipError_t e = hipSuccess;

@@ -947,6 +947,10 @@ hipError_t run_g(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipS
 }  // namespace
 
 hipError_t launch_gemv(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
+  // Block-residual handles carry their residual as code tiles only, which
+  // the K = 4096 kernels up to 16 tokens multiply; otherwise the mid-size
+  // kernel (any K, up to 64 tokens) takes them.
+  if (p->blocks && (p->K != 4096 || M > 16)) return launch_gemm_mid(p, X, M, Y, s);
   if (M <= 16) return run_g<1>(p, X, (int)M, Y, s);
   if (M <= 32) return run_g<2>(p, X, (int)M, Y, s);
   return run_g<4>(p, X, (int)M, Y, s);

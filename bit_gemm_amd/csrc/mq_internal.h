@@ -57,8 +57,8 @@ struct mq_packed {
   uint16_t* col;        // [nnz]
   uint8_t* rcodes;      // [(nnz+1)/2 rounded up to 4]
   float* rscale;        // [N]
-  uint32_t* tile_ptr;   // [Nb*Kt + 1]
-  uint32_t* entries;    // [nstream + kEntryPad]: residual stream, row blocks padded to 32 entries
+  uint32_t* tile_ptr;   // [Nb*Kt + 1] (element-wise handles)
+  uint32_t* entries;    // [nstream + kEntryPad]: residual stream, row blocks padded to 32 entries (element-wise)
   uint32_t max_seg;     // the longest per-tile segment of the stream (entries, padding included)
   uint32_t* wpatch;     // [nstream + kEntryPad]: the same entries as patches of the GEMM kernels' widened
                         // weights: bits 0-6 column mod 128, 11 valid, 12-15 row mod 16, 16-31
@@ -71,7 +71,6 @@ struct mq_packed {
   int64_t nblk;         // selected 16 x 128 residual blocks
   int32_t* blk;         // [nblk] block indices rb * Kt + kt, ascending
   float* bscale;        // [nblk][16] residual scale of each block row
-  uint8_t* bcodes;      // [nblk][16][64] residual codes u = qr + 8, even column in the low nibble
   uint32_t* rt_ptr;     // [Nb + 1]: the blocks of row block rb are blk[rt_ptr[rb] .. rt_ptr[rb + 1])
   uint8_t* rt_tiles;    // [nblk + 1][1 KiB]: the blocks' codes in the code-tile layout; slot nblk
                         // (like blk[nblk] = 0 and bscale[nblk][*] = 0) is an all-zero residual
@@ -108,8 +107,12 @@ hipError_t smooth_activations(const uint16_t* X, int64_t M, int64_t K, const int
 
 // Canonical / tiled export (pack.hip).
 hipError_t export_codes(const mq_packed* p, uint8_t* codes, hipStream_t stream);
+// The same for any array of code tiles laid out as an N x K layer (tile
+// (rb, kt) at (rb * ceil(K / 128) + kt) * 1 KiB; K a multiple of 32).
+hipError_t export_tile_codes(const uint8_t* tiles, int64_t N, int64_t K, uint8_t* codes, hipStream_t stream);
 
-// Decode kernel (gemv.hip): M <= 64.
+// Decode kernel (gemv.hip): M <= 64 (block-residual handles with K != 4096
+// or more than 16 tokens run the mid-size kernel).
 hipError_t launch_gemv(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
 
 // Prefill kernel (gemm.hip): any M >= 1 (up to 64 tokens it runs the

@@ -556,11 +556,17 @@ hipError_t launch_scan_tiles(const uint32_t* tile_cnt, int64_t ntiles, uint32_t*
   return hipGetLastError();
 }
 
-hipError_t export_codes(const mq_packed* p, uint8_t* codes, hipStream_t stream) {
-  const int64_t n = p->N * (p->K / 32);
+hipError_t export_tile_codes(const uint8_t* tiles, int64_t N, int64_t K, uint8_t* codes, hipStream_t stream) {
+  const int64_t n = N * (K / 32);
+  if (n == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((n + 255) / 256);
-  k_export_codes<<<dim3(blocks), dim3(256), 0, stream>>>(p->tiles, (int)p->N, (int)p->K, (int)p->Kt, codes);
+  k_export_codes<<<dim3(blocks), dim3(256), 0, stream>>>(tiles, (int)N, (int)K, (int)((K + kTileCols - 1) / kTileCols),
+                                                          codes);
   return hipGetLastError();
+}
+
+hipError_t export_codes(const mq_packed* p, uint8_t* codes, hipStream_t stream) {
+  return export_tile_codes(p->tiles, p->N, p->K, codes, stream);
 }
 
 }  // namespace mq

@@ -17,17 +17,11 @@
 //   3. k_block_select (one workgroup): radix select of the K-th largest score
 //      (8 passes of 8 bits over the double's bit pattern), then the chosen
 //      block indices in ascending order (ties at the threshold by index);
-//   4. k_block_codes: the selected blocks' scales and codes in canonical form
-//      and their nonzero counts per row and per tile; k_block_pad rounds each
-//      row block's stream segment up to whole 32-entry chunks;
-//   5. k_block_emit: the residual stream the fused kernels read (entries with
-//      fp16(sr qr), and the patched weights fp16(s q + fp16(sr qr))), in the
-//      same (row block, tile, row, column) order as element-wise packing, so
-//      the prefill and general decode kernels run these handles unchanged;
-//      the blocks are also kept as 4-bit code tiles (with k_block_rtptr's
-//      per-row-block ranges and k_block_slots' per-tile slots), which the
-//      K = 4096 decode kernels multiply on the MFMA path like the base tiles
-//      and the prefill GEMM widens into the weight tile it stages.
+//   4. k_block_codes: the selected blocks' residual scales and codes, as
+//      4-bit code tiles in the base tile layout (with k_block_rtptr's
+//      per-row-block ranges and k_block_slots' per-tile slots): the decode,
+//      mid-size and prefill kernels widen them like the base tiles (the
+//      canonical codes are derived from these tiles on export).
 #include "mq_internal.h"
 #include "pack_common.h"
 #include "quant_exact.h"
@@ -171,10 +165,7 @@ __global__ __launch_bounds__(1024) void k_block_select(const uint64_t* __restric
 __global__ __launch_bounds__(kWave) void k_block_codes(const uint16_t* __restrict__ W,
                                                        const uint16_t* __restrict__ scales, int N, int K, int G,
                                                        int Kt, int64_t sstride, const int32_t* __restrict__ blk,
-                                                       float* __restrict__ bscale, uint8_t* __restrict__ bcodes,
-                                                       uint8_t* __restrict__ rt_tiles,
-                                                       uint32_t* __restrict__ row_cnt,
-                                                       uint32_t* __restrict__ tile_cnt,
+                                                       float* __restrict__ bscale, uint8_t* __restrict__ rt_tiles,
                                                        unsigned long long* __restrict__ nnz) {
   __shared__ uint8_t u[kRowsPerBlock][kTileCols];
   const int n = blockIdx.x, b = blk[n], rb = b / Kt, kt = b - (b / Kt) * Kt;
@@ -190,10 +181,7 @@ __global__ __launch_bounds__(kWave) void k_block_codes(const uint16_t* __restric
   }
   if (kq == 0) bscale[(int64_t)n * kRowsPerBlock + r] = __builtin_bit_cast(float, L.srbits);
   __syncthreads();
-  uint8_t* dst = bcodes + ((int64_t)n * kRowsPerBlock + r) * (kTileCols / 2) + 16 * kq;
-#pragma unroll
-  for (int t = 0; t < 16; ++t) dst[t] = (uint8_t)(u[r][32 * kq + 2 * t] | (u[r][32 * kq + 2 * t + 1] << 4));
-  // the same codes in the code-tile layout (as the base tiles): lane r + 16 g,
+  // the codes in the code-tile layout (as the base tiles): lane r + 16 g,
   // dword s4 holds columns 32 s4 + 8 g + c at nibble nib_pos(c)
   uint32_t d[4];
 #pragma unroll
@@ -204,16 +192,11 @@ __global__ __launch_bounds__(kWave) void k_block_codes(const uint16_t* __restric
     d[s4] = v;
   }
   reinterpret_cast<uint4*>(rt_tiles)[(int64_t)n * kWave + lane] = make_uint4(d[0], d[1], d[2], d[3]);
-  uint32_t ex, tot;
-  row_lanes(nz, lane, &ex, &tot);
-  if (kq == 0) row_cnt[(int64_t)n * kRowsPerBlock + r] = tot;
-  uint32_t v = (kq == 0) ? tot : 0u;
+  // the block's nonzero residual codes, counted into nnz
+  uint32_t v = nz;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o);
-  if (lane == 0) {
-    tile_cnt[b] = v;
-    atomicAdd(nnz, (unsigned long long)v);
-  }
+  if (lane == 0) atomicAdd(nnz, (unsigned long long)v);
 }
 
 // rt_ptr[rb] = first selected block of row block rb (blk is ascending, so a
@@ -245,62 +228,6 @@ __global__ __launch_bounds__(256) void k_block_slots_set(const int32_t* __restri
   if (n < nsel) rt_slot[blk[n]] = (int32_t)n;
 }
 
-// A row block's stream segment ends on a whole 32-entry chunk (zero entries).
-__global__ __launch_bounds__(256) void k_block_pad(uint32_t* __restrict__ tile_cnt, int64_t Nb, int Kt) {
-  const int64_t rb = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (rb >= Nb) return;
-  uint32_t total = 0;
-  for (int kt = 0; kt < Kt; ++kt) total += tile_cnt[rb * Kt + kt];
-  if (total % kChunk) tile_cnt[rb * Kt + Kt - 1] += kChunk - total % kChunk;
-}
-
-// -------------------------------------------------------------- 5. emit
-__global__ __launch_bounds__(kWave) void k_block_emit(const uint16_t* __restrict__ W,
-                                                      const uint16_t* __restrict__ scales, int N, int K, int G,
-                                                      int Kt, int64_t sstride, const int32_t* __restrict__ blk,
-                                                      const uint32_t* __restrict__ row_cnt,
-                                                      const uint32_t* __restrict__ tile_ptr,
-                                                      const uint8_t* __restrict__ tiles,
-                                                      uint32_t* __restrict__ entries, int64_t stream_cap,
-                                                      SelState* flags) {
-  const int n = blockIdx.x, b = blk[n], rb = b / Kt, kt = b - (b / Kt) * Kt;
-  const int lane = threadIdx.x, r = lane & 15, kq = lane >> 4;
-  BlockLane L;
-  block_lane(W, scales, N, K, G, sstride, rb, kt, lane, L);
-  int qr[32];
-  uint32_t nz = 0;
-#pragma unroll
-  for (int c = 0; c < 32; ++c) {
-    qr[c] = L.t.valid ? quant7_scaled(L.e[c], L.sm, L.sQ) : 0;
-    nz += (qr[c] != 0) ? 1u : 0u;
-  }
-  // entries of rows r' < r of the tile come first
-  const uint32_t rc = row_cnt[(int64_t)n * kRowsPerBlock + r];
-  uint32_t incl = rc;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    const uint32_t x = (uint32_t)__shfl_up((int)incl, o, 16);
-    if (r >= o) incl += x;
-  }
-  uint32_t ex, tot;
-  row_lanes(nz, lane, &ex, &tot);
-  if (!L.t.valid || nz == 0) return;
-  uint32_t ps = tile_ptr[b] + (incl - rc) + ex;
-  for (int c = 0; c < 32; ++c) {
-    if (qr[c] == 0) continue;
-    if ((int64_t)ps >= stream_cap) {   // counts disagree: never write out of bounds
-      atomicOr(&flags->flags, kFlagCountMismatch);
-      return;
-    }
-    const int j = L.t.c0 + c;
-    // residual value sr qr = sm qr 2^(sQ - 24), rounded to fp16 for the kernels
-    const _Float16 dh = (_Float16)ldexpf((float)((int64_t)L.sm * qr[c]), L.sQ - 24);
-    entries[ps] = ((uint32_t)__builtin_bit_cast(uint16_t, dh) << 16) | ((uint32_t)r << 12) |
-                  ((uint32_t)j & (kColWindow - 1));
-    ++ps;
-  }
-}
-
 struct Temp {
   void* p = nullptr;
   ~Temp() {
@@ -320,13 +247,11 @@ hipError_t pack_blocks_on_device(const uint16_t* W, const float* h, mq_packed* p
                                  uint32_t* flags_out) {
   const int N = (int)p->N, K = (int)p->K, G = p->G, Kt = (int)p->Kt;
   const int64_t Nb = p->Nb, ntiles = Nb * Kt, nsel = p->nblk;
-  Temp t_state, t_keys, t_rc, t_tc, t_nnz;
+  Temp t_state, t_keys, t_nnz;
   MQ_TRY(hipMalloc(&t_state.p, sizeof(SelState)));
   SelState* st = static_cast<SelState*>(t_state.p);
   MQ_TRY(hipMemsetAsync(st, 0, sizeof(SelState), stream));
   MQ_TRY(hipMemsetAsync(p->scales, 0, (size_t)Nb * kRowsPerBlock * p->sstride * sizeof(uint16_t), stream));
-  MQ_TRY(hipMemsetAsync(p->tile_ptr, 0, (size_t)(ntiles + 1) * sizeof(uint32_t), stream));
-  MQ_TRY(hipMemsetAsync(p->entries, 0, (size_t)(p->stream_cap + kEntryPad) * sizeof(uint32_t), stream));
   MQ_TRY(launch_pack_base(W, p, st, stream));
   // the all-zero block slot nblk: block 0's column tile, scales 0, codes 8 (q = 0)
   MQ_TRY(hipMemsetAsync(p->blk + nsel, 0, sizeof(int32_t), stream));
@@ -337,47 +262,31 @@ hipError_t pack_blocks_on_device(const uint16_t* W, const float* h, mq_packed* p
   MQ_TRY(hipGetLastError());
 
   MQ_TRY(hipMalloc(&t_keys.p, (size_t)ntiles * sizeof(uint64_t)));
-  MQ_TRY(hipMalloc(&t_tc.p, (size_t)ntiles * sizeof(uint32_t)));
   MQ_TRY(hipMalloc(&t_nnz.p, sizeof(unsigned long long)));
-  MQ_TRY(hipMemsetAsync(t_tc.p, 0, (size_t)ntiles * sizeof(uint32_t), stream));
   MQ_TRY(hipMemsetAsync(t_nnz.p, 0, sizeof(unsigned long long), stream));
   uint64_t* keys = static_cast<uint64_t*>(t_keys.p);
-  uint32_t* tcnt = static_cast<uint32_t*>(t_tc.p);
   k_block_scores<<<dim3((unsigned)ntiles), dim3(kWave), 0, stream>>>(W, p->scales, h, N, K, G, Kt, p->sstride,
                                                                      keys, st);
   MQ_TRY(hipGetLastError());
   if (nsel > 0) {
-    MQ_TRY(hipMalloc(&t_rc.p, (size_t)nsel * kRowsPerBlock * sizeof(uint32_t)));
-    uint32_t* rcnt = static_cast<uint32_t*>(t_rc.p);
     k_block_select<<<dim3(1), dim3(1024), 0, stream>>>(keys, ntiles, nsel, p->blk);
     MQ_TRY(hipGetLastError());
     k_block_codes<<<dim3((unsigned)nsel), dim3(kWave), 0, stream>>>(
-        W, p->scales, N, K, G, Kt, p->sstride, p->blk, p->bscale, p->bcodes, p->rt_tiles, rcnt, tcnt,
+        W, p->scales, N, K, G, Kt, p->sstride, p->blk, p->bscale, p->rt_tiles,
         static_cast<unsigned long long*>(t_nnz.p));
     MQ_TRY(hipGetLastError());
     k_block_rtptr<<<dim3((unsigned)((Nb + 1 + 255) / 256)), dim3(256), 0, stream>>>(p->blk, nsel, Nb, Kt, p->rt_ptr);
     MQ_TRY(hipGetLastError());
     k_block_slots_set<<<dim3((unsigned)((nsel + 255) / 256)), dim3(256), 0, stream>>>(p->blk, nsel, p->rt_slot);
     MQ_TRY(hipGetLastError());
-    k_block_pad<<<dim3((unsigned)((Nb + 255) / 256)), dim3(256), 0, stream>>>(tcnt, Nb, Kt);
-    MQ_TRY(hipGetLastError());
-    MQ_TRY(launch_scan_tiles(tcnt, ntiles, p->tile_ptr, st, stream));
-    k_block_emit<<<dim3((unsigned)nsel), dim3(kWave), 0, stream>>>(W, p->scales, N, K, G, Kt, p->sstride, p->blk,
-                                                                   rcnt, p->tile_ptr, p->tiles, p->entries,
-                                                                   p->stream_cap, st);
-    MQ_TRY(hipGetLastError());
   }
   SelState fin;
-  uint32_t nstream = 0;
   unsigned long long nnz = 0;
   MQ_TRY(hipMemcpyAsync(&fin, st, sizeof(fin), hipMemcpyDeviceToHost, stream));
-  MQ_TRY(hipMemcpyAsync(&nstream, p->tile_ptr + ntiles, sizeof(nstream), hipMemcpyDeviceToHost, stream));
   MQ_TRY(hipMemcpyAsync(&nnz, t_nnz.p, sizeof(nnz), hipMemcpyDeviceToHost, stream));
   MQ_TRY(hipStreamSynchronize(stream));
   *flags_out = fin.flags;
-  p->nstream = nstream;
   p->nnz = (int64_t)nnz;
-  if ((int64_t)nstream > p->stream_cap) *flags_out |= kFlagCountMismatch;
   return hipSuccess;
 }
 

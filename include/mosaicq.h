@@ -159,8 +159,9 @@ mq_status mq_residual_add(const void* X_dev_fp16, int64_t M, const mq_packed* p,
 
 /*
  * mq_packed_info -- sizes of a packed layer; any output pointer may be NULL.
- *   bytes = device bytes the handle owns (codes, scales, the canonical
- *   residual, and the two tile-ordered residual streams the kernels read).
+ *   bytes = device bytes the handle owns: codes and scales, and for mq_pack
+ *   the canonical residual and the two tile-ordered residual streams the
+ *   kernels read, for mq_pack_blocks the residual blocks as code tiles.
  */
 mq_status mq_packed_info(const mq_packed* p, int64_t* N, int64_t* K, int32_t* G,
                          int64_t* nnz, size_t* bytes);
@@ -198,9 +199,11 @@ mq_status mq_export_canonical(const mq_packed* p, void* codes_u8, void* scales_f
  *                 bits 16-31 the residual value sr*qr rounded to fp16, which the
  *                 decode kernels add to the base weight s*q. Each row block's
  *                 segment ends with zero entries up to a multiple of 32. (The
- *                 prefill kernel reads a parallel copy of this stream, not
- *                 exported, whose entries hold the patched weight
- *                 fp16(s*q + that value) instead.)
+ *                 mid-size and prefill kernels read a parallel copy of this
+ *                 stream, not exported, whose entries hold the patched weight
+ *                 fp16(s*q + that value) XOR fp16(s*q) instead.)
+ * A handle from mq_pack_blocks has no residual stream: tile_ptr_u32 or
+ * entries_u32 non-NULL return MQ_ERR_UNSUPPORTED for it (tiles_u8 works).
  */
 mq_status mq_export_tiled(const mq_packed* p, void* tiles_u8, void* tile_ptr_u32,
                           void* entries_u32, void* hip_stream);
@@ -231,12 +234,16 @@ mq_status mq_export_tiled(const mq_packed* p, void* tiles_u8, void* tile_ptr_u32
  *                   finite (for calibration activations X: h_j = sum_m X_mj^2);
  *                   read during the call only, 4-byte aligned
  *
- * The handle runs in mq_linear / mq_linear_with like any other (the selected
- * blocks' nonzero residual codes become entries of the residual stream
- * described at mq_export_tiled). mq_packed_info's nnz counts those entries.
- * mq_residual_add and the residual arrays of mq_export_canonical are not
- * available for it (MQ_ERR_UNSUPPORTED; codes and scales export as usual);
- * mq_export_blocks gives the residual. Synchronises hip_stream once, like
+ * The handle runs in mq_linear / mq_linear_with like any other. It holds the
+ * selected blocks as 4-bit code tiles with a scale per row, which every
+ * kernel widens like the base tiles (MQ_KERNEL_GEMV with K != 4096 or more
+ * than 16 tokens runs the mid-size kernel for it), and nothing else of the
+ * residual: about 1 KiB + 64 B per block on top of the plain handle.
+ * mq_packed_info's nnz counts the blocks' nonzero residual codes.
+ * mq_residual_add, the residual arrays of mq_export_canonical and the
+ * residual stream of mq_export_tiled are not available for it
+ * (MQ_ERR_UNSUPPORTED; codes and scales export as usual); mq_export_blocks
+ * gives the residual. Synchronises hip_stream once, like
  * mq_pack. Errors as mq_pack, plus MQ_ERR_INVALID_ARG for block_fraction
  * outside [0, 1] (or NaN), a NULL or misaligned h, or a negative or
  * non-finite h value.

@@ -104,6 +104,13 @@ def test_decode_layer_block_budget(mq):
     p, got, base, ref = _pack_both(mq, W, layer.group, 0.1, h)
     assert p.nblk == 2201
     _assert_blocks_equal(got, base, ref)
+    # the handle holds the base and the blocks as code tiles, nothing else of
+    # the residual: within 1.12 x the device bytes of the plain 4-bit handle
+    plain = mq.mq_pack(to_dev(W), layer.group, 0.0)
+    ratio = p.device_bytes / plain.device_bytes
+    print(f"[block bytes] {p.device_bytes} vs plain {plain.device_bytes}: {ratio:.4f}", flush=True)
+    assert ratio <= 1.12, ratio
+    plain.free()
     Wt = ob.dequant_blocks(ref)
     for M in (1, 16):
         X = layer.X(M)
@@ -132,6 +139,8 @@ def test_block_handle_errors(mq):
     rp = torch.zeros(33, dtype=torch.int32, device="cuda")
     assert mq.lib.mq_export_canonical(p.handle, None, None, ctypes.c_void_p(rp.data_ptr()), None, None, None,
                                       None) == -2
+    # no element-wise residual stream in a block handle
+    assert mq.lib.mq_export_tiled(p.handle, None, ctypes.c_void_p(rp.data_ptr()), None, None) == -2
     q = mq.mq_pack(to_dev(W), 128, 0.01)
     assert mq.lib.mq_export_blocks(q.handle, None, None, None, None) == -2
     n = ctypes.c_int64()
