@@ -778,6 +778,80 @@ def cpu_baseline(layer, Ms, min_seconds=10.0, max_steps=60):
             "seconds": round(t_lin, 3), "steps": steps, "pack_seconds": round(t_pack, 2)}
 
 
+def cpu_baseline_configs(synth):
+    """The oracle, as it stands, on the other configurations, pack and
+    linear timed apart (one run each; a baseline, not a target):
+      * block-4096h: the seven linears of the 4096-hidden block, packed, then
+        dequantised and multiplied at M = 16;
+      * prefill-28672x8192: packed, dequantised, multiplied at M = 512 and
+        2048 (float64);
+      * sweep-14336x4096 (columns placement): packed at each density, and at
+        0.5 % dequantised and multiplied at M = 1, 64 and 512."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    out = {"cores": int(threads), "kind": "oracle"}
+    # block-4096h at M = 16
+    wl = synth.WORKLOADS["block-4096h"]
+    M = wl.batch[0]
+    t_pack = t_deq = t_lin = 0.0
+    flops = 0
+    for layer in wl.layers:
+        W = layer.W()
+        pk, dt = timed(lambda: oracle.pack(W, layer.group, layer.rho))
+        t_pack += dt
+        Wt, dt = timed(lambda: oracle.dequant(pk))
+        t_deq += dt
+        _, dt = timed(lambda: oracle.linear(layer.X(M), Wt))
+        t_lin += dt
+        flops += 2 * M * layer.N * layer.K
+    out["block_4096h_m16"] = {"pack_seconds": round(t_pack, 2), "dequant_seconds": round(t_deq, 2),
+                              "linear_seconds": round(t_lin, 3), "linear_GFLOPs": round(flops / t_lin / 1e9, 2),
+                              "sample": "the 7 layers once each"}
+    # prefill at M = 512, 2048
+    layer = synth.WORKLOADS["prefill-28672x8192"].layers[0]
+    W = layer.W()
+    pk, t_pack = timed(lambda: oracle.pack(W, layer.group, layer.rho))
+    Wt, t_deq = timed(lambda: oracle.dequant(pk))
+    lin = {}
+    for M in (512, 2048):
+        X = layer.X(M)
+        _, dt = timed(lambda: oracle.linear(X, Wt))
+        lin[str(M)] = {"seconds": round(dt, 3), "TFLOPs": round(2.0 * M * layer.N * layer.K / dt / 1e12, 4)}
+    out["prefill_28672x8192"] = {"pack_seconds": round(t_pack, 2), "dequant_seconds": round(t_deq, 2),
+                                 "linear": lin, "sample": "one pack, one dequant, one linear per M"}
+    del Wt, pk, W
+    # residual sweep, columns placement
+    packs = {}
+    for rho in synth.SWEEP_RHOS:
+        sl = synth.sweep_layer("columns", rho)
+        W = sl.W()
+        pk, dt = timed(lambda: oracle.pack(W, sl.group, rho))
+        packs[str(rho)] = round(dt, 2)
+        if rho == 0.005:
+            Wt, t_deq = timed(lambda: oracle.dequant(pk))
+            lin = {}
+            for M in synth.SWEEP_BATCH:
+                X = sl.X(M)
+                _, dt = timed(lambda: oracle.linear(X, Wt))
+                lin[str(M)] = round(dt, 4)
+            del Wt
+    out["sweep_14336x4096_columns"] = {"pack_seconds_by_rho": packs, "dequant_seconds_rho_0.005": round(t_deq, 2),
+                                       "linear_seconds_rho_0.005": lin,
+                                       "sample": "one pack per density; one dequant and linear per M at 0.5 %"}
+    return out
+
+
 def progress(leg):
     """One line on stderr per finished leg (the JSON line stays alone on stdout)."""
     print(f"[bench] {leg} done at {time.strftime('%H:%M:%S')}", file=sys.stderr, flush=True)
@@ -874,6 +948,8 @@ def main():
     if args.only != "decode" and not args.skip_cpu:
         line["cpu_baseline"] = cpu_baseline(d["layer"], [1, 4, 16])
         progress("cpu_baseline")
+        line["cpu_baseline_configs"] = cpu_baseline_configs(synth)
+        progress("cpu_baseline_configs")
     print(json.dumps(line), flush=True)
 
 
