@@ -131,8 +131,9 @@ def replay_spread(torch, fn, warmup, steps, reps=9):
 
 
 DECODE_SOURCES = ("gemv.hip", "kernel_common.h", "mq_internal.h")
-GEMM_SOURCES = ("gemm.hip", "kernel_common.h", "mq_internal.h")
 MID_SOURCES = ("gemm_mid.hip", "kernel_common.h", "mq_internal.h")
+PREFILL_SOURCES = ("gemm.hip", "gemm_rw.hip", "kernel_common.h", "mq_internal.h")
+STREAM_SOURCES = ("probe.hip",)
 
 
 def source_digest(files=DECODE_SOURCES):
@@ -335,17 +336,21 @@ def bench_prefill(args, mq, synth, torch):
     # dense fp16 MFMA peak, with the matrix-core busy fraction and the clock
     # that the committed rocprofv3 counter summary measured for this kernel
     mtop = str(max(wl.batch))
-    cnt = profile_values("prefill_mfma_counters.txt", GEMM_SOURCES)
+    cnt = profile_values("prefill_mfma_counters.txt", PREFILL_SOURCES)
     out["roofline"] = {"bound": "mfma", "achieved": out["M"][mtop]["TFLOPs"], "peak": FP16_PEAK_TFLOPS,
                        "unit": "TFLOP/s", "frac": out["M"][mtop]["frac_mfma_peak"], "M": int(mtop),
                        "flops_per_launch": 2 * int(mtop) * layer.N * layer.K,
                        "profile_mfma_busy": float(cnt[f"mfma_busy[M={mtop}]"]) if f"mfma_busy[M={mtop}]" in cnt else None,
-                       "profile_clock_GHz": float(cnt[f"clock_GHz[M={mtop}]"]) if f"clock_GHz[M={mtop}]" in cnt else None}
-    # the same layer without residual (rho = 0): t(rho) / t(0)
+                       "profile_clock_GHz": float(cnt[f"clock_GHz[M={mtop}]"]) if f"clock_GHz[M={mtop}]" in cnt else None,
+                       "profile_kernel_avg_us": float(cnt[f"kernel_avg_us[M={mtop}]"]) if f"kernel_avg_us[M={mtop}]" in cnt else None,
+                       "profile_mfma_busy_rho0": float(cnt[f"mfma_busy_rw[M={mtop}]"]) if f"mfma_busy_rw[M={mtop}]" in cnt else None}
+    # the same layer without residual (rho = 0; the register-weight kernel):
+    # its time and TFLOP/s, and t(rho) / t(0)
     W = torch.from_numpy(layer.W()).cuda()
     p0 = mq.mq_pack(W, layer.group, 0.0)
     del W
     out["residual_overhead_t_rho_over_t0"] = {}
+    out["plain_w4"] = {}
     for M in wl.batch:
         X = torch.from_numpy(layer.X(M)).cuda()
         Y = torch.empty((M, layer.N), dtype=torch.float16, device="cuda")
@@ -356,6 +361,8 @@ def bench_prefill(args, mq, synth, torch):
         n = max(3, min(args.steps, 50))
         ms0 = time_events(run0, n) / n
         out["residual_overhead_t_rho_over_t0"][str(M)] = round(out["M"][str(M)]["us"] / (ms0 * 1e3), 3)
+        out["plain_w4"][str(M)] = {"us": round(ms0 * 1e3, 2),
+                                   "TFLOPs": round(2.0 * M * layer.N * layer.K / (ms0 * 1e-3) / 1e12, 1)}
     p0.free()
     # Context only: a dense fp16 GEMM of the same shape through torch.matmul
     # (the vendor BLAS), random weights. It shows what the matrix cores give a
@@ -910,6 +917,10 @@ def main():
     trace = profile_values("decode_kernel_stats.txt", DECODE_SOURCES)
     trace_us = float(trace[f"kernel_avg_us[{tag}]"]) if f"kernel_avg_us[{tag}]" in trace else None
     period_us = float(trace[f"launch_period_us[{tag}]"]) if f"launch_period_us[{tag}]" in trace else None
+    # the committed streaming-read ceiling for a buffer of this size (a plain
+    # read kernel): the kernel's rate on kernel time as a fraction of it
+    ceil = profile_values("stream_read_ceiling.txt", STREAM_SOURCES)
+    ceil_gbs = float(ceil["ceiling_GBps"]) if "ceiling_GBps" in ceil else None
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(d["ms_per_step"], 5),
@@ -925,7 +936,10 @@ def main():
                                    "(each on another packed copy) / launches = launch period, kernel + dispatch gap",
                      "profile_launch_period_us": period_us, "profile_kernel_avg_us": trace_us,
                      "frac_kernel_time": (round(dom["bytes"] / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
-                                          if trace_us else None)},
+                                          if trace_us else None),
+                     "streaming_ceiling_GBps": ceil_gbs,
+                     "frac_of_streaming_ceiling": (round(dom["bytes"] / (trace_us * 1e-6) / 1e9 / ceil_gbs, 4)
+                                                   if trace_us and ceil_gbs else None)},
         "decode_per_M": d["per_m"],
         "decode_residual_overhead_t_rho_over_t0": d["overhead"],
         "decode_unfused_two_kernels": d["unfused"],
