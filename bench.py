@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-extra", action="store_true",
                     help="skip the transformer-block, residual-sweep, block-residual, migration and W4A4 legs")
-    ap.add_argument("--only", choices=["decode", "prefill", "copy", "stream", "mid", "blocks", "migration", "w4a4"],
+    ap.add_argument("--only", choices=["decode", "prefill", "copy", "stream", "mid", "sweep", "blocks", "migration", "w4a4"],
                     default=None,
                     help="run one leg only (profiling runs); 'copy' runs the plain device copy that "
                          "calibrates the HBM byte counters; 'stream' times a plain streaming read of a "
@@ -893,6 +893,9 @@ def main():
         return
     if args.only == "mid":
         print(json.dumps({"mid_batch": bench_mid(args, mq, synth, torch)}), flush=True)
+        return
+    if args.only == "sweep":
+        print(json.dumps({"residual_sweep": bench_sweep(args, mq, synth, torch)}), flush=True)
         return
     if args.only == "blocks":
         print(json.dumps({"block_residual": bench_blocks(args, mq, synth, torch)}), flush=True)

@@ -40,7 +40,6 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 constexpr int BN = 256;               // output features per workgroup (16 row blocks)
 constexpr int BK = 64;                // K columns per LDS stage
 constexpr int LDW = BK + 8;           // LDS row (halves): 144 B, so 8 consecutive rows hit distinct banks
-constexpr int kBufferFlags = 0x00020000;   // buffer descriptor word 3: 32-bit data format, raw (unswizzled) addressing
 constexpr int kSplitTarget = 256;       // workgroups to aim for when K is split (one per CU)
 
 // Workgroup shape: a BN x BM_ output tile (features x tokens) computed by
@@ -341,7 +340,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void k_gemm(const uint4* __restrict
   const int lrb0 = RB * wave;                // local row blocks widened by this wave
   const int rbw = rb0 + lrb0;
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(X + (int64_t)m0 * K), 0, (int)(min(BM, M - m0) * K * 2), kBufferFlags);
+      const_cast<uint16_t*>(X + (int64_t)m0 * K), 0, (int)(min(BM, M - m0) * K * 2), kBufferRaw);
   const uint32_t xoff = (uint32_t)((tid >> 3) * K + 8 * (tid & 7)) * 2u;
   uint32_t vmask = 0x000F000Fu, vmask4 = 0x00F000F0u, vmagic = 0x64006400u;
   asm volatile("" : "+v"(vmask), "+v"(vmask4), "+v"(vmagic));   // keep the constants in VGPRs for v_and_or_b32

@@ -38,7 +38,6 @@ constexpr int kWavesM = 8;
 constexpr int kThreadsM = 64 * kWavesM;
 constexpr int kPlaneStrideM = 40;   // patch plane: halves per lane (80 B: 4 k-steps x 8, then 8 unused; 16 lanes
                                     // on distinct banks)
-constexpr int kBufferFlagsM = 0x00020000;   // buffer descriptor word 3: 32-bit data format, raw addressing
 constexpr int kXSlotBytes = 4096;           // per wave: one token block's X for one code tile (16 x 128 fp16)
 constexpr int kRingM = 2;   // register sets in a wave's load ring (deeper rings measured slower at every shape)
 
@@ -365,7 +364,7 @@ __global__ __launch_bounds__(kThreadsM, 1) void k_gemm_mid(const uint4* __restri
   // X through a buffer resource over the workgroup's token rows: rows past M
   // read as zero
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(X + (int64_t)m0 * K), 0, (int)(min(16 * NTB, M - m0) * K * 2), kBufferFlagsM);
+      const_cast<uint16_t*>(X + (int64_t)m0 * K), 0, (int)(min(16 * NTB, M - m0) * K * 2), kBufferRaw);
   uint32_t xoff[4], xpos[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {

@@ -90,7 +90,6 @@ __device__ __forceinline__ void w_load(WTile<GSH>& T, const WSrc& S, int64_t sst
 // l's 16 bytes landing at 16 l. The buffer resource spans the workgroup's
 // token rows; the whole byte offset (xl: the lane's part) goes into the
 // per-lane offset, which its range check covers, so rows past M read zero.
-constexpr int kBufferFlagsW = 0x00020000;   // buffer descriptor word 3: 32-bit data format, raw addressing
 __device__ __forceinline__ void x_copy(uint8_t* buf, __amdgpu_buffer_rsrc_t xr, const uint32_t (&xl)[4], int K,
                                        int kt, int wave) {
 #pragma unroll
@@ -159,7 +158,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void k_gemm_rw(const uint4* __restric
   const int m0 = mt * kBMW;
 
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(X + (int64_t)m0 * K), 0, (int)(min(kBMW, M - m0) * K * 2), kBufferFlagsW);
+      const_cast<uint16_t*>(X + (int64_t)m0 * K), 0, (int)(min(kBMW, M - m0) * K * 2), kBufferRaw);
   uint32_t xl[4], xpos[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -188,8 +187,8 @@ __global__ __launch_bounds__(kThreadsW, 1) void k_gemm_rw(const uint4* __restric
   // barrier publishes them and frees the buffer just read. One stage per
   // iteration, with no exit inside: the accumulators then stay in place.
   WSrc S;
-  S.tiles = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(tiles), 0, 0x7fffffff, kBufferFlagsW);
-  S.scales = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, 0x7fffffff, kBufferFlagsW);
+  S.tiles = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(tiles), 0, 0x7fffffff, kBufferRaw);
+  S.scales = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, 0x7fffffff, kBufferRaw);
   S.tl = 16u * (uint32_t)lane;
   S.sl = (uint32_t)(lane & 15) * (uint32_t)sstride * 2u;
   const int xwo = kTbWave * wm * kXBlock;   // the wave's token blocks in a stage buffer

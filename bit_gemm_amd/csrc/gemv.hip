@@ -344,20 +344,69 @@ __device__ __forceinline__ void res_tile(float4_t (&acc)[1], const ResTile& T, c
 // from LDS), then tiles 2 and 3, so the residual work overlaps the second
 // half of the stream. Partial 16 x 1 tiles are summed in LDS in a fixed
 // order.
-template <int GSH, int XR, bool DR>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 6 : 1, 8))) void k_gemv_x(
-    const uint4* __restrict__ tiles, const uint16_t* __restrict__ scales, int sstride,
-    const uint32_t* __restrict__ tile_ptr, const uint32_t* __restrict__ entries, const uint16_t* __restrict__ X,
-    uint16_t* __restrict__ Y, int M, int N, int zero_off, DenseRes D) {
+// RS > 0 (handles whose densest row block has more than 16 chunks): the
+// row block's chunks 16 .. 16 + RS - 1 are copied straight from global
+// memory into LDS after the code tiles, 8 chunks (1 KiB) per load
+// instruction, all in flight together; a row block far denser than the rest
+// (outliers clustered in a few rows) then waits one memory latency for its
+// residual instead of one per 4 chunks of each wave. The chunks are added in
+// the same order either way. Such a launch also starts the row blocks of
+// more than 16 chunks first: workgroups 0 .. n - 1 take the n row blocks the
+// handle lists (up to 64, with their stream offsets), and workgroup n + rb
+// takes row block rb unless that one is listed, in which case it ends at
+// once. The list and a bitmask of the workgroups that end are kernel
+// arguments indexed by the workgroup alone, so a workgroup learns its row
+// block from argument loads issued together with the others.
+constexpr int kRegChunks = 2 * kWaves;   // chunks of a row block held in registers by k_gemv_x
+static_assert(kRegChunks == kDenseRbChunks, "the dense list names the row blocks that stage chunks");
+constexpr int kDenseMaskWords = 256;     // bitmask of the workgroups that end at once: up to 8192 workgroups
+
+struct DenseList {
+  uint32_t n;                         // listed row blocks (0: one workgroup per row block, in order)
+  uint32_t rb[kDenseListMax];         // ascending
+  uint32_t e0[kDenseListMax];         // first stream entry of each
+  uint32_t nch[kDenseListMax];        // chunks of each
+  uint32_t mask[kDenseMaskWords];     // bit b: workgroup b ends at once (its row block is listed)
+};
+
+// One workgroup of k_gemv_x on row block rb. RS = 0: its stream offsets read
+// from tile_ptr, chunks past the first 16 through registers. RS > 0 and LST:
+// a row block from the dense list (le0, lnch: its stream), whose chunks past
+// the first 16 are staged in LDS, requested first; the listed and the other
+// row blocks take separate code paths of the kernel, so the plain one never
+// waits on a staging load. RS > 0 and !LST (every row block dense, too many
+// to list): the chunks are staged once the offsets have been read.
+template <int GSH, int XR, bool DR, int RS, bool LST>
+__device__ __forceinline__ void gemv_x_block(const uint4* __restrict__ tiles, const uint16_t* __restrict__ scales,
+                                             int sstride, const uint32_t* __restrict__ tile_ptr,
+                                             const uint32_t* __restrict__ entries, const uint16_t* __restrict__ X,
+                                             uint16_t* __restrict__ Y, int M, int N, int zero_off, const DenseRes& D,
+                                             uint16_t* xs, float4_t (*red)[64], uint8_t* stg, int rb, uint32_t le0,
+                                             uint32_t lnch) {
   constexpr int KS = 8, TPW = 4, K = 4096, Kt = 32, NS = 1 << GSH, LDX = K + kXPad;
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][LDX]
-  __shared__ float4_t red[KS][64];
-  const int rb = blockIdx.x;
+  static_assert(RS % (8 * KS) == 0 && (!DR || RS == 0), "staged chunks: whole load instructions per wave");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int kt0 = wave * TPW, c0 = kt0 * kTileCols, tbase = rb * Kt;
   int mrow[1];
   token_rows<1>(M, r, mrow);
+
+  // 0. (RS: a listed row block) chunks kRegChunks .. kRegChunks + nstg - 1
+  // into LDS, requested first: instruction i of the workgroup (issued by
+  // wave i mod 8) carries chunks 8 i .. 8 i + 7, lane l's 16 bytes landing at
+  // 16 l. The stream's zero pad covers the chunks read past the row block,
+  // which are never used.
+  uint32_t nstg = 0;
+  auto stage = [&](uint32_t e0, uint32_t nch) __attribute__((always_inline)) {
+    nstg = nch > (uint32_t)kRegChunks ? min(nch - (uint32_t)kRegChunks, (uint32_t)RS) : 0u;
+    const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(entries), 0, (int)((zero_off + kEntryPad) * 4), kBufferRaw);
+    const uint32_t ebase = (e0 + (uint32_t)(kChunk * kRegChunks)) * 4u + 16u * (uint32_t)lane;
+    for (uint32_t i = (uint32_t)wave; 8 * i < nstg; i += KS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void*)(stg + 1024 * i), 16,
+                                               ebase + 1024u * i, 0, 0, 0);
+  };
+  if constexpr (RS > 0 && LST) stage(le0, lnch);
 
   // 1. X slice (rows >= M repeat row 0, never stored) and scales (raw: the
   // rows past N are zeroed at use, after the loads have been issued)
@@ -417,8 +466,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
       load_res_tile(rt[j], D, c < nrt ? R0 + c : D.zero, lane, g);
     }
   } else {
-    E0 = tile_ptr[tbase];
-    nchunks = (tile_ptr[tbase + Kt] - E0) / (uint32_t)kChunk;
+    if constexpr (RS > 0 && LST) {   // its stream from the list
+      E0 = le0;
+      nchunks = lnch;
+    } else {
+      E0 = tile_ptr[tbase];
+      nchunks = (tile_ptr[tbase + Kt] - E0) / (uint32_t)kChunk;
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const uint32_t c = (uint32_t)(wave + j * KS);
@@ -433,6 +487,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
   __builtin_amdgcn_sched_barrier(0);
   code[2] = tp[128];
   code[3] = tp[192];
+  if constexpr (RS > 0 && !LST) stage(E0, nchunks);
 
   // X slices into LDS, published with a wait on LDS traffic only
   uint16_t* xdst = xs + c0 + 8 * lane;
@@ -488,8 +543,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
     }
     tile(2);
     tile(3);
-    res_rest<1, true, false, KS>(acc, entries, E0, (uint32_t)(wave + 2 * KS), nchunks, zero_off, tile_ptr + tbase, 1,
-                                 X, xs, mrow, K, LDX, r, g);
+    if constexpr (RS > 0) {
+      if (nstg > 0) {   // the same in every wave of the workgroup
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        // two chunks a round: both chunks' entries and X gathers are in
+        // flight together, and the MFMAs keep the chunk order
+        uint32_t c = (uint32_t)wave;
+        for (; c + KS < nstg; c += 2 * KS) {
+          const uint4* ep = reinterpret_cast<const uint4*>(stg + 128 * c + 32 * g);
+          const uint4* eq = reinterpret_cast<const uint4*>(stg + 128 * (c + KS) + 32 * g);
+          const uint4 a0 = ep[0], a1 = ep[1], b0 = eq[0], b1 = eq[1];
+          res_chunk<1, true, false>(acc, a0, a1, 0u, tile_ptr + tbase, 1, X, xs, mrow, K, LDX, r, g);
+          res_chunk<1, true, false>(acc, b0, b1, 0u, tile_ptr + tbase, 1, X, xs, mrow, K, LDX, r, g);
+        }
+        if (c < nstg) {
+          const uint4* ep = reinterpret_cast<const uint4*>(stg + 128 * c + 32 * g);
+          res_chunk<1, true, false>(acc, ep[0], ep[1], 0u, tile_ptr + tbase, 1, X, xs, mrow, K, LDX, r, g);
+        }
+      }
+    }
+    res_rest<1, true, false, KS>(acc, entries, E0, (uint32_t)(wave + kRegChunks + RS), nchunks, zero_off,
+                                 tile_ptr + tbase, 1, X, xs, mrow, K, LDX, r, g);
   }
 
   red[wave][lane] = acc[0];
@@ -500,6 +575,33 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
     for (int w = 1; w < KS; ++w) sum += red[w][lane];
     const int n0 = rb * kRowsPerBlock + 4 * g;
     if (r < M) store4(Y + (int64_t)r * N + n0, sum, N - n0, (N & 3) == 0);
+  }
+}
+
+template <int GSH, int XR, bool DR, int RS, bool LST>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 6 : GSH == 2 && RS > 0 ? 4 : 5, 8))) void k_gemv_x(
+    const uint4* __restrict__ tiles, const uint16_t* __restrict__ scales, int sstride,
+    const uint32_t* __restrict__ tile_ptr, const uint32_t* __restrict__ entries, const uint16_t* __restrict__ X,
+    uint16_t* __restrict__ Y, int M, int N, int zero_off, DenseRes D, DenseList L) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][4096 + kXPad]
+  __shared__ float4_t red[kWaves][64];
+  __shared__ __attribute__((aligned(16))) uint8_t stg[RS > 0 ? RS * kChunk * 4 : 16];   // staged chunks
+  if constexpr (RS == 0 || !LST) {
+    gemv_x_block<GSH, XR, DR, RS, false>(tiles, scales, sstride, tile_ptr, entries, X, Y, M, N, zero_off, D, xs, red,
+                                         stg, (int)blockIdx.x, 0u, 0u);
+  } else {
+    // the list's fields at clamped indices, without branches, so that their
+    // argument loads go out together
+    const uint32_t b = blockIdx.x, bq = min(b, (uint32_t)kDenseListMax - 1);
+    const uint32_t mw = L.mask[min(b >> 5, (uint32_t)kDenseMaskWords - 1)];
+    const uint32_t lrb = L.rb[bq], le0 = L.e0[bq], lnch = L.nch[bq];
+    if ((mw >> (b & 31)) & 1u) return;   // listed row block: taken by workgroup < n (the same in all waves)
+    if (b < L.n)
+      gemv_x_block<GSH, XR, false, RS, true>(tiles, scales, sstride, tile_ptr, entries, X, Y, M, N, zero_off, D, xs,
+                                             red, stg, (int)lrb, le0, lnch);
+    else
+      gemv_x_block<GSH, XR, false, 0, false>(tiles, scales, sstride, tile_ptr, entries, X, Y, M, N, zero_off, D, xs,
+                                             red, stg, (int)(b - L.n), 0u, 0u);
   }
 }
 
@@ -830,18 +932,56 @@ DenseRes dense_res(const mq_packed* p) {
   return DenseRes{p->rt_ptr, reinterpret_cast<const uint4*>(p->rt_tiles), p->bscale, p->blk, (uint32_t)p->nblk};
 }
 
-template <int GSH, int XR, bool DR>
+constexpr size_t kLdsMaxBytes = 160 * 1024;   // LDS of one CU
+
+// the handle's dense row blocks for a launch that takes them first
+DenseList dense_list(const mq_packed* p) {
+  DenseList L{};
+  if (p->ndense <= (uint32_t)kDenseListMax && p->Nb + p->ndense <= 32 * kDenseMaskWords) {
+    L.n = p->ndense;
+    for (uint32_t i = 0; i < L.n; ++i) {
+      L.rb[i] = p->dense_rb[i];
+      L.e0[i] = p->dense_e0[i];
+      L.nch[i] = p->dense_nch[i];
+      const uint32_t b = L.n + L.rb[i];   // the workgroup that would take it in order
+      L.mask[b >> 5] |= 1u << (b & 31);
+    }
+  }
+  return L;
+}
+
+// LST: the handle's dense row blocks go first, one workgroup more per listed
+// row block (whose in-order workgroup ends at once)
+template <int GSH, int XR, bool DR, int RS, bool LST>
 hipError_t launch_x(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
+  // dynamic LDS: X (the partials and the staged chunks are static)
+  constexpr size_t lds = (size_t)XR * (4096 + kXPad) * 2;
   static bool done = false;
-  const hipError_t e = allow_lds(&k_gemv_x<GSH, XR, DR>, done);
-  if (e != hipSuccess) return e;
-  k_gemv_x<GSH, XR, DR><<<dim3((unsigned)p->Nb), dim3(512), (size_t)XR * (4096 + kXPad) * 2, s>>>(
+  if (!done) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_x<GSH, XR, DR, RS, LST>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    done = true;
+  }
+  const DenseList L = LST ? dense_list(p) : DenseList{};
+  k_gemv_x<GSH, XR, DR, RS, LST><<<dim3((unsigned)(p->Nb + L.n)), dim3(512), lds, s>>>(
       reinterpret_cast<const uint4*>(p->tiles), p->scales, (int)p->sstride, p->tile_ptr, p->entries, X, Y, M,
-      (int)p->N, (int)p->stream_cap, dense_res(p));
+      (int)p->N, (int)p->stream_cap, dense_res(p), L);
   return hipGetLastError();
 }
 
-constexpr size_t kLdsMaxBytes = 160 * 1024;   // LDS of one CU
+// Element-wise residual: LDS staging sized to the densest row block
+// (beyond 16 + 256 chunks the rest goes through registers as below 16),
+// the dense row blocks first when the handle lists them.
+template <int GSH, int XR>
+hipError_t launch_x_res(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
+  const uint32_t mc = p->max_rb / (uint32_t)kChunk;
+  if (mc <= (uint32_t)kRegChunks) return launch_x<GSH, XR, false, 0, false>(p, X, M, Y, s);
+  const bool lst = dense_list(p).n > 0;
+  if (mc <= (uint32_t)kRegChunks + 64)
+    return lst ? launch_x<GSH, XR, false, 64, true>(p, X, M, Y, s) : launch_x<GSH, XR, false, 64, false>(p, X, M, Y, s);
+  return lst ? launch_x<GSH, XR, false, 256, true>(p, X, M, Y, s) : launch_x<GSH, XR, false, 256, false>(p, X, M, Y, s);
+}
 
 template <int GSH, int XR, int R, bool DR>
 hipError_t launch_r(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
@@ -916,13 +1056,13 @@ hipError_t run(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStr
   if constexpr (MB == 1) {
     if (p->K == 4096 && M <= 4) {   // fast kernel: X slices in LDS, residual amid the tiles
       if (p->blocks) {   // the block residual as code tiles
-        if (M == 1) return launch_x<GSH, 1, true>(p, X, M, Y, s);
-        if (M == 2) return launch_x<GSH, 2, true>(p, X, M, Y, s);
-        return launch_x<GSH, 4, true>(p, X, M, Y, s);
+        if (M == 1) return launch_x<GSH, 1, true, 0, false>(p, X, M, Y, s);
+        if (M == 2) return launch_x<GSH, 2, true, 0, false>(p, X, M, Y, s);
+        return launch_x<GSH, 4, true, 0, false>(p, X, M, Y, s);
       }
-      if (M == 1) return launch_x<GSH, 1, false>(p, X, M, Y, s);
-      if (M == 2) return launch_x<GSH, 2, false>(p, X, M, Y, s);
-      return launch_x<GSH, 4, false>(p, X, M, Y, s);
+      if (M == 1) return launch_x_res<GSH, 1>(p, X, M, Y, s);
+      if (M == 2) return launch_x_res<GSH, 2>(p, X, M, Y, s);
+      return launch_x_res<GSH, 4>(p, X, M, Y, s);
     }
     if (p->K == 4096) {   // 5..16 tokens: X whole in LDS, several row blocks per workgroup
       if (p->blocks) {

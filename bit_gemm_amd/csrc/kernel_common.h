@@ -10,6 +10,10 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// Buffer descriptor word 3 for raw (unswizzled) byte addressing with a 32-bit
+// data format: loads past the descriptor's byte range return zero.
+constexpr int kBufferRaw = 0x00020000;
+
 // D = (a & m) | o, one v_and_or_b32 when m and o already sit in VGPRs (a
 // VOP3 instruction on this target takes at most one scalar operand). Plain C
 // rather than inline asm: the compiler's hazard checks do not see into an asm

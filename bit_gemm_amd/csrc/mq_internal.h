@@ -17,6 +17,8 @@ constexpr int kTileBytes = 1024;    // 16 rows x 128 columns x 4 bits
 constexpr int kColWindow = 4096;    // residual entries store column mod 4096
 constexpr int kEntryPad = 1024;     // zero entries after the residual stream (read-ahead slack)
 constexpr int kChunk = 32;          // residual entries per MFMA chunk; row-block segments are padded to it
+constexpr int kDenseRbChunks = 16;  // row blocks with more chunks lead the dense-first decode order
+constexpr int kDenseListMax = 64;   // dense row blocks a handle lists for the decode launch
 constexpr uint32_t kPatchValid = 0x800u;   // bit 11 of a patched-weight entry (stream padding is 0)
 
 struct Packed;  // layout of mq_packed (the opaque handle)
@@ -27,6 +29,8 @@ struct SelState {
   uint64_t krem;     // entries still to take among keys equal to the current prefix
   uint32_t flags;    // kFlag* bits raised by the kernels
   uint32_t max_seg;  // the longest per-tile segment of the residual stream (entries, padding included)
+  uint32_t max_rb;   // the longest row-block segment of the residual stream (entries, padding included)
+  uint32_t ndense;   // row blocks with more than kDenseRbChunks chunks of the stream
 };
 constexpr uint32_t kFlagNonFinite = 1u;
 constexpr uint32_t kFlagScaleOverflow = 2u;
@@ -60,6 +64,7 @@ struct mq_packed {
   uint32_t* tile_ptr;   // [Nb*Kt + 1] (element-wise handles)
   uint32_t* entries;    // [nstream + kEntryPad]: residual stream, row blocks padded to 32 entries (element-wise)
   uint32_t max_seg;     // the longest per-tile segment of the stream (entries, padding included)
+  uint32_t max_rb;      // the longest row-block segment of the stream (entries, padding included)
   uint32_t* wpatch;     // [nstream + kEntryPad]: the same entries as patches of the GEMM kernels' widened
                         // weights: bits 0-6 column mod 128, 11 valid, 12-15 row mod 16, 16-31
                         // fp16(s q + fp16(sr qr)) XOR fp16(s q); element-wise handles only
@@ -75,6 +80,12 @@ struct mq_packed {
   uint8_t* rt_tiles;    // [nblk + 1][1 KiB]: the blocks' codes in the code-tile layout; slot nblk
                         // (like blk[nblk] = 0 and bscale[nblk][*] = 0) is an all-zero residual
   int32_t* rt_slot;     // [Nb * Kt]: the residual slot of each tile (nblk where it has none)
+  // the row blocks with more than mq::kDenseRbChunks chunks of the stream, ascending (element-wise
+  // handles; ndense > mq::kDenseListMax: too many to list, the decode launch keeps the plain order)
+  uint32_t ndense;
+  uint32_t dense_rb[mq::kDenseListMax];
+  uint32_t dense_e0[mq::kDenseListMax];    // their first stream entries
+  uint32_t dense_nch[mq::kDenseListMax];   // their chunks
 };
 
 namespace mq {
@@ -93,7 +104,8 @@ hipError_t pack_blocks_on_device(const uint16_t* W, const float* h, mq_packed* p
 
 // Pieces of the element-wise pipeline the block packer reuses (pack.hip).
 hipError_t launch_pack_base(const uint16_t* W, mq_packed* p, SelState* st, hipStream_t stream);
-hipError_t launch_scan_tiles(const uint32_t* tile_cnt, int64_t ntiles, uint32_t* tile_ptr, SelState* st,
+hipError_t launch_scan_tiles(const uint32_t* tile_cnt, int64_t ntiles, int64_t Kt, uint32_t* tile_ptr,
+                             uint32_t* dense_rb, SelState* st,
                              hipStream_t stream);
 
 // Outlier migration (migrate.hip): e_j and W^ = W 2^e (W_out may be W);

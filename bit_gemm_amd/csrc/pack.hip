@@ -303,9 +303,16 @@ __global__ __launch_bounds__(kWave) void k_row_select(const uint16_t* __restrict
 }
 
 // One block of 1024 threads: exclusive scan of the per-tile entry counts,
-// and their maximum into st->max_seg.
-__global__ __launch_bounds__(1024) void k_scan_tiles(const uint32_t* __restrict__ tile_cnt, int64_t ntiles,
-                                                     uint32_t* __restrict__ tile_ptr, SelState* st) {
+// their maximum into st->max_seg, the longest row block (Kt tiles) into
+// st->max_rb, and the row blocks of more than kDenseRbChunks chunks: their
+// count into st->ndense and (dense_rb not null) the first kDenseListMax of
+// them, ascending, into dense_rb[0 .. 64), with their first stream entry
+// and chunk count in dense_rb[64 ..) and dense_rb[128 ..). A decode launch
+// that takes these row blocks first, knowing their streams without a load,
+// starts its slowest workgroups in its first round.
+__global__ __launch_bounds__(1024) void k_scan_tiles(const uint32_t* __restrict__ tile_cnt, int64_t ntiles, int64_t Kt,
+                                                     uint32_t* __restrict__ tile_ptr,
+                                                     uint32_t* __restrict__ dense_rb, SelState* st) {
   __shared__ uint64_t wave_tot[16];
   __shared__ uint64_t tot;
   __shared__ uint32_t seg_max;
@@ -324,10 +331,47 @@ __global__ __launch_bounds__(1024) void k_scan_tiles(const uint32_t* __restrict_
     __syncthreads();
   }
   atomicMax(&seg_max, mx);
+  if (threadIdx.x == 0) tile_ptr[ntiles] = (uint32_t)carry;
+  __syncthreads();   // the block's tile_ptr writes are visible to all its threads
+  __shared__ uint32_t rb_max;
+  if (threadIdx.x == 0) rb_max = 0u;
   __syncthreads();
+  __shared__ uint32_t ndense;
+  if (threadIdx.x == 0) ndense = 0u;
+  __syncthreads();
+  const int64_t Nb = ntiles / Kt;
+  auto dense = [&](int64_t rb) { return tile_ptr[(rb + 1) * Kt] - tile_ptr[rb * Kt] > (uint32_t)(kChunk * kDenseRbChunks); };
+  uint32_t rmx = 0u, nd = 0u;
+  for (int64_t rb = threadIdx.x; rb < Nb; rb += blockDim.x) {
+    rmx = max(rmx, tile_ptr[(rb + 1) * Kt] - tile_ptr[rb * Kt]);
+    nd += dense(rb) ? 1u : 0u;
+  }
+  atomicMax(&rb_max, rmx);
+  atomicAdd(&ndense, nd);
+  __syncthreads();
+  if (dense_rb) {
+    uint64_t before = 0;   // dense row blocks ahead of this tile of row blocks
+    for (int64_t base = 0; base < Nb && before < (uint64_t)kDenseListMax; base += blockDim.x) {
+      const int64_t rb = base + threadIdx.x;
+      const uint64_t f = (rb < Nb && dense(rb)) ? 1u : 0u;
+      const uint64_t incl = block_scan_incl(f, wave_tot);
+      const uint64_t d = before + incl - f;   // dense row blocks before rb
+      if (f && d < (uint64_t)kDenseListMax) {
+        const uint32_t e0 = tile_ptr[rb * Kt];
+        dense_rb[d] = (uint32_t)rb;
+        dense_rb[kDenseListMax + d] = e0;
+        dense_rb[2 * kDenseListMax + d] = (tile_ptr[(rb + 1) * Kt] - e0) / (uint32_t)kChunk;
+      }
+      if (threadIdx.x == blockDim.x - 1) tot = incl;
+      __syncthreads();
+      before += tot;
+      __syncthreads();
+    }
+  }
   if (threadIdx.x == 0) {
-    tile_ptr[ntiles] = (uint32_t)carry;
     st->max_seg = seg_max;
+    st->max_rb = rb_max;
+    st->ndense = ndense;
   }
 }
 
@@ -475,7 +519,8 @@ hipError_t pack_on_device(const uint16_t* W, mq_packed* p, hipStream_t stream, u
   const int N = (int)p->N, K = (int)p->K, G = p->G;
   const int Kt = (int)p->Kt, Nb = (int)p->Nb;
   const int64_t ntiles = (int64_t)Nb * Kt;
-  Temp t_state, t_hist, t_gt, t_eq, t_eb, t_rt, t_tc;
+  Temp t_state, t_hist, t_gt, t_eq, t_eb, t_rt, t_tc, t_dense;
+  uint32_t* dense = nullptr;   // the dense row blocks (set when the stream is built)
   MQ_TRY(hipMalloc(&t_state.p, sizeof(SelState)));
   SelState* st = static_cast<SelState*>(t_state.p);
   SelState init{0ull, (uint64_t)p->nnz, 0u, 0u};
@@ -522,7 +567,9 @@ hipError_t pack_on_device(const uint16_t* W, mq_packed* p, hipStream_t stream, u
     k_row_select<<<dim3(Nb), dim3(kWave), 0, stream>>>(W, p->scales, N, K, G, Kt, p->sstride, st, eb, p->rscale,
                                                        crt, tcnt);
     MQ_TRY(hipGetLastError());
-    k_scan_tiles<<<dim3(1), dim3(1024), 0, stream>>>(tcnt, ntiles, p->tile_ptr, st);
+    MQ_TRY(hipMalloc(&t_dense.p, 3 * kDenseListMax * sizeof(uint32_t)));
+    dense = static_cast<uint32_t*>(t_dense.p);
+    k_scan_tiles<<<dim3(1), dim3(1024), 0, stream>>>(tcnt, ntiles, p->Kt, p->tile_ptr, dense, st);
     MQ_TRY(hipGetLastError());
     k_row_emit<<<dim3(Nb), dim3(kWave), 0, stream>>>(W, p->scales, N, K, G, Kt, p->sstride, st, eb, p->row_ptr,
                                                      p->rscale, crt, p->tile_ptr, p->tiles, p->col,
@@ -535,10 +582,22 @@ hipError_t pack_on_device(const uint16_t* W, mq_packed* p, hipStream_t stream, u
   uint32_t nstream = 0;
   MQ_TRY(hipMemcpyAsync(&fin, st, sizeof(fin), hipMemcpyDeviceToHost, stream));
   MQ_TRY(hipMemcpyAsync(&nstream, p->tile_ptr + ntiles, sizeof(nstream), hipMemcpyDeviceToHost, stream));
+  p->ndense = 0;
+  if (dense) {
+    MQ_TRY(hipStreamSynchronize(stream));
+    p->ndense = fin.ndense;
+    if (fin.ndense > 0 && fin.ndense <= (uint32_t)kDenseListMax) {
+      uint32_t* dst[3] = {p->dense_rb, p->dense_e0, p->dense_nch};
+      for (int a = 0; a < 3; ++a)
+        MQ_TRY(hipMemcpyAsync(dst[a], dense + a * kDenseListMax, fin.ndense * sizeof(uint32_t),
+                              hipMemcpyDeviceToHost, stream));
+    }
+  }
   MQ_TRY(hipStreamSynchronize(stream));
   *flags_out = fin.flags;
   p->nstream = nstream;
   p->max_seg = fin.max_seg;
+  p->max_rb = fin.max_rb;
   if ((int64_t)nstream > p->stream_cap) *flags_out |= kFlagCountMismatch;
   return hipSuccess;
 }
@@ -550,9 +609,9 @@ hipError_t launch_pack_base(const uint16_t* W, mq_packed* p, SelState* st, hipSt
   return hipGetLastError();
 }
 
-hipError_t launch_scan_tiles(const uint32_t* tile_cnt, int64_t ntiles, uint32_t* tile_ptr, SelState* st,
-                             hipStream_t stream) {
-  k_scan_tiles<<<dim3(1), dim3(1024), 0, stream>>>(tile_cnt, ntiles, tile_ptr, st);
+hipError_t launch_scan_tiles(const uint32_t* tile_cnt, int64_t ntiles, int64_t Kt, uint32_t* tile_ptr,
+                             uint32_t* dense_rb, SelState* st, hipStream_t stream) {
+  k_scan_tiles<<<dim3(1), dim3(1024), 0, stream>>>(tile_cnt, ntiles, Kt, tile_ptr, dense_rb, st);
   return hipGetLastError();
 }
 

@@ -48,7 +48,6 @@ typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kBn = 256;                 // output features per workgroup (16 row blocks)
 constexpr int kLdsRow = 144;             // bytes per staged token row: 128 + 16, so 8 rows hit distinct banks
-constexpr int kBufferFlags = 0x00020000;   // buffer descriptor word 3: 32-bit data format, raw addressing
 constexpr int kSplitTarget = 256;        // workgroups to aim for when K is split
 constexpr int kE8m0One = 127;            // MFMA block scale 2^0
 constexpr uint32_t kNibbleBytes = 0x0F0F0F0Fu;
@@ -169,10 +168,10 @@ struct WSrc {
 };
 __device__ __forceinline__ WSrc make_wsrc(const WArrays& a) {
   WSrc s;
-  s.tiles = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.tiles), 0, a.tiles_b, kBufferFlags);
-  s.scales = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.scales), 0, a.scales_b, kBufferFlags);
-  s.rtiles = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.rtiles), 0, a.rtiles_b, kBufferFlags);
-  s.rscale = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.rscale), 0, a.rscale_b, kBufferFlags);
+  s.tiles = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.tiles), 0, a.tiles_b, kBufferRaw);
+  s.scales = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.scales), 0, a.scales_b, kBufferRaw);
+  s.rtiles = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.rtiles), 0, a.rtiles_b, kBufferRaw);
+  s.rscale = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.rscale), 0, a.rscale_b, kBufferRaw);
   s.sstride_b = a.sstride_b;
   return s;
 }
@@ -438,9 +437,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void k_gemm_a4(WArrays 
   const uint32_t vcode = 16u * (uint32_t)lane, vscale = (uint32_t)(lane & 15) * src.sstride_b,
                  vrs = 4u * (uint32_t)(lane & 15);
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(xq + (int64_t)m0 * Kp), 0, rows * Kp, kBufferFlags);
+      const_cast<uint8_t*>(xq + (int64_t)m0 * Kp), 0, rows * Kp, kBufferRaw);
   const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(xmeta + (int64_t)m0 * ngt), 0, rows * ngt * 4, kBufferFlags);
+      const_cast<uint32_t*>(xmeta + (int64_t)m0 * ngt), 0, rows * ngt * 4, kBufferRaw);
 
   float4_t acc[MS][RB];
 #pragma unroll
@@ -619,9 +618,9 @@ __global__ __launch_bounds__(512) void k_gemv_a4(WArrays warr, const uint8_t* __
   const int Kp = Kt * kTileCols, ngt = Kt * NG;
   // tokens past M read as zero codes and zero metadata
   const __amdgpu_buffer_rsrc_t xrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(xq), 0, M * Kp, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(xq), 0, M * Kp, kBufferRaw);
   const __amdgpu_buffer_rsrc_t mrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(xmeta), 0, M * ngt * 4, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(xmeta), 0, M * ngt * 4, kBufferRaw);
   const uint32_t vcode = 16u * (uint32_t)lane, vscale = (uint32_t)r * src.sstride_b, vrs = 4u * (uint32_t)r;
   const uint32_t va = (uint32_t)(r * Kp + 32 * g);
 

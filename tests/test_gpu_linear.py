@@ -131,6 +131,49 @@ def _longest_segment(ref, N, K):
     return int(cnt.max())
 
 
+def _longest_row_block(ref, N):
+    """Entries in the longest row-block segment of the residual stream (each
+    row block padded to whole 32-entry chunks), from the oracle's CSR."""
+    rp = ref["row_ptr"].astype(np.int64)
+    Nb = -(-N // 16)
+    per_row = np.zeros(Nb * 16, dtype=np.int64)
+    per_row[:N] = np.diff(rp)
+    blk = per_row.reshape(Nb, 16).sum(1)
+    return int((blk + (-blk) % 32).max())
+
+
+@pytest.mark.parametrize("N,rows,nnz,staged",
+                         [(64, (20,), 2400, 64), (64, (20, 40, 41, 42), 16000, 256), (1088, (), 68 * 3277, 256)])
+def test_decode_dense_row_blocks(mq, N, rows, nnz, staged):
+    """Outliers in whole rows make a few row blocks far denser than the rest;
+    the up-to-4-token decode kernel then copies a row block's chunks past the
+    16 it holds in registers into LDS, 64 or 256 of them sized to the densest
+    row block, takes any further ones through registers again, and starts the
+    dense row blocks first when there are at most 64 of them. The densities
+    put the densest row block at 75 and 364 chunks; the last case makes all
+    68 row blocks dense (about 100 chunks each), too many to list."""
+    K, G = 4096, 128
+    rng = np.random.default_rng(61)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[list(rows)] *= 20
+    W = W.astype(np.float16)
+    rho = nnz / (N * K)   # exact: a multiple of 2^-16
+    ref = oracle.pack(W, G, rho)
+    chunks = _longest_row_block(ref, N) // 32
+    assert chunks > 16 and (16 + 64 >= chunks) == (staged == 64), chunks
+    assert staged == 64 or chunks > 16 + 256 or not rows, chunks
+    p = mq.mq_pack(to_dev(W), G, rho)
+    assert p.nnz == nnz
+    Wt = oracle.dequant(ref)
+    for M in (1, 2, 3, 4, 16):
+        X = _x(M, K, seed=200 + M)
+        print(f"[dense row blocks] N={N} chunks={chunks} M={M}", flush=True)
+        Y = mq.mq_linear_with(to_dev(X), p, mq.KERNEL_GEMV).cpu().numpy()
+        check_linear(Y, X, Wt, f"dense row block {chunks} chunks M={M}")
+        Y2 = mq.mq_linear_with(to_dev(X), p, mq.KERNEL_GEMV).cpu().numpy()
+        assert np.array_equal(Y.view(np.uint16), Y2.view(np.uint16))
+
+
 @pytest.mark.parametrize("nnz,bucket", [(200, 1), (440, 2), (640, 3), (1100, 4)])
 def test_mid_kernel_patch_segment_lengths(mq, nnz, bucket):
     """The mid-size kernel applies a tile's element-wise patches branch-free
