@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-extra", action="store_true",
                     help="skip the transformer-block, residual-sweep, block-residual, migration and W4A4 legs")
-    ap.add_argument("--only", choices=["decode", "prefill", "copy", "stream", "mid", "sweep", "blocks", "migration", "w4a4"],
+    ap.add_argument("--only", choices=["decode", "prefill", "copy", "stream", "mid", "tblock", "sweep", "blocks", "migration", "w4a4"],
                     default=None,
                     help="run one leg only (profiling runs); 'copy' runs the plain device copy that "
                          "calibrates the HBM byte counters; 'stream' times a plain streaming read of a "
@@ -413,13 +413,43 @@ def bench_block(args, mq, synth, torch):
             mq.mq_linear(x, p, y)
     med, p10, p90 = replay_spread(torch, step, max(2, args.warmup // 4), max(10, args.steps // 4))
     nbytes = sum(p.canonical_bytes() + 2 * M * p.K + 2 * M * p.N for p in first)
+    # The same packed layers with the ones that read the same input joined
+    # by mq_concat (q, k, v; and gate, up, or not): fewer launches per step,
+    # each group reading its input once. Every layer keeps its own packing.
+    names = [layer.name for layer in wl.layers]
+    joined = {}
+    for groups in ([["q", "k", "v"], ["o"], ["gate", "up"], ["down"]],
+                   [["q", "k", "v"], ["o"], ["gate"], ["up"], ["down"]]):
+        fused = []
+        for c in copies:
+            fused.append([mq.mq_concat([c[names.index(n)] for n in g]) if len(g) > 1 else None for g in groups])
+        Xg = [Xs[names.index(g[0])] for g in groups]
+        Yg = [torch.empty((M, sum(wl.layers[names.index(n)].N for n in g)), dtype=torch.float16, device="cuda")
+              for g in groups]
+
+        def step_fused(i, groups=groups, fused=fused, Xg=Xg, Yg=Yg):
+            c, fc = copies[i % ncopy], fused[i % ncopy]
+            for gi, g in enumerate(groups):
+                mq.mq_linear(Xg[gi], fc[gi] if fc[gi] is not None else c[names.index(g[0])], Yg[gi])
+        fmed, fp10, fp90 = replay_spread(torch, step_fused, max(2, args.warmup // 4), max(10, args.steps // 4))
+        fbytes = sum(p.canonical_bytes() + 2 * M * p.N for p in first) + sum(
+            2 * M * wl.layers[names.index(g[0])].K for g in groups)
+        for fc in fused:
+            for p in fc:
+                if p is not None:
+                    p.free()
+        joined[" ".join("+".join(g) for g in groups)] = {
+            "launches_per_step": len(groups), "us": round(fmed * 1e3, 2), "p10_us": round(fp10 * 1e3, 2),
+            "p90_us": round(fp90 * 1e3, 2), "GBps": round(fbytes / (fmed * 1e-3) / 1e9, 1),
+            "frac_hbm": round(fbytes / (fmed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": fbytes,
+            "speedup_vs_separate": round(med / fmed, 3)}
     for c in copies:
         for p in c:
             p.free()
     return {"workload": wl.name, "M": M, "launches_per_step": len(wl.layers), "packed_copies": ncopy,
             "us": round(med * 1e3, 2), "p10_us": round(p10 * 1e3, 2), "p90_us": round(p90 * 1e3, 2),
             "GBps": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes": nbytes}
+            "bytes": nbytes, "shared_input_joined": joined}
 
 
 def bench_sweep(args, mq, synth, torch):
@@ -893,6 +923,9 @@ def main():
         return
     if args.only == "mid":
         print(json.dumps({"mid_batch": bench_mid(args, mq, synth, torch)}), flush=True)
+        return
+    if args.only == "tblock":
+        print(json.dumps({"block_4096h_m16": bench_block(args, mq, synth, torch)}), flush=True)
         return
     if args.only == "sweep":
         print(json.dumps({"residual_sweep": bench_sweep(args, mq, synth, torch)}), flush=True)

@@ -2,6 +2,7 @@
 // dispatch to the HIP kernels. No kernel code lives here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -330,6 +331,170 @@ MQ_API mq_status mq_linear_noalloc(const void* X_dev_fp16, int64_t M, const mq_p
   if (mq::auto_gemv(p, M)) return from_hip(mq::launch_gemv(p, X, M, Y, s));   // no workspace on this path
   if (mq::gemm_workspace_bytes(p, M) > mq::gemm_scratch_capacity()) return MQ_ERR_UNSUPPORTED;
   return from_hip(mq::launch_gemm_noalloc(p, X, M, Y, s));
+}
+
+// Row-wise concatenation of element-wise (or residual-free) handles; see
+// include/mosaicq.h. Setup-time host code: the large arrays are copied device
+// to device, the three whose values or nibble positions shift (row and tile
+// pointers, residual codes) pass through host memory.
+MQ_API mq_status mq_concat(const mq_packed* const* parts, int32_t n, void* hip_stream, mq_packed** out) {
+  if (out) *out = nullptr;
+  if (!parts || !out || n < 1) return MQ_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    if (!is_live(parts[i])) return MQ_ERR_BAD_HANDLE;
+  const mq_packed* p0 = parts[0];
+  int64_t N = 0, nnz = 0, nstream = 0;
+  uint32_t max_seg = 0, max_rb = 0;
+  uint64_t ndense = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const mq_packed* q = parts[i];
+    if (q->blocks) return MQ_ERR_UNSUPPORTED;
+    if (q->K != p0->K || q->G != p0->G || q->device != p0->device) return MQ_ERR_INVALID_ARG;
+    // every part but the last fills its last row block, so output row r of
+    // a part stays row r of its row blocks
+    if (i + 1 < n && q->N % mq::kRowsPerBlock != 0) return MQ_ERR_INVALID_ARG;
+    N += q->N;
+    nnz += q->nnz;
+    nstream += q->nstream;
+    max_seg = std::max(max_seg, q->max_seg);
+    max_rb = std::max(max_rb, q->max_rb);
+    ndense += q->ndense;
+  }
+  const int64_t K = p0->K;
+  if (N >= (int64_t(1) << 31) / K || nstream + mq::kEntryPad >= (int64_t(1) << 31)) return MQ_ERR_UNSUPPORTED;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MQ_ERR_DEVICE;
+  if (dev != p0->device) return MQ_ERR_INVALID_ARG;
+
+  mq_packed* p = new (std::nothrow) mq_packed();
+  if (!p) return MQ_ERR_OUT_OF_MEMORY;
+  std::memset(p, 0, sizeof(*p));
+  p->N = N;
+  p->K = K;
+  p->G = p0->G;
+  p->rho = (double)nnz / ((double)N * (double)K);
+  p->nnz = nnz;
+  p->Nb = ceil_div(N, mq::kRowsPerBlock);
+  p->Kt = p0->Kt;
+  p->sstride = p0->sstride;
+  p->device = dev;
+  p->max_seg = max_seg;
+  p->max_rb = max_rb;
+  p->nstream = nstream;
+  p->stream_cap = nstream;   // the zero entries the kernels read past a segment start here
+  const int64_t Kt = p->Kt;
+  const size_t n_tiles = (size_t)(p->Nb * Kt);
+  const size_t sz_rcodes = (size_t)round_up((nnz + 1) / 2 + 1, 4);
+  const size_t sz_ent = (size_t)(nstream + mq::kEntryPad) * sizeof(uint32_t);
+  struct {
+    void** dst;
+    size_t n;
+  } allocs[] = {{(void**)&p->tiles, n_tiles * mq::kTileBytes},
+                {(void**)&p->scales, (size_t)(p->Nb * mq::kRowsPerBlock * p->sstride) * sizeof(uint16_t)},
+                {(void**)&p->row_ptr, (size_t)(N + 1) * sizeof(int32_t)},
+                {(void**)&p->col, (size_t)std::max<int64_t>(nnz, 1) * sizeof(uint16_t)},
+                {(void**)&p->rcodes, sz_rcodes},
+                {(void**)&p->rscale, (size_t)N * sizeof(float)},
+                {(void**)&p->tile_ptr, (n_tiles + 1) * sizeof(uint32_t)},
+                {(void**)&p->entries, sz_ent},
+                {(void**)&p->wpatch, sz_ent}};
+  size_t total = 0;
+  for (auto& a : allocs) {
+    const hipError_t e = hipMalloc(a.dst, a.n);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      release(p);
+      return e == hipErrorOutOfMemory ? MQ_ERR_OUT_OF_MEMORY : MQ_ERR_DEVICE;
+    }
+    total += a.n;
+  }
+  p->bytes = total;
+
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  // host images of the shifted arrays
+  int32_t* row_ptr = static_cast<int32_t*>(std::malloc((size_t)(N + 1) * sizeof(int32_t)));
+  uint32_t* tile_ptr = static_cast<uint32_t*>(std::malloc((n_tiles + 1) * sizeof(uint32_t)));
+  uint8_t* rcodes = static_cast<uint8_t*>(std::calloc(sz_rcodes, 1));
+  size_t part_max = 1;
+  for (int32_t i = 0; i < n; ++i)
+    part_max = std::max({part_max, (size_t)(parts[i]->N + 1) * 4, (size_t)(parts[i]->Nb * Kt + 1) * 4,
+                         (size_t)(parts[i]->nnz + 1) / 2 + 1});
+  uint8_t* tmp = static_cast<uint8_t*>(std::malloc(part_max));
+  hipError_t e = (row_ptr && tile_ptr && rcodes && tmp) ? hipSuccess : hipErrorOutOfMemory;
+  if (e == hipSuccess) e = hipMemsetAsync(p->entries, 0, sz_ent, s);
+  if (e == hipSuccess) e = hipMemsetAsync(p->wpatch, 0, sz_ent, s);
+  int64_t rbo = 0, eo = 0, so = 0;
+  for (int32_t i = 0; i < n && e == hipSuccess; ++i) {
+    const mq_packed* q = parts[i];
+    const int64_t ro = rbo * mq::kRowsPerBlock;
+    e = hipMemcpyAsync(p->tiles + (size_t)(rbo * Kt) * mq::kTileBytes, q->tiles,
+                       (size_t)(q->Nb * Kt) * mq::kTileBytes, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(p->scales + (size_t)(ro * p->sstride), q->scales,
+                         (size_t)(q->Nb * mq::kRowsPerBlock * q->sstride) * sizeof(uint16_t), hipMemcpyDeviceToDevice,
+                         s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(p->rscale + ro, q->rscale, (size_t)q->N * sizeof(float), hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && q->nnz > 0)
+      e = hipMemcpyAsync(p->col + eo, q->col, (size_t)q->nnz * sizeof(uint16_t), hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && q->nstream > 0)
+      e = hipMemcpyAsync(p->entries + so, q->entries, (size_t)q->nstream * 4, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && q->nstream > 0)
+      e = hipMemcpyAsync(p->wpatch + so, q->wpatch, (size_t)q->nstream * 4, hipMemcpyDeviceToDevice, s);
+    // row pointers and tile pointers, shifted by the entries before this part
+    if (e == hipSuccess) e = hipMemcpyAsync(tmp, q->row_ptr, (size_t)(q->N + 1) * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) {
+      const int32_t* rp = reinterpret_cast<const int32_t*>(tmp);
+      for (int64_t r = 0; r <= q->N; ++r) row_ptr[ro + r] = rp[r] + (int32_t)eo;
+      e = hipMemcpyAsync(tmp, q->tile_ptr, (size_t)(q->Nb * Kt + 1) * 4, hipMemcpyDeviceToHost, s);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) {
+      const uint32_t* tp = reinterpret_cast<const uint32_t*>(tmp);
+      for (int64_t t = 0; t <= q->Nb * Kt; ++t) tile_ptr[rbo * Kt + t] = tp[t] + (uint32_t)so;
+      if (q->nnz > 0) e = hipMemcpyAsync(tmp, q->rcodes, (size_t)(q->nnz + 1) / 2, hipMemcpyDeviceToHost, s);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) {   // entry t of the part is entry eo + t here: nibble (eo + t) & 1 of byte (eo + t) / 2
+      for (int64_t t = 0; t < q->nnz; ++t) {
+        const uint32_t u = (tmp[t >> 1] >> (4 * (t & 1))) & 0xFu;
+        rcodes[(eo + t) >> 1] |= (uint8_t)(u << (4 * ((eo + t) & 1)));
+      }
+      // dense row blocks of this part, shifted (listed only while all fit)
+      if (ndense <= (uint64_t)mq::kDenseListMax)
+        for (uint32_t d = 0; d < q->ndense; ++d) {
+          p->dense_rb[p->ndense] = q->dense_rb[d] + (uint32_t)rbo;
+          p->dense_e0[p->ndense] = q->dense_e0[d] + (uint32_t)so;
+          p->dense_nch[p->ndense] = q->dense_nch[d];
+          ++p->ndense;
+        }
+    }
+    rbo += q->Nb;
+    eo += q->nnz;
+    so += q->nstream;
+  }
+  p->ndense = (uint32_t)std::min<uint64_t>(ndense, 0xFFFFFFFFu);
+  if (e == hipSuccess) e = hipMemcpyAsync(p->row_ptr, row_ptr, (size_t)(N + 1) * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(p->tile_ptr, tile_ptr, (n_tiles + 1) * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(p->rcodes, rcodes, sz_rcodes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);   // the host images are freed below
+  std::free(row_ptr);
+  std::free(tile_ptr);
+  std::free(rcodes);
+  std::free(tmp);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    release(p);
+    return from_hip(e);
+  }
+  p->magic = mq::kMagic;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_live.insert(p);
+  }
+  *out = p;
+  return MQ_OK;
 }
 
 MQ_API mq_status mq_residual_add(const void* X_dev_fp16, int64_t M, const mq_packed* p, void* Y_dev_fp16,

@@ -24,7 +24,7 @@ GEMV_MAX_M = 64
 EXPORTED = ("mq_pack", "mq_linear", "mq_linear_with", "mq_linear_noalloc", "mq_residual_add", "mq_packed_info",
             "mq_export_canonical", "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks",
             "mq_smooth_weights", "mq_smooth_activations", "mq_quantize_activations", "mq_linear_a4",
-            "mq_stream_read", "mq_free", "mq_status_string")
+            "mq_stream_read", "mq_concat", "mq_free", "mq_status_string")
 
 
 class MQError(RuntimeError):
@@ -71,6 +71,8 @@ def _load():
     lib.mq_linear_a4.restype = ctypes.c_int
     lib.mq_stream_read.argtypes = [vp, i64, i32, vp, vp]
     lib.mq_stream_read.restype = ctypes.c_int
+    lib.mq_concat.argtypes = [ctypes.POINTER(vp), i32, vp, ctypes.POINTER(vp)]
+    lib.mq_concat.restype = ctypes.c_int
     lib.mq_free.argtypes = [vp]
     lib.mq_free.restype = None
     lib.mq_status_string.argtypes = [ctypes.c_int]
@@ -149,6 +151,19 @@ def mq_pack(W, group_size: int = 128, residual_density: float = 0.0, stream=None
     _check(lib.mq_pack(ptr, N, K, group_size, float(residual_density), _stream_handle(stream),
                        ctypes.byref(out)), "mq_pack")
     return Packed(out, N, K, group_size, float(residual_density))
+
+
+def mq_concat(parts, stream=None) -> Packed:
+    """One handle for several packed layers that read the same input, their
+    rows stacked in order (see mq_concat in include/mosaicq.h); the parts
+    stay owned by the caller."""
+    parts = list(parts)
+    arr = (ctypes.c_void_p * len(parts))(*[p.handle for p in parts])
+    out = ctypes.c_void_p()
+    _check(lib.mq_concat(arr, len(parts), _stream_handle(stream), ctypes.byref(out)), "mq_concat")
+    N = sum(p.N for p in parts)
+    info_nnz = sum(p.nnz for p in parts)
+    return Packed(out, N, parts[0].K, parts[0].G, info_nnz / float(N * parts[0].K))
 
 
 def mq_pack_blocks(W, group_size: int, block_fraction: float, h, stream=None) -> Packed:

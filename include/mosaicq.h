@@ -379,6 +379,35 @@ mq_status mq_linear_a4(const void* xq_dev_u8, const void* xmeta_dev_u32, int64_t
 mq_status mq_stream_read(const void* src_dev, int64_t bytes, int32_t workgroups, void* sink_dev_u32,
                          void* hip_stream);
 
+/*
+ * mq_concat -- one handle for several layers that read the same input
+ * (for example the query, key and value projections, or the gate and up
+ * projections of a transformer block): their rows stacked in the order
+ * given, so that one mq_linear call computes all of them. This is launch
+ * plumbing, not a step of the method: each part keeps the codes, scales and
+ * residual selected when it was packed (its own top-k), and mq_linear on the
+ * result writes Y[:, rows of part i] = mq_linear of part i, within the same
+ * tolerance (the kernels may group row blocks differently).
+ *
+ *   parts        n handles from mq_pack (element-wise or residual-free; read
+ *                only, still owned by the caller, who may free them after the
+ *                call returns)
+ *   n            n >= 1
+ *   hip_stream   stream the copies run on; the call synchronises it
+ *   out          receives the new handle (free it with mq_free)
+ *
+ * Every part needs the same K, group size and device, and every part but
+ * the last a row count that is a multiple of 16 (whole row blocks).
+ * mq_export_canonical of the result gives the parts' canonical arrays
+ * concatenated row-wise (residual entries renumbered). The result owns its
+ * memory: about the sum of the parts'. Errors: MQ_ERR_INVALID_ARG for a NULL
+ * argument, n < 1, parts that differ in K, group size or device, or a
+ * ragged part before the last; MQ_ERR_BAD_HANDLE for a handle that is not
+ * live; MQ_ERR_UNSUPPORTED for a block-residual part or more than 2^31 - 1
+ * weights in all; MQ_ERR_OUT_OF_MEMORY / MQ_ERR_DEVICE from HIP.
+ */
+mq_status mq_concat(const mq_packed* const* parts, int32_t n, void* hip_stream, mq_packed** out);
+
 /* mq_free -- release a handle and its device memory (NULL is accepted). The
  * caller must make sure no enqueued mq_linear still reads it. */
 void mq_free(mq_packed* p);
