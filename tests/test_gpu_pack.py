@@ -58,14 +58,26 @@ def test_pack_matches_oracle_bit_exact(mq, N, K, G, rho, kind):
 
 
 def test_pack_hand_example(mq):
-    W = np.zeros((2, 64), dtype=np.float16)
-    W[0, :5] = [7.0, -3.5, 2.5, 1.25, 0.5]
-    W[0, 32:36] = [-14.0, 3.0, 5.0, 0.75]
-    W[1, :2] = [0.5, 0.25]
-    p, got = gpu_canonical(mq, W, 32, 5 / 128)
-    assert got["col"].view(np.uint16).tolist() == [1, 2, 33, 34, 35]
-    assert got["rcodes"].tolist() == [0xBB, 0xF1, 0x0D]
-    assert_canonical_equal(got, oracle.pack(W, 32, 5 / 128))
+    """The packing derived by hand in tests/golden/hand_2x64_g32.json, every
+    array of it, and the oracle's pack of the same matrix."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "hand_2x64_g32.json")) as fh:
+        g = json.load(fh)
+    W = np.zeros((g["N"], g["K"]), dtype=np.float16)
+    for i, j, v in g["W_nonzero"]:
+        W[i, j] = v
+    rho = g["rho_num"] / g["rho_den"]
+    p, got = gpu_canonical(mq, W, g["G"], rho)
+    ex = g["expected"]
+    assert got["scales"].view(np.uint16).tolist() == ex["scales_fp16_bits"]
+    assert [bytes(r).hex() for r in got["codes"]] == ex["codes_hex"]
+    assert p.nnz == ex["nnz"]
+    assert got["row_ptr"].tolist() == ex["row_ptr"]
+    assert got["col"].view(np.uint16).tolist() == ex["col"]
+    assert got["rscale"].view(np.uint32).tolist() == ex["rscale_fp32_bits"]
+    assert got["rcodes"].tolist() == ex["rcodes"]
+    assert_canonical_equal(got, oracle.pack(W, g["G"], rho))
 
 
 @pytest.mark.parametrize("name", ["tiny-1024x1024", "decode-11008x4096"])

@@ -401,3 +401,34 @@ def test_linear_matches_exact_sums_on_tiny_inputs():
     ok = oracle.within_tolerance(Y.astype(np.float16), Y, B)
     assert ok.all()
     assert not oracle.within_tolerance(Y + 0.01 * B + 1e-3, Y, B).any()
+
+
+# ------------------------------------------------ golden fixtures (by hand)
+def _golden(name):
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as fh:
+        return json.load(fh)
+
+
+def golden_matrix(g):
+    W = np.zeros((g["N"], g["K"]), dtype=np.float16)
+    for i, j, v in g["W_nonzero"]:
+        W[i, j] = v
+    return W
+
+
+def test_oracle_reproduces_the_hand_derived_fixture():
+    """tests/golden/hand_2x64_g32.json holds a packing derived by hand from the
+    rules (its `derivation` lines); the oracle must give every array of it."""
+    g = _golden("hand_2x64_g32.json")
+    p = oracle.pack(golden_matrix(g), g["G"], g["rho_num"] / g["rho_den"])
+    ex = g["expected"]
+    assert p["scales"].view(np.uint16).tolist() == ex["scales_fp16_bits"]
+    assert [bytes(r).hex() for r in p["codes"]] == ex["codes_hex"]
+    assert p["nnz"] == ex["nnz"]
+    assert p["row_ptr"].tolist() == ex["row_ptr"]
+    assert p["col"].tolist() == ex["col"]
+    assert p["rscale"].view(np.uint32).tolist() == ex["rscale_fp32_bits"]
+    assert p["qr"].tolist() == ex["qr"]
+    assert p["rcodes"].tolist() == ex["rcodes"]
