@@ -24,7 +24,7 @@ GEMV_MAX_M = 64
 EXPORTED = ("mq_pack", "mq_linear", "mq_linear_with", "mq_linear_noalloc", "mq_residual_add", "mq_packed_info",
             "mq_export_canonical", "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks",
             "mq_smooth_weights", "mq_smooth_activations", "mq_quantize_activations", "mq_linear_a4",
-            "mq_stream_read", "mq_concat", "mq_free", "mq_status_string")
+            "mq_stream_read", "mq_concat", "mq_decode_a4", "mq_free", "mq_status_string")
 
 
 class MQError(RuntimeError):
@@ -71,6 +71,8 @@ def _load():
     lib.mq_linear_a4.restype = ctypes.c_int
     lib.mq_stream_read.argtypes = [vp, i64, i32, vp, vp]
     lib.mq_stream_read.restype = ctypes.c_int
+    lib.mq_decode_a4.argtypes = [vp, i64, vp, vp, vp]
+    lib.mq_decode_a4.restype = ctypes.c_int
     lib.mq_concat.argtypes = [ctypes.POINTER(vp), i32, vp, ctypes.POINTER(vp)]
     lib.mq_concat.restype = ctypes.c_int
     lib.mq_free.argtypes = [vp]
@@ -108,6 +110,30 @@ def _dev_fp16(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+_deferred = []   # handles released while a stream capture was running, freed at the next release
+
+
+def _capturing() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available() and torch.cuda.is_current_stream_capturing()
+    except Exception:
+        return False
+
+
+def _release(h) -> None:
+    """mq_free, except while the current stream is being captured into a HIP
+    graph: freeing device memory then would invalidate the capture (a handle
+    collected by the garbage collector mid-capture does exactly that), so the
+    handle waits for the next release outside a capture."""
+    if _capturing():
+        _deferred.append(h)
+        return
+    while _deferred:
+        lib.mq_free(_deferred.pop())
+    lib.mq_free(h)
+
+
 class Packed:
     """A packed layer (owns the library handle; freed with free() or on GC)."""
 
@@ -131,7 +157,7 @@ class Packed:
 
     def free(self):
         if self._h is not None:
-            lib.mq_free(self._h)
+            _release(self._h)
             self._h = None
 
     def __del__(self):
@@ -275,6 +301,24 @@ def mq_linear_a4(xq, xmeta, packed: Packed, Y=None, stream=None):
         raise ValueError(f"Y must be [{M}, {packed.N}]")
     _check(lib.mq_linear_a4(ctypes.c_void_p(xq.data_ptr()), ctypes.c_void_p(xmeta.data_ptr()), M, packed.handle,
                             yp, _stream_handle(stream)), "mq_linear_a4")
+    return Y
+
+
+def mq_decode_a4(X, packed: Packed, Y=None, stream=None):
+    """W4A4 decode (up to 2 tokens) in one kernel that quantizes X itself:
+    equal to mq_linear_a4(*mq_quantize_activations(X, G), packed) (enqueued,
+    no sync)."""
+    import torch
+    xp = _dev_fp16(X, "X")
+    if X.dim() != 2 or X.shape[1] != packed.K:
+        raise ValueError(f"X must be [M, {packed.K}]")
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty((M, packed.N), dtype=torch.float16, device=X.device)
+    yp = _dev_fp16(Y, "Y")
+    if tuple(Y.shape) != (M, packed.N):
+        raise ValueError(f"Y must be [{M}, {packed.N}]")
+    _check(lib.mq_decode_a4(xp, M, packed.handle, yp, _stream_handle(stream)), "mq_decode_a4")
     return Y
 
 

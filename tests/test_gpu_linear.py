@@ -274,3 +274,30 @@ def test_linear_in_graph_replays_match_eager(mq, M, kern):
         print(f"[graph replay] M={M} kernel={kern} replay={rep}", flush=True)
         assert np.array_equal(Y.cpu().numpy().view(np.uint16), ref.view(np.uint16))
         assert np.array_equal(junk.cpu().numpy().view(np.uint16), ref.view(np.uint16))
+
+
+def test_free_during_graph_capture_is_deferred(mq):
+    """Releasing a handle while the stream is being captured (as the garbage
+    collector may do) must not free device memory then, which would
+    invalidate the capture: the binding defers it to the next release."""
+    import torch
+    K, N, G = 4096, 64, 128
+    keep = mq.mq_pack(to_dev(_layer(N, K, seed=5)), G, 0.01)
+    gone = mq.mq_pack(to_dev(_layer(N, K, seed=6)), G, 0.01)
+    X = to_dev(_x(4, K, seed=7))
+    Y = torch.empty((4, N), dtype=torch.float16, device="cuda")
+    eager = mq.mq_linear(X, keep).cpu().numpy()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mq.mq_linear(X, keep, Y, stream=torch.cuda.current_stream())
+        gone.free()
+    assert len(mq._deferred) == 1
+    for _ in range(3):
+        Y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy().view(np.uint16), eager.view(np.uint16))
+    keep.free()   # outside the capture: frees the deferred handle too
+    assert not mq._deferred
