@@ -710,7 +710,7 @@ def bench_w4a4(args, mq, synth, torch):
     N, K, G = layer.N, layer.K, layer.group
     W = torch.from_numpy(layer.W()).cuda()
     dec = {}
-    for M in (1, 16):
+    for M in (1, 2, 16):
         X = torch.from_numpy(layer.X(M)).cuda()
         Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
         p0 = mq.mq_pack(W, G, 0.0)
@@ -724,8 +724,13 @@ def bench_w4a4(args, mq, synth, torch):
 
         def a16(i, X=X, Y=Y):
             mq.mq_linear(X, copies[i % ncopy], Y)
+
+        def a4f(i, X=X, Y=Y):   # the quantizer inside the decode kernel: one launch
+            mq.mq_decode_a4(X, copies[i % ncopy], Y)
         dec[str(M)] = {"w4a4_step_us": round(replay_spread(torch, a4, 4, 40, reps=5)[0] * 1e3, 2),
                        "w4a16_us": round(replay_spread(torch, a16, 4, 40, reps=5)[0] * 1e3, 2)}
+        if M <= 2:
+            dec[str(M)]["w4a4_one_kernel_us"] = round(replay_spread(torch, a4f, 4, 40, reps=5)[0] * 1e3, 2)
         for c in copies:
             c.free()
     res["decode_11008x4096_plain"] = dec

@@ -542,6 +542,19 @@ MQ_API mq_status mq_linear_a4(const void* xq_dev_u8, const void* xmeta_dev_u32, 
                                      static_cast<uint16_t*>(Y_dev_fp16), static_cast<hipStream_t>(hip_stream)));
 }
 
+MQ_API mq_status mq_decode_a4(const void* X_dev_fp16, int64_t M, const mq_packed* p, void* Y_dev_fp16,
+                              void* hip_stream) {
+  if (!is_live(p)) return MQ_ERR_BAD_HANDLE;
+  if (!X_dev_fp16 || !Y_dev_fp16 || M <= 0) return MQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(X_dev_fp16) & 15u) || (reinterpret_cast<uintptr_t>(Y_dev_fp16) & 1u))
+    return MQ_ERR_INVALID_ARG;
+  if (!p->blocks && p->nnz > 0) return MQ_ERR_UNSUPPORTED;   // as mq_linear_a4
+  if (p->Nb * p->Kt * mq::kTileBytes >= (int64_t(1) << 31)) return MQ_ERR_UNSUPPORTED;
+  if (!mq::decode_a4_fused_takes(p, M)) return MQ_ERR_UNSUPPORTED;
+  return from_hip(mq::launch_decode_a4_fused(p, static_cast<const uint16_t*>(X_dev_fp16), M,
+                                             static_cast<uint16_t*>(Y_dev_fp16), static_cast<hipStream_t>(hip_stream)));
+}
+
 MQ_API mq_status mq_stream_read(const void* src_dev, int64_t bytes, int32_t workgroups, void* sink_dev_u32,
                                 void* hip_stream) {
   if (!src_dev || !sink_dev_u32 || bytes <= 0 || workgroups <= 0) return MQ_ERR_INVALID_ARG;

@@ -162,6 +162,11 @@ hipError_t quantize_a4(const uint16_t* X, int64_t M, int64_t K, int G, uint8_t* 
                        hipStream_t stream);
 hipError_t launch_gemm_a4(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, int64_t M, uint16_t* Y,
                           hipStream_t stream);
+// The W4A4 decode kernel quantizing the fp16 activations itself (one
+// kernel, no intermediate buffers), for the (p, M) decode_a4_fused_takes
+// accepts: up to 2 tokens and K <= 4096.
+bool decode_a4_fused_takes(const mq_packed* p, int64_t M);
+hipError_t launch_decode_a4_fused(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream);
 
 // Streaming-read probe (probe.hip): reads bytes (a multiple of 16) of src
 // with 16-byte loads, one XOR word per workgroup into sink[workgroups].

@@ -61,21 +61,16 @@ __device__ __forceinline__ uint32_t e4m3_code(int q) {
   return v | (q < 0 ? 0x80u : 0u);
 }
 
-// One thread per 8 columns of a token row (chunk c = 4 g + t of a tile: the
+// One lane per 8 columns of a token row (chunk c = 4 g + t of a tile: the
 // tile-order bytes 8 c .. 8 c + 7). The 16 chunks of a (token, tile) are 16
-// consecutive lanes; a group's chunks differ in g (all G), in t's low bit
-// (G >= 64) and in t's high bit (G = 128), and reduce over those lanes.
+// consecutive lanes, all active; a group's chunks differ in g (all G), in t's
+// low bit (G >= 64) and in t's high bit (G = 128), and reduce over those
+// lanes. Writes the chunk's 8 codes at xq_tile + 8 c (the tile's 128 bytes
+// of token m) and the group metadata at meta_tile[0 .. NG) (token m, tile kt).
+// v: the chunk's 8 fp16 values (zero past K).
 template <int NG>
-__global__ __launch_bounds__(256) void k_quant_a4(const uint16_t* __restrict__ X, int M, int K, int Kt,
-                                                  uint8_t* __restrict__ xq, uint32_t* __restrict__ xmeta) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t unit = gid >> 4;                      // (token, tile); the 16 lanes exit together
-  if (unit >= (int64_t)M * Kt) return;
-  const int c = (int)(gid & 15), g = c >> 2, t = c & 3;
-  const int m = (int)(unit / Kt), kt = (int)(unit - (int64_t)m * Kt);
-  const int col0 = 128 * kt + 32 * t + 8 * g;
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (col0 < K) v = *reinterpret_cast<const uint4*>(X + (int64_t)m * K + col0);
+__device__ __forceinline__ void quant_chunk_v(uint4 v, int c, uint8_t* xq_tile, uint32_t* meta_tile) {
+  const int g = c >> 2, t = c & 3;
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t h[8];
 #pragma unroll
@@ -100,15 +95,35 @@ __global__ __launch_bounds__(256) void k_quant_a4(const uint16_t* __restrict__ X
   }
   const uint32_t lo = e4m3_code(q[0]) | (e4m3_code(q[4]) << 8) | (e4m3_code(q[1]) << 16) | (e4m3_code(q[5]) << 24);
   const uint32_t hi = e4m3_code(q[2]) | (e4m3_code(q[6]) << 8) | (e4m3_code(q[3]) << 16) | (e4m3_code(q[7]) << 24);
-  const int64_t Kp = (int64_t)Kt * kTileCols;
-  *reinterpret_cast<uint2*>(xq + (int64_t)m * Kp + 128 * kt + 8 * c) = make_uint2(lo, hi);
+  *reinterpret_cast<uint2*>(xq_tile + 8 * c) = make_uint2(lo, hi);
   sum += __shfl_xor(sum, 4);
   sum += __shfl_xor(sum, 8);
   if (NG <= 2) sum += __shfl_xor(sum, 1);
   if (NG == 1) sum += __shfl_xor(sum, 2);
   constexpr int TPG = 4 / NG;   // t values per group
-  if (g == 0 && (t % TPG) == 0)
-    xmeta[(int64_t)m * Kt * NG + (int64_t)kt * NG + t / TPG] = sbits | ((uint32_t)(sum & 0xFFFF) << 16);
+  if (g == 0 && (t % TPG) == 0) meta_tile[t / TPG] = sbits | ((uint32_t)(sum & 0xFFFF) << 16);
+}
+
+template <int NG>
+__device__ __forceinline__ void quant_chunk(const uint16_t* __restrict__ X, int K, int m, int kt, int c,
+                                            uint8_t* xq_tile, uint32_t* meta_tile) {
+  const int col0 = 128 * kt + 32 * (c & 3) + 8 * (c >> 2);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (col0 < K) v = *reinterpret_cast<const uint4*>(X + (int64_t)m * K + col0);
+  quant_chunk_v<NG>(v, c, xq_tile, meta_tile);
+}
+
+// The quantizer kernel: one thread per chunk of every (token, tile).
+template <int NG>
+__global__ __launch_bounds__(256) void k_quant_a4(const uint16_t* __restrict__ X, int M, int K, int Kt,
+                                                  uint8_t* __restrict__ xq, uint32_t* __restrict__ xmeta) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t unit = gid >> 4;                      // (token, tile); the 16 lanes exit together
+  if (unit >= (int64_t)M * Kt) return;
+  const int c = (int)(gid & 15);
+  const int m = (int)(unit / Kt), kt = (int)(unit - (int64_t)m * Kt);
+  const int64_t Kp = (int64_t)Kt * kTileCols;
+  quant_chunk<NG>(X, K, m, kt, c, xq + (int64_t)m * Kp + 128 * kt, xmeta + ((int64_t)m * Kt + kt) * NG);
 }
 
 // ------------------------------------------------------------- W4A4 GEMM
@@ -605,10 +620,117 @@ struct DecRegs {
   uint32_t meta[T][4][NG];   // metadata of tokens 4 (l / 16) + 0..3 of each tile
 };
 
+// Activations quantized inside the decode kernel (QX): up to kDecQxMaxM
+// tokens and K <= kDecQxMaxK, held in LDS in the layout of the quantizer's
+// output.
+constexpr int kDecQxMaxM = 2;
+constexpr int kDecQxMaxK = 4096;
+
+// The lane's activation operand and metadata of tile kt (tokens past M read
+// zero codes and metadata): from the quantizer's output in global memory, or
+// with QX from its copy in LDS.
+template <int NG, bool QX>
+__device__ __forceinline__ void dec_load_x(uint4& a0, uint4& a1, uint32_t (&meta)[4][NG],
+                                           __amdgpu_buffer_rsrc_t xrs, __amdgpu_buffer_rsrc_t mrs,
+                                           const uint8_t* xq_s, const uint32_t* meta_s, int M, int Kp, int ngt,
+                                           uint32_t va, int r, int g, int kt) {
+  if constexpr (QX) {
+    const int rr = min(r, M - 1);   // a token past M repeats the last one; its outputs are never stored
+    const uint4* p = reinterpret_cast<const uint4*>(xq_s + rr * Kp + kt * kTileCols + 32 * g);
+    a0 = p[0];
+    a1 = p[1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) meta[q][gi] = meta_s[min(4 * g + q, M - 1) * ngt + kt * NG + gi];
+  } else {
+    const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(xrs, va, kt * kTileCols, 0);
+    const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(xrs, va, kt * kTileCols + 16, 0);
+    a0 = make_uint4(v0[0], v0[1], v0[2], v0[3]);
+    a1 = make_uint4(v1[0], v1[1], v1[2], v1[3]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+        meta[q][gi] = __builtin_amdgcn_raw_buffer_load_b32(mrs, (uint32_t)(((4 * g + q) * ngt + kt * NG + gi) * 4), 0, 0);
+  }
+}
+
+// The weight side of tile kt for the RBW row blocks: codes, scales, and the
+// block residual's tile and row scale.
 template <int NG, bool DR, int RBW>
+__device__ __forceinline__ void dec_load_w(DecRegs<NG, RBW>& D, int t, const WSrc& src, const DenseA4& dr,
+                                           int rb0, int Nb, int Kt, int kt, uint32_t vcode, uint32_t vscale,
+                                           uint32_t vrs) {
+#pragma unroll
+  for (int j = 0; j < RBW; ++j) {
+    const int rb = min(rb0 + j, Nb - 1);
+    const auto c = __builtin_amdgcn_raw_buffer_load_b128(src.tiles, vcode, (rb * Kt + kt) * kTileBytes, 0);
+    D.code[t][j] = make_uint4(c[0], c[1], c[2], c[3]);
+    const int srow = rb * kRowsPerBlock * (int)src.sstride_b;
+    if constexpr (NG == 1) {
+      D.sraw[t][j] = __builtin_amdgcn_raw_buffer_load_b32(src.scales, vscale, srow + 4 * (kt >> 1), 0);
+    } else if constexpr (NG == 2) {
+      D.sraw[t][j] = __builtin_amdgcn_raw_buffer_load_b32(src.scales, vscale, srow + 4 * kt, 0);
+    } else {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(src.scales, vscale, srow + 8 * kt, 0);
+      D.sraw[t][j] = make_uint2(v[0], v[1]);
+    }
+    if constexpr (DR) {
+      const int sl = __builtin_amdgcn_readfirstlane(dr.slot[(int64_t)rb * Kt + kt]);
+      D.slot[t][j] = sl;
+      const auto rc = __builtin_amdgcn_raw_buffer_load_b128(src.rtiles, vcode, sl * kTileBytes, 0);
+      D.rcode[t][j] = make_uint4(rc[0], rc[1], rc[2], rc[3]);
+      D.rsc[t][j] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(src.rscale, vrs, sl * kRowsPerBlock * 4, 0));
+    }
+  }
+}
+
+// QX: the workgroup's 512 threads quantize the M token rows (every tile)
+// into LDS, 16 lanes per (token, tile) as in the quantizer kernel, in two
+// parts: the loads of the thread's PQ chunks (issued before the weight
+// loads, so that waiting for them waits for nothing else; chunks past the
+// batch or past K read zero through the buffer's range), then the
+// quantization into LDS.
+template <int PQ>
+__device__ __forceinline__ void dec_quant_load(uint4 (&xv)[PQ], __amdgpu_buffer_rsrc_t xs, int K, int Kt, int units) {
+#pragma unroll
+  for (int i = 0; i < PQ; ++i) {
+    const int u = (int)threadIdx.x + 512 * i;
+    const int pair = u >> 4, c = u & 15;
+    const int m = pair / Kt, kt = pair - m * Kt;
+    const int col0 = 128 * kt + 32 * (c & 3) + 8 * (c >> 2);
+    const uint32_t off = (u < units && col0 < K) ? (uint32_t)(m * K + col0) * 2u : 0x7FFFFFF0u;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(xs, off, 0, 0);
+    xv[i] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+template <int NG, int PQ>
+__device__ __forceinline__ void dec_quant_store(const uint4 (&xv)[PQ], int Kt, int units, uint8_t* xq_s,
+                                                uint32_t* meta_s) {
+  const int Kp = Kt * kTileCols;
+#pragma unroll
+  for (int i = 0; i < PQ; ++i) {
+    const int u = (int)threadIdx.x + 512 * i;
+    if (u < units) {   // units is a multiple of 16: a 16-lane group is all in or all out
+      const int pair = u >> 4, c = u & 15;
+      const int m = pair / Kt, kt = pair - m * Kt;
+      quant_chunk_v<NG>(xv[i], c, xq_s + m * Kp + 128 * kt, meta_s + (m * Kt + kt) * NG);
+    }
+  }
+  // publish the codes: an LDS-only barrier (the weight loads stay in flight)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int NG, bool DR, int RBW, bool QX, int PQ>
 __global__ __launch_bounds__(512) void k_gemv_a4(WArrays warr, const uint8_t* __restrict__ xq,
-                                                 const uint32_t* __restrict__ xmeta, uint16_t* __restrict__ Y,
-                                                 int M, int N, int Kt, int Nb, DenseA4 dr) {
+                                                 const uint32_t* __restrict__ xmeta, const uint16_t* __restrict__ X,
+                                                 int K, uint16_t* __restrict__ Y, int M, int N, int Kt, int Nb,
+                                                 DenseA4 dr) {
   __shared__ float4_t red[RBW][8][64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
@@ -618,55 +740,66 @@ __global__ __launch_bounds__(512) void k_gemv_a4(WArrays warr, const uint8_t* __
   const int Kp = Kt * kTileCols, ngt = Kt * NG;
   // tokens past M read as zero codes and zero metadata
   const __amdgpu_buffer_rsrc_t xrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(xq), 0, M * Kp, kBufferRaw);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(xq), 0, QX ? 0 : M * Kp, kBufferRaw);
   const __amdgpu_buffer_rsrc_t mrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(xmeta), 0, M * ngt * 4, kBufferRaw);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(xmeta), 0, QX ? 0 : M * ngt * 4, kBufferRaw);
   const uint32_t vcode = 16u * (uint32_t)lane, vscale = (uint32_t)r * src.sstride_b, vrs = 4u * (uint32_t)r;
   const uint32_t va = (uint32_t)(r * Kp + 32 * g);
+  uint8_t* xq_s = nullptr;
+  uint32_t* meta_s = nullptr;
+  if constexpr (QX) {
+    __shared__ __attribute__((aligned(16))) uint8_t xq_lds[kDecQxMaxM * kDecQxMaxK];
+    __shared__ uint32_t meta_lds[kDecQxMaxM * (kDecQxMaxK / 32)];
+    xq_s = xq_lds;
+    meta_s = meta_lds;
+  }
 
   float4_t acc[RBW];
 #pragma unroll
   for (int j = 0; j < RBW; ++j) acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+  const int units = M * Kt * 16;
+  uint4 xv[QX ? PQ : 1];
+  if constexpr (QX) {
+    const __amdgpu_buffer_rsrc_t xs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), 0, M * K * 2, kBufferRaw);
+    dec_quant_load<PQ>(xv, xs, K, Kt, units);
+    // memory operations keep their program order across this point (no
+    // register is named, so nothing waits here): the X loads go out first
+    asm volatile("" ::: "memory");
+  }
+
   constexpr int T = dec_tiles<NG>();
+  bool first = true;
   for (int base = kt0; base < kt1; base += T) {
     DecRegs<NG, RBW> D;
     // every load of the batch first (tiles past kt1 are clamped; their math is skipped)
+    if constexpr (QX) {
+      // the weight loads go out first; the first batch's are in flight while
+      // the workgroup quantizes the activations into LDS
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int kt = min(base + t, Kt - 1);
-      const auto a0 = __builtin_amdgcn_raw_buffer_load_b128(xrs, va, kt * kTileCols, 0);
-      const auto a1 = __builtin_amdgcn_raw_buffer_load_b128(xrs, va, kt * kTileCols + 16, 0);
-      D.a0[t] = make_uint4(a0[0], a0[1], a0[2], a0[3]);
-      D.a1[t] = make_uint4(a1[0], a1[1], a1[2], a1[3]);
+      for (int t = 0; t < T; ++t) dec_load_w<NG, DR, RBW>(D, t, src, dr, rb0, Nb, Kt, min(base + t, Kt - 1), vcode, vscale, vrs);
+      if (first) {
+        // The quantization starts only here, after the weight requests: the
+        // empty asm redefines the X registers (and orders memory), so none
+        // of the arithmetic can move above it, and the wait it needs covers
+        // the X loads alone (issued first; the weight loads stay in flight).
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+        for (int i = 0; i < PQ; ++i)
+          asm volatile("" : "+v"(xv[i].x), "+v"(xv[i].y), "+v"(xv[i].z), "+v"(xv[i].w) :: "memory");
+        dec_quant_store<NG, PQ>(xv, Kt, units, xq_s, meta_s);
+        first = false;
+      }
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi)
-          D.meta[t][q][gi] =
-              __builtin_amdgcn_raw_buffer_load_b32(mrs, (uint32_t)(((4 * g + q) * ngt + kt * NG + gi) * 4), 0, 0);
+      for (int t = 0; t < T; ++t)
+        dec_load_x<NG, true>(D.a0[t], D.a1[t], D.meta[t], xrs, mrs, xq_s, meta_s, M, Kp, ngt, va, r, g,
+                             min(base + t, Kt - 1));
+    } else {
 #pragma unroll
-      for (int j = 0; j < RBW; ++j) {
-        const int rb = min(rb0 + j, Nb - 1);
-        const auto c = __builtin_amdgcn_raw_buffer_load_b128(src.tiles, vcode, (rb * Kt + kt) * kTileBytes, 0);
-        D.code[t][j] = make_uint4(c[0], c[1], c[2], c[3]);
-        const int srow = rb * kRowsPerBlock * (int)src.sstride_b;
-        if constexpr (NG == 1) {
-          D.sraw[t][j] = __builtin_amdgcn_raw_buffer_load_b32(src.scales, vscale, srow + 4 * (kt >> 1), 0);
-        } else if constexpr (NG == 2) {
-          D.sraw[t][j] = __builtin_amdgcn_raw_buffer_load_b32(src.scales, vscale, srow + 4 * kt, 0);
-        } else {
-          const auto v = __builtin_amdgcn_raw_buffer_load_b64(src.scales, vscale, srow + 8 * kt, 0);
-          D.sraw[t][j] = make_uint2(v[0], v[1]);
-        }
-        if constexpr (DR) {
-          const int sl = __builtin_amdgcn_readfirstlane(dr.slot[(int64_t)rb * Kt + kt]);
-          D.slot[t][j] = sl;
-          const auto rc = __builtin_amdgcn_raw_buffer_load_b128(src.rtiles, vcode, sl * kTileBytes, 0);
-          D.rcode[t][j] = make_uint4(rc[0], rc[1], rc[2], rc[3]);
-          D.rsc[t][j] = __builtin_bit_cast(
-              float, __builtin_amdgcn_raw_buffer_load_b32(src.rscale, vrs, sl * kRowsPerBlock * 4, 0));
-        }
+      for (int t = 0; t < T; ++t) {
+        const int kt = min(base + t, Kt - 1);
+        dec_load_x<NG, false>(D.a0[t], D.a1[t], D.meta[t], xrs, mrs, xq_s, meta_s, M, Kp, ngt, va, r, g, kt);
+        dec_load_w<NG, DR, RBW>(D, t, src, dr, rb0, Nb, Kt, kt, vcode, vscale, vrs);
       }
     }
 #pragma unroll
@@ -707,6 +840,9 @@ __global__ __launch_bounds__(512) void k_gemv_a4(WArrays warr, const uint8_t* __
       }
     }
   }
+  if constexpr (QX) {
+    if (first) dec_quant_store<NG, PQ>(xv, Kt, units, xq_s, meta_s);   // a wave with no tiles (Kt < 8)
+  }
 
 #pragma unroll
   for (int j = 0; j < RBW; ++j) red[j][wave][lane] = acc[j];
@@ -726,36 +862,40 @@ __global__ __launch_bounds__(512) void k_gemv_a4(WArrays warr, const uint8_t* __
   }
 }
 
-template <int NG, bool DR, int RBW>
-hipError_t launch_dec(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, int64_t M, uint16_t* Y,
-                      hipStream_t s) {
+// QX: X holds the fp16 activations (K columns), quantized inside the kernel;
+// otherwise xq / xmeta hold the quantizer's output.
+template <int NG, bool DR, int RBW, bool QX>
+hipError_t launch_dec(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, const uint16_t* X, int64_t M,
+                      uint16_t* Y, hipStream_t s) {
   const WArrays warr = weight_arrays<DR>(p);
   const DenseA4 dr = DR ? DenseA4{p->rt_slot, reinterpret_cast<const uint4*>(p->rt_tiles), p->bscale, (int)p->nblk}
                         : DenseA4{nullptr, nullptr, nullptr, 0};
   const unsigned grid = (unsigned)((p->Nb + RBW - 1) / RBW);
-  k_gemv_a4<NG, DR, RBW><<<dim3(grid), dim3(512), 0, s>>>(warr, xq, xmeta, Y, (int)M, (int)p->N, (int)p->Kt,
-                                                          (int)p->Nb, dr);
+  // QX: 16 M Kt / 512 <= 2 chunks per thread (M <= 2, Kt <= 32)
+  constexpr int PQ = QX ? (16 * kDecQxMaxM * (kDecQxMaxK / kTileCols)) / 512 : 1;
+  k_gemv_a4<NG, DR, RBW, QX, PQ><<<dim3(grid), dim3(512), 0, s>>>(warr, xq, xmeta, X, (int)p->K, Y, (int)M,
+                                                                 (int)p->N, (int)p->Kt, (int)p->Nb, dr);
   return hipGetLastError();
 }
 
 // row blocks per workgroup: enough that one round of workgroups covers the
 // layer on 256 CUs, at most 4
-template <int NG, bool DR>
-hipError_t launch_dec_r(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, int64_t M, uint16_t* Y,
-                        hipStream_t s) {
+template <int NG, bool DR, bool QX>
+hipError_t launch_dec_r(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, const uint16_t* X, int64_t M,
+                        uint16_t* Y, hipStream_t s) {
   const int64_t rbw = std::min<int64_t>(4, std::max<int64_t>(1, (p->Nb + 255) / 256));
-  if (rbw == 1) return launch_dec<NG, DR, 1>(p, xq, xmeta, M, Y, s);
-  if (rbw == 2) return launch_dec<NG, DR, 2>(p, xq, xmeta, M, Y, s);
-  if (rbw == 3) return launch_dec<NG, DR, 3>(p, xq, xmeta, M, Y, s);
-  return launch_dec<NG, DR, 4>(p, xq, xmeta, M, Y, s);
+  if (rbw == 1) return launch_dec<NG, DR, 1, QX>(p, xq, xmeta, X, M, Y, s);
+  if (rbw == 2) return launch_dec<NG, DR, 2, QX>(p, xq, xmeta, X, M, Y, s);
+  if (rbw == 3) return launch_dec<NG, DR, 3, QX>(p, xq, xmeta, X, M, Y, s);
+  return launch_dec<NG, DR, 4, QX>(p, xq, xmeta, X, M, Y, s);
 }
 
-template <bool DR>
-hipError_t launch_dec_g(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, int64_t M, uint16_t* Y,
-                        hipStream_t s) {
-  if (p->G == 128) return launch_dec_r<1, DR>(p, xq, xmeta, M, Y, s);
-  if (p->G == 64) return launch_dec_r<2, DR>(p, xq, xmeta, M, Y, s);
-  return launch_dec_r<4, DR>(p, xq, xmeta, M, Y, s);
+template <bool DR, bool QX>
+hipError_t launch_dec_g(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, const uint16_t* X, int64_t M,
+                        uint16_t* Y, hipStream_t s) {
+  if (p->G == 128) return launch_dec_r<1, DR, QX>(p, xq, xmeta, X, M, Y, s);
+  if (p->G == 64) return launch_dec_r<2, DR, QX>(p, xq, xmeta, X, M, Y, s);
+  return launch_dec_r<4, DR, QX>(p, xq, xmeta, X, M, Y, s);
 }
 
 }  // namespace
@@ -773,10 +913,19 @@ hipError_t quantize_a4(const uint16_t* X, int64_t M, int64_t K, int G, uint8_t* 
 hipError_t launch_gemm_a4(const mq_packed* p, const uint8_t* xq, const uint32_t* xmeta, int64_t M, uint16_t* Y,
                           hipStream_t s) {
   if (M <= kDecMaxM) {
-    return (p->blocks && p->nblk > 0) ? launch_dec_g<true>(p, xq, xmeta, M, Y, s)
-                                      : launch_dec_g<false>(p, xq, xmeta, M, Y, s);
+    return (p->blocks && p->nblk > 0) ? launch_dec_g<true, false>(p, xq, xmeta, nullptr, M, Y, s)
+                                      : launch_dec_g<false, false>(p, xq, xmeta, nullptr, M, Y, s);
   }
   return launch_a4_d<CfgA4Mid>(p, xq, xmeta, M, Y, s);
+}
+
+bool decode_a4_fused_takes(const mq_packed* p, int64_t M) {
+  return M >= 1 && M <= kDecQxMaxM && p->K <= kDecQxMaxK;
+}
+
+hipError_t launch_decode_a4_fused(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
+  return (p->blocks && p->nblk > 0) ? launch_dec_g<true, true>(p, nullptr, nullptr, X, M, Y, s)
+                                    : launch_dec_g<false, true>(p, nullptr, nullptr, X, M, Y, s);
 }
 
 }  // namespace mq

@@ -366,6 +366,31 @@ mq_status mq_linear_a4(const void* xq_dev_u8, const void* xmeta_dev_u32, int64_t
                        void* Y_dev_fp16, void* hip_stream);
 
 /*
+ * mq_decode_a4 -- the W4A4 layer for a decode batch in one kernel: the
+ * activations are quantized as mq_quantize_activations does (the same codes,
+ * scales and code sums, bit for bit) inside the kernel that multiplies them,
+ * so quantization runs as a stage of the fused pipeline (MosaicQuant
+ * explainer, Methodology section 3) and no intermediate buffer exists.
+ * Every workgroup quantizes the whole batch into its LDS, so the call is
+ * limited to small batches; for more tokens use mq_quantize_activations and
+ * mq_linear_a4.
+ *
+ *   X_dev_fp16   [M, K] fp16 activations (device, 16-byte aligned)
+ *   M            1 <= M <= 2
+ *   p            as for mq_linear_a4, with K <= 4096
+ *   Y_dev_fp16   [M, N] fp16 output (device, 2-byte aligned, overwritten);
+ *                equal, bit for bit, to mq_quantize_activations followed by
+ *                mq_linear_a4 on the same X
+ *   hip_stream   stream to enqueue on (no synchronisation)
+ *
+ * Errors: MQ_ERR_BAD_HANDLE, MQ_ERR_INVALID_ARG (NULL or misaligned
+ * pointers, M <= 0), MQ_ERR_UNSUPPORTED (M > 2, K > 4096, or a handle
+ * mq_linear_a4 refuses), MQ_ERR_DEVICE.
+ */
+mq_status mq_decode_a4(const void* X_dev_fp16, int64_t M, const mq_packed* p, void* Y_dev_fp16,
+                       void* hip_stream);
+
+/*
  * mq_stream_read -- measurement helper, not a step of the method: reads
  * `bytes` of src_dev once with 16-byte loads (workgroups of 256 threads,
  * each thread issuing all of its U = ceil(bytes / (16 * 256 * workgroups))

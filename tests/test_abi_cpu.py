@@ -30,7 +30,7 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["mq_pack", "mq_linear", "mq_linear_with", "mq_linear_noalloc", "mq_residual_add", "mq_stream_read", "mq_packed_info", "mq_export_canonical",
          "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks", "mq_smooth_weights",
-         "mq_smooth_activations", "mq_quantize_activations", "mq_linear_a4", "mq_concat", "mq_free",
+         "mq_smooth_activations", "mq_quantize_activations", "mq_linear_a4", "mq_decode_a4", "mq_concat", "mq_free",
          "mq_status_string"])
 
 
@@ -116,6 +116,7 @@ def test_bad_handles_are_rejected(lib):
     assert lib.mq_export_tiled(bogus, None, None, None, None) == -6
     assert lib.mq_block_count(bogus, ctypes.byref(n)) == -6
     assert lib.mq_export_blocks(bogus, None, None, None, None) == -6
+    assert lib.mq_decode_a4(FAKE, 1, bogus, FAKE, None) == -6
     out = ctypes.c_void_p()
     arr = (ctypes.c_void_p * 2)(bogus, bogus)
     assert lib.mq_concat(arr, 2, None, ctypes.byref(out)) == -6

@@ -183,6 +183,61 @@ def test_linear_a4_decode_layer_11008x4096(mq):
         p.free()
 
 
+# mq_decode_a4 (activations quantized inside the decode kernel, M = 1, 2): 1,
+# 2, 3 and 4 row blocks per workgroup, plain and block handles, G = 128, 64, 32, K up
+# to its limit of 4096, K not a multiple of 128, a wave without tiles (K <
+# 1024), and a NaN group
+FUSED = [(40, 4096, 128, 0.0), (4100, 4096, 64, 0.1), (8200, 1024, 32, 0.0), (12300, 512, 128, 0.05),
+         (300, 4096, 128, 0.2), (90, 320, 64, 0.2), (16, 4096, 32, 0.0), (11008, 4096, 128, 0.1)]
+
+
+@pytest.mark.parametrize("N,K,G,beta", FUSED)
+def test_decode_a4_equals_quantizer_and_linear(mq, N, K, G, beta):
+    W = _layer(N, K, 3 * N + K)
+    if beta > 0:
+        rng = np.random.default_rng(N + 5)
+        Xc = rng.standard_normal((32, K)).astype(np.float16)
+        h = ob.hessian_diag(Xc)
+        p = mq.mq_pack_blocks(to_dev(W), G, beta, to_dev(h))
+        Wt = ob.dequant_blocks(ob.pack_blocks(W, G, beta, h))
+    else:
+        p = mq.mq_pack(to_dev(W), G, 0.0)
+        Wt = oracle.dequant(oracle.pack(W, G, 0.0))
+    for M in (1, 2):
+        X = _acts(M, K, 77 + M)
+        if M == 2:
+            X[1, G:2 * G] = np.float16("nan")   # its group's outputs are NaN on both paths
+        print(f"[a4 decode fused] N={N} K={K} G={G} beta={beta} M={M}", flush=True)
+        Yf = mq.mq_decode_a4(to_dev(X), p).cpu().numpy()
+        xq, xm = mq.mq_quantize_activations(to_dev(X), G)
+        Y2 = mq.mq_linear_a4(xq, xm, p).cpu().numpy()
+        assert np.array_equal(Yf.view(np.uint16), Y2.view(np.uint16)), "fused and two-kernel results differ"
+        fin = np.isfinite(X).all(1)
+        if fin.any():
+            qx, sx = oa.quantize_activations(X[fin], G)
+            check_linear(Yf[fin], oa.dequant_activations(qx, sx, G), Wt, f"fused N={N} K={K} M={M}")
+        assert np.isnan(Yf[~fin]).all()
+    p.free()
+
+
+def test_decode_a4_limits(mq):
+    W = _layer(32, 4224, 9)
+    p = mq.mq_pack(to_dev(W), 128, 0.0)
+    with pytest.raises(mq.MQError) as ei:   # K above 4096
+        mq.mq_decode_a4(to_dev(_acts(1, 4224, 1)), p)
+    assert "UNSUPPORTED" in str(ei.value)
+    q = mq.mq_pack(to_dev(_layer(32, 256, 9)), 128, 0.0)
+    with pytest.raises(mq.MQError) as ei:   # more than 2 tokens
+        mq.mq_decode_a4(to_dev(_acts(3, 256, 1)), q)
+    assert "UNSUPPORTED" in str(ei.value)
+    r = mq.mq_pack(to_dev(_layer(32, 256, 9)), 128, 0.01)
+    with pytest.raises(mq.MQError) as ei:   # single residual entries
+        mq.mq_decode_a4(to_dev(_acts(1, 256, 1)), r)
+    assert "UNSUPPORTED" in str(ei.value)
+    for h in (p, q, r):
+        h.free()
+
+
 def test_linear_a4_rejects_element_residual(mq):
     W = _layer(32, 256, 5)
     p = mq.mq_pack(to_dev(W), 128, 0.01)
@@ -190,6 +245,7 @@ def test_linear_a4_rejects_element_residual(mq):
     with pytest.raises(mq.MQError) as ei:
         mq.mq_linear_a4(xq, xm, p)
     assert "UNSUPPORTED" in str(ei.value)
+    p.free()   # not left to the garbage collector, which may run during a later graph capture
 
 
 def test_linear_a4_graph_replay(mq):
