@@ -49,9 +49,10 @@ def _unpack_nibbles(b, n):
 
 # (rows, residual density, outlier rows) of each part, K = 4096 (the decode
 # kernels): odd residual counts shift the nibble position of the next part's
-# residual codes; one part has no residual; the first has dense row blocks;
-# the last is ragged
-PARTS_K4096 = [(1024, 0.00501, (5, 6, 7)), (512, 0.0, ()), (512, 0.0031, ()), (520, 0.01, ())]
+# residual codes; one part has no residual; the third has dense row blocks
+# (whole outlier rows), which the joined handle lists shifted by the rows and
+# residual entries before it; the last is ragged
+PARTS_K4096 = [(1024, 0.00501, ()), (512, 0.0, ()), (512, 0.0031, (5, 6, 7, 40)), (520, 0.01, ())]
 
 
 def test_concat_export_is_the_parts_joined(mq):
