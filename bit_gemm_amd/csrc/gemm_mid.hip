@@ -39,7 +39,13 @@ constexpr int kThreadsM = 64 * kWavesM;
 constexpr int kPlaneStrideM = 40;   // patch plane: halves per lane (80 B: 4 k-steps x 8, then 8 unused; 16 lanes
                                     // on distinct banks)
 constexpr int kXSlotBytes = 4096;           // per wave: one token block's X for one code tile (16 x 128 fp16)
-constexpr int kRingM = 2;   // register sets in a wave's load ring (deeper rings measured slower at every shape)
+// Register sets in a wave's load ring: 2, or 3 for one row block and one
+// token block per workgroup, where a wave's tiles (1 KiB each) are too small
+// to keep enough bytes in flight (4096x11008 at 4 / 8 / 16 tokens: 15.3 /
+// 15.4 / 15.7 us with 2, 13.8 / 13.9 / 15.1 with 3, 14.4 / 14.4 / 15.8 with
+// 4); with more row blocks deeper rings measured slower at every shape.
+template <int R, int NTB>
+constexpr int mid_ring() { return R == 1 && NTB == 1 ? 3 : 2; }
 
 // Residual of the handle: none; element-wise, either branch-free (kElemFlat1M
 // + e - 1 when no tile's segment of the patch stream exceeds 64 e entries,
@@ -390,6 +396,7 @@ __global__ __launch_bounds__(kThreadsM, 1) void k_gemm_mid(const uint4* __restri
   // (one costs registers): the steps past the wave's last tile compute on
   // zero X. The segment table is requested first; the first tiles' residual
   // loads, which need it, follow their code tiles.
+  constexpr int kRingM = mid_ring<R, NTB>();
   MidTab<R> tab;
   mid_table<MODE, R>(tab, tile_ptr, dr, Kt, Nb, rb0, wave, lane);
   MidTile<GSH, MODE, NTB, R> T[kRingM];
