@@ -89,6 +89,16 @@ def test_pack_workload_layers_bit_exact(mq, name):
     ref = oracle.pack(W, layer.group, layer.rho)
     assert p.nnz == ref["nnz"] == oracle.budget(layer.rho, layer.N, layer.K)
     assert_canonical_equal(got, ref)
+    # device bytes over the plain handle (which reserves the same room for
+    # the row blocks' padding entries): the canonical CSR (2.5 B per entry)
+    # and the two tile-ordered streams the kernels read (4 B per entry each),
+    # 1.10 x the plain handle on the decode layer at rho = 0.5 %
+    plain = mq.mq_pack(to_dev(W), layer.group, 0.0)
+    extra = p.device_bytes - plain.device_bytes
+    assert extra <= 10.5 * p.nnz + 64, (extra, p.nnz)
+    if name == "decode-11008x4096":
+        assert p.device_bytes / plain.device_bytes <= 1.105
+    plain.free()
 
 
 def test_pack_is_deterministic(mq):
