@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 from bit_gemm_amd import synth
-from tests.gpu_util import assert_canonical_equal, gpu_canonical, require_gpu
+from tests.gpu_util import assert_canonical_equal, gpu_canonical, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
