@@ -220,6 +220,36 @@ def test_decode_a4_equals_quantizer_and_linear(mq, N, K, G, beta):
     p.free()
 
 
+def test_decode_a4_graph_replay(mq):
+    """mq_decode_a4 is one kernel with no buffers of its own: captured in a
+    HIP graph and replayed with new activations between replays, every
+    replay equals the eager call bit for bit."""
+    import torch
+    N, K, G = 4100, 4096, 128
+    p = mq.mq_pack(to_dev(_layer(N, K, 21)), G, 0.0)
+    for M in (1, 2):
+        Xd = to_dev(_acts(M, K, 5 * M))
+        Yd = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            mq.mq_decode_a4(Xd, p, Yd, stream=s)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            mq.mq_decode_a4(Xd, p, Yd, stream=torch.cuda.current_stream())
+        for rep in range(3):
+            X = _acts(M, K, 300 + 7 * M + rep)
+            Xd.copy_(torch.from_numpy(X))
+            eager = mq.mq_decode_a4(to_dev(X), p).cpu().numpy()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(Yd.cpu().numpy().view(np.uint16), eager.view(np.uint16)), (M, rep)
+    p.free()
+
+
 def test_decode_a4_limits(mq):
     W = _layer(32, 4224, 9)
     p = mq.mq_pack(to_dev(W), 128, 0.0)
