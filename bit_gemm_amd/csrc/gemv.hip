@@ -210,10 +210,24 @@ __device__ __forceinline__ void res_chunk(float4_t (&acc)[MB], const uint4 v0, c
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     u32x4_t bv;
+    // X in LDS: the token row's base as one LDS byte address, so a gather
+    // address is one shift-add of the column (2 instructions, not the 3 the
+    // compiler otherwise emits)
+    typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+    const uint32_t xrow = (uint32_t)reinterpret_cast<uintptr_t>(reinterpret_cast<lds_u16*>(
+                              reinterpret_cast<uintptr_t>(xs))) + 2u * (uint32_t)(mrow[mb] * ldx);
+    auto gather = [&](uint32_t ent) __attribute__((always_inline)) {
+      uint32_t a;
+      asm("v_lshl_add_u32 %0, %1, 1, %2" : "=v"(a) : "v"(ent_col(ent)), "v"(xrow));
+      return (uint32_t)*reinterpret_cast<lds_u16*>((uintptr_t)a);
+    };
 #pragma unroll
     for (int u = 0; u < 8; u += 2) {
       uint32_t lo, hi;
-      if (XLDS) {
+      if (XLDS && !MW) {
+        lo = gather(e[u]);
+        hi = gather(e[u + 1]);
+      } else if (XLDS) {
         lo = xs[mrow[mb] * ldx + col[u]];
         hi = xs[mrow[mb] * ldx + col[u + 1]];
       } else {
