@@ -121,5 +121,10 @@ def test_concat_errors(mq):
     rc, out = status(b, a)                    # a ragged last part is fine
     assert rc == mq.MQ_OK
     mq.lib.mq_free(out)
+    one = mq.mq_concat([a])                     # one part: a copy of it
+    g1 = {k: v.cpu().numpy() for k, v in mq.mq_export_canonical(one).items()}
+    g0 = {k: v.cpu().numpy() for k, v in mq.mq_export_canonical(a).items()}
+    assert all(np.array_equal(g1[k], g0[k]) for k in g0)
+    one.free()
     for p in (a, b, d, blk):
         p.free()

@@ -188,13 +188,15 @@ def test_linear_a4_decode_layer_11008x4096(mq):
 # to its limit of 4096, K not a multiple of 128, a wave without tiles (K <
 # 1024), and a NaN group
 FUSED = [(40, 4096, 128, 0.0), (4100, 4096, 64, 0.1), (8200, 1024, 32, 0.0), (12300, 512, 128, 0.05),
-         (300, 4096, 128, 0.2), (90, 320, 64, 0.2), (16, 4096, 32, 0.0), (11008, 4096, 128, 0.1)]
+         (300, 4096, 128, 0.2), (90, 320, 64, 0.2), (16, 4096, 32, 0.0), (11008, 4096, 128, 0.1),
+         (64, 1024, 128, -1.0)]   # -1: a block handle with no block selected
 
 
 @pytest.mark.parametrize("N,K,G,beta", FUSED)
 def test_decode_a4_equals_quantizer_and_linear(mq, N, K, G, beta):
     W = _layer(N, K, 3 * N + K)
-    if beta > 0:
+    if beta != 0:
+        beta = max(beta, 0.0)
         rng = np.random.default_rng(N + 5)
         Xc = rng.standard_normal((32, K)).astype(np.float16)
         h = ob.hessian_diag(Xc)
