@@ -130,7 +130,7 @@ def replay_spread(torch, fn, warmup, steps, reps=9):
     return float(np.median(out)), float(np.percentile(out, 10)), float(np.percentile(out, 90))
 
 
-DECODE_SOURCES = ("gemv.hip", "kernel_common.h", "mq_internal.h")
+DECODE_SOURCES = ("gemv.hip", "gemv_group.h", "kernel_common.h", "mq_internal.h")
 MID_SOURCES = ("gemm_mid.hip", "kernel_common.h", "mq_internal.h")
 PREFILL_SOURCES = ("gemm.hip", "gemm_rw.hip", "kernel_common.h", "mq_internal.h")
 STREAM_SOURCES = ("probe.hip",)
@@ -151,6 +151,27 @@ def counted_traffic(kernel_tag):
     taken on other kernel sources."""
     v = profile_values("decode_hbm_counters.txt", DECODE_SOURCES).get(f"hbm_bytes_per_launch[{kernel_tag}]")
     return float(v) if v else None
+
+
+def sha256_of(a) -> str:
+    """SHA-256 of a generated host array's bytes (C order), so a run names
+    the exact inputs it timed."""
+    import numpy as np
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def host_cpu() -> dict:
+    """The host CPU model and the cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
 
 
 def profile_values(name, sources):
@@ -224,7 +245,10 @@ class ClockSampler:
 def bench_decode(args, mq, synth, torch):
     wl = synth.WORKLOADS["decode-11008x4096"]
     layer = wl.layers[0]
-    W = torch.from_numpy(layer.W()).cuda()
+    W_host = layer.W()
+    shas = {"W": sha256_of(W_host)}
+    W = torch.from_numpy(W_host).cuda()
+    del W_host
     # packing, timed on its own (GPU events around mq_pack, which ends with a sync)
     t0 = time.perf_counter()
     first = mq.mq_pack(W, layer.group, layer.rho)
@@ -241,7 +265,9 @@ def bench_decode(args, mq, synth, torch):
         copies.append(mq.mq_pack(W, layer.group, layer.rho))
     del W
     Ms = list(wl.batch)
-    Xs = {M: torch.from_numpy(layer.X(M)).cuda() for M in Ms}
+    X_host = {M: layer.X(M) for M in Ms}
+    shas.update({f"X[M={M}]": sha256_of(x) for M, x in X_host.items()})
+    Xs = {M: torch.from_numpy(x).cuda() for M, x in X_host.items()}
     Ys = {M: torch.empty((M, layer.N), dtype=torch.float16, device="cuda") for M in Ms}
 
     def step(i):
@@ -301,14 +327,17 @@ def bench_decode(args, mq, synth, torch):
         "layer": layer, "first": first, "ms_per_step": ms / args.steps, "bytes_step": bytes_step,
         "launches_per_step": len(Ms), "per_m": per_m, "pack_ms": pack_ms, "pack_wall_ms": pack_wall_ms,
         "copies": ncopy, "warm_us_m1": warm_ms * 1e3, "nnz": first.nnz, "overhead": overhead,
-        "unfused": unfused, "handle": handle,
+        "unfused": unfused, "handle": handle, "inputs_sha256": shas,
     }
 
 
 def bench_prefill(args, mq, synth, torch):
     wl = synth.WORKLOADS["prefill-28672x8192"]
     layer = wl.layers[0]
-    W = torch.from_numpy(layer.W()).cuda()
+    W_host = layer.W()
+    shas = {"W": sha256_of(W_host)}
+    W = torch.from_numpy(W_host).cuda()
+    del W_host
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     p = mq.mq_pack(W, layer.group, layer.rho)
@@ -318,8 +347,11 @@ def bench_prefill(args, mq, synth, torch):
     del W
     out = {"workload": wl.name, "N": layer.N, "K": layer.K, "rho": layer.rho, "nnz": p.nnz,
            "pack_ms": round(pack_ms, 3), "M": {}}
+    out["inputs_sha256"] = shas
     for M in wl.batch:
-        X = torch.from_numpy(layer.X(M)).cuda()
+        X_host = layer.X(M)
+        shas[f"X[M={M}]"] = sha256_of(X_host)
+        X = torch.from_numpy(X_host).cuda()
         Y = torch.empty((M, layer.N), dtype=torch.float16, device="cuda")
         n = max(3, min(args.steps, 50))
 
@@ -330,7 +362,10 @@ def bench_prefill(args, mq, synth, torch):
             ms = time_events(run, n) / n
         tflops = 2.0 * M * layer.N * layer.K / (ms * 1e-3) / 1e12
         out["M"][str(M)] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tflops, 1),
-                            "frac_mfma_peak": round(tflops / FP16_PEAK_TFLOPS, 4), "sclk": clk.summary()}
+                            "frac_mfma_peak": round(tflops / FP16_PEAK_TFLOPS, 4), "sclk": clk.summary(),
+                            # the sparse residual's own multiply-adds, not in 2 M N K: the kernel
+                            # folds the residual into the weight tile, so it issues no MFMA work for them
+                            "residual_GFLOP": round(2.0 * M * p.nnz / 1e9, 4)}
     p.free()
     # roofline of the GEMM at the largest M: achieved TFLOP/s against the
     # dense fp16 MFMA peak, with the matrix-core busy fraction and the clock
@@ -387,7 +422,9 @@ def bench_prefill(args, mq, synth, torch):
 def bench_block(args, mq, synth, torch):
     """The seven linears of one 4096-hidden block at M = 16, back to back on
     one stream (one step = 7 launches), rotated over enough packed copies
-    that the Infinity Cache cannot hold them."""
+    that the Infinity Cache cannot hold them; then the same step with the
+    layers of K = 4096 in one mq_linear_group launch, and with the layers
+    that read one input joined by mq_concat (with and without the group)."""
     wl = synth.WORKLOADS["block-4096h"]
     M = wl.batch[0]
     first = []
@@ -417,6 +454,22 @@ def bench_block(args, mq, synth, torch):
     # by mq_concat (q, k, v; and gate, up, or not): fewer launches per step,
     # each group reading its input once. Every layer keeps its own packing.
     names = [layer.name for layer in wl.layers]
+    # The six layers of K = 4096, each with its own input and handle, in one
+    # mq_linear_group launch; the down projection (K = 11008) on its own
+    k4 = [i for i, layer in enumerate(wl.layers) if layer.K == 4096]
+    kr = [i for i in range(len(wl.layers)) if i not in k4]
+
+    def step_group(i):
+        c = copies[i % ncopy]
+        mq.mq_linear_group([Xs[j] for j in k4], [c[j] for j in k4], [Ys[j] for j in k4])
+        for j in kr:
+            mq.mq_linear(Xs[j], c[j], Ys[j])
+    gmed, gp10, gp90 = replay_spread(torch, step_group, max(2, args.warmup // 4), max(10, args.steps // 4))
+    grouped = {" ".join(names[j] for j in k4) + " grouped, down": {
+        "launches_per_step": 1 + len(kr), "us": round(gmed * 1e3, 2), "p10_us": round(gp10 * 1e3, 2),
+        "p90_us": round(gp90 * 1e3, 2), "GBps": round(nbytes / (gmed * 1e-3) / 1e9, 1),
+        "frac_hbm": round(nbytes / (gmed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes,
+        "speedup_vs_separate": round(med / gmed, 3)}}
     joined = {}
     for groups in ([["q", "k", "v"], ["o"], ["gate", "up"], ["down"]],
                    [["q", "k", "v"], ["o"], ["gate"], ["up"], ["down"]]):
@@ -434,6 +487,24 @@ def bench_block(args, mq, synth, torch):
         fmed, fp10, fp90 = replay_spread(torch, step_fused, max(2, args.warmup // 4), max(10, args.steps // 4))
         fbytes = sum(p.canonical_bytes() + 2 * M * p.N for p in first) + sum(
             2 * M * wl.layers[names.index(g[0])].K for g in groups)
+        if len(groups) == 4:
+            # the joined K = 4096 layers in one mq_linear_group launch, the
+            # down projection on its own
+            gk = [gi for gi, g in enumerate(groups) if wl.layers[names.index(g[0])].K == 4096]
+            go = [gi for gi in range(len(groups)) if gi not in gk]
+
+            def step_fg(i, groups=groups, fused=fused, Xg=Xg, Yg=Yg):
+                c, fc = copies[i % ncopy], fused[i % ncopy]
+                hs = [fc[gi] if fc[gi] is not None else c[names.index(g[0])] for gi, g in enumerate(groups)]
+                mq.mq_linear_group([Xg[gi] for gi in gk], [hs[gi] for gi in gk], [Yg[gi] for gi in gk])
+                for gi in go:
+                    mq.mq_linear(Xg[gi], hs[gi], Yg[gi])
+            gmed, gp10, gp90 = replay_spread(torch, step_fg, max(2, args.warmup // 4), max(10, args.steps // 4))
+            grouped[" ".join("+".join(groups[gi]) for gi in gk) + " grouped, down"] = {
+                "launches_per_step": 1 + len(go), "us": round(gmed * 1e3, 2), "p10_us": round(gp10 * 1e3, 2),
+                "p90_us": round(gp90 * 1e3, 2), "GBps": round(fbytes / (gmed * 1e-3) / 1e9, 1),
+                "frac_hbm": round(fbytes / (gmed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": fbytes,
+                "speedup_vs_separate": round(med / gmed, 3)}
         for fc in fused:
             for p in fc:
                 if p is not None:
@@ -449,7 +520,7 @@ def bench_block(args, mq, synth, torch):
     return {"workload": wl.name, "M": M, "launches_per_step": len(wl.layers), "packed_copies": ncopy,
             "us": round(med * 1e3, 2), "p10_us": round(p10 * 1e3, 2), "p90_us": round(p90 * 1e3, 2),
             "GBps": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes": nbytes, "shared_input_joined": joined}
+            "bytes": nbytes, "shared_input_joined": joined, "grouped_launch": grouped}
 
 
 def bench_sweep(args, mq, synth, torch):
@@ -815,6 +886,7 @@ def cpu_baseline(layer, Ms, min_seconds=10.0, max_steps=60):
              + 2 * packed["nnz"] + (packed["nnz"] + 1) // 2 + 4 * layer.N)
     nbytes = steps * sum(canon + 2 * M * layer.K + 2 * M * layer.N for M in Ms)
     return {"value": round(nbytes / t_lin / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            **host_cpu(),
             "sample": f"{steps} steps of the oracle's dequant + float64 linear of the full {layer.N}x{layer.K} "
                       f"layer at M={Ms}; the oracle's pack of the layer ({t_pack:.1f} s) is not included",
             "seconds": round(t_lin, 3), "steps": steps, "pack_seconds": round(t_pack, 2)}
@@ -842,7 +914,7 @@ def cpu_baseline_configs(synth):
         r = fn()
         return r, time.perf_counter() - t0
 
-    out = {"cores": int(threads), "kind": "oracle"}
+    out = {"cores": int(threads), "kind": "oracle", **host_cpu()}
     # block-4096h at M = 16
     wl = synth.WORKLOADS["block-4096h"]
     M = wl.batch[0]
@@ -986,6 +1058,7 @@ def main():
         "decode_unfused_two_kernels": d["unfused"],
         "decode_warm_single_copy_us_M1": None if args.no_warm else round(d["warm_us_m1"], 3),
         "handle_device_bytes": d["handle"],
+        "inputs_sha256": d["inputs_sha256"],
         "pack": {"workload": "decode-11008x4096", "gpu_ms": round(d["pack_ms"], 3),
                  "wall_ms_first_call": round(d["pack_wall_ms"], 3)},
     }

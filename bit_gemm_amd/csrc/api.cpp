@@ -11,6 +11,7 @@
 #include <unordered_set>
 
 #include "mq_internal.h"
+#include "gemv_group.h"
 
 #define MQ_API extern "C" __attribute__((visibility("default")))
 
@@ -331,6 +332,39 @@ MQ_API mq_status mq_linear_noalloc(const void* X_dev_fp16, int64_t M, const mq_p
   if (mq::auto_gemv(p, M)) return from_hip(mq::launch_gemv(p, X, M, Y, s));   // no workspace on this path
   if (mq::gemm_workspace_bytes(p, M) > mq::gemm_scratch_capacity()) return MQ_ERR_UNSUPPORTED;
   return from_hip(mq::launch_gemm_noalloc(p, X, M, Y, s));
+}
+
+// n layers, each with its own input: one launch of the grouped decode kernel
+// per run of up to kGroupMax layers when they all qualify, else mq_linear per
+// layer. Everything is validated before the first launch.
+MQ_API mq_status mq_linear_group(const void* const* X_dev_fp16, int64_t M, const mq_packed* const* p,
+                                 void* const* Y_dev_fp16, int32_t n, void* hip_stream) {
+  if (!X_dev_fp16 || !p || !Y_dev_fp16 || n < 1 || M <= 0) return MQ_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!is_live(p[i])) return MQ_ERR_BAD_HANDLE;
+    if (!X_dev_fp16[i] || !Y_dev_fp16[i]) return MQ_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(X_dev_fp16[i]) & 15u) != 0 || (reinterpret_cast<uintptr_t>(Y_dev_fp16[i]) & 7u) != 0)
+      return MQ_ERR_INVALID_ARG;
+    if (M > (int64_t(1) << 31) / p[i]->K || M > (int64_t(1) << 31) / p[i]->N) return MQ_ERR_UNSUPPORTED;
+  }
+  bool grouped = true;
+  for (int32_t i0 = 0; i0 < n && grouped; i0 += mq::kGroupMax)
+    grouped = mq::gemv_group_takes(p + i0, std::min<int32_t>(mq::kGroupMax, n - i0), M);
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (grouped) {
+    for (int32_t i0 = 0; i0 < n; i0 += mq::kGroupMax) {
+      const mq_status st = from_hip(mq::launch_gemv_group(
+          p + i0, reinterpret_cast<const uint16_t* const*>(X_dev_fp16 + i0), M,
+          reinterpret_cast<uint16_t* const*>(Y_dev_fp16 + i0), std::min<int32_t>(mq::kGroupMax, n - i0), s));
+      if (st != MQ_OK) return st;
+    }
+    return MQ_OK;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const mq_status st = linear_impl(X_dev_fp16[i], M, p[i], Y_dev_fp16[i], hip_stream, MQ_KERNEL_AUTO);
+    if (st != MQ_OK) return st;
+  }
+  return MQ_OK;
 }
 
 // Row-wise concatenation of element-wise (or residual-free) handles; see

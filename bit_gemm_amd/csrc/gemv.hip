@@ -18,6 +18,7 @@
 //   * the 8 partial 16 x M tiles are summed in LDS in a fixed order.
 #include "kernel_common.h"
 #include "mq_internal.h"
+#include "gemv_group.h"
 
 namespace mq {
 namespace {
@@ -627,16 +628,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 
 // residual chunks of all R row blocks before computing anything. The row
 // blocks are computed in order (residual chunks gather their X columns from
 // LDS) and the 8 partials of each are summed in LDS in a fixed order.
+// The workgroup's body: row blocks rb0 .. rb0 + R - 1 of one layer.
 template <int GSH, int XR, int R, bool DR>
-__global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles, const uint16_t* __restrict__ scales,
-                                               int sstride, const uint32_t* __restrict__ tile_ptr,
-                                               const uint32_t* __restrict__ entries, const uint16_t* __restrict__ X,
-                                               uint16_t* __restrict__ Y, int M, int N, int Nb, int zero_off,
-                                               DenseRes D) {
+__device__ __forceinline__ void gemv_r_block(const uint4* tiles, const uint16_t* scales, int sstride,
+                                             const uint32_t* tile_ptr, const uint32_t* entries, const uint16_t* X,
+                                             uint16_t* Y, int M, int N, int Nb, int zero_off, DenseRes D,
+                                             const int rb0) {
   constexpr int KS = 8, TPW = 4, K = 4096, Kt = 32, NS = 1 << GSH, LDX = K + kXPad;
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][LDX], then the partials [R][KS][64]
   static_assert(R * KS * 64 * sizeof(float4_t) <= XR * LDX * sizeof(uint16_t), "partials fit in the X space");
-  const int rb0 = blockIdx.x * R;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int kt0 = wave * TPW, c0 = kt0 * kTileCols;
@@ -777,6 +777,48 @@ __global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles,
     const int n0 = rb * kRowsPerBlock + 4 * g;
     if (r < M) store4(Y + (int64_t)r * N + n0, sum, N - n0, (N & 3) == 0);
   }
+}
+
+template <int GSH, int XR, int R, bool DR>
+__global__ __launch_bounds__(512) void k_gemv_r(const uint4* __restrict__ tiles, const uint16_t* __restrict__ scales,
+                                               int sstride, const uint32_t* __restrict__ tile_ptr,
+                                               const uint32_t* __restrict__ entries, const uint16_t* __restrict__ X,
+                                               uint16_t* __restrict__ Y, int M, int N, int Nb, int zero_off,
+                                               DenseRes D) {
+  gemv_r_block<GSH, XR, R, DR>(tiles, scales, sstride, tile_ptr, entries, X, Y, M, N, Nb, zero_off, D,
+                               blockIdx.x * R);
+}
+
+// Several layers of K = 4096 (element-wise or no residual, one group size)
+// with inputs of the same token count in one launch: layer i owns
+// workgroups wg0[i] .. wg0[i + 1] - 1, each of R of its row blocks, which
+// are computed exactly as k_gemv_r computes them (the same sums in the same
+// order), so each output equals that layer's own launch bit for bit. More
+// row blocks per workgroup than one small layer can fill amortise the copy
+// of X into LDS (at 16 tokens as many bytes per workgroup as 4 row blocks
+// of codes), and the layers' ramps and tails overlap.
+struct GroupR {
+  const uint4* tiles[kGroupMax];
+  const uint16_t* scales[kGroupMax];
+  const uint32_t* tile_ptr[kGroupMax];
+  const uint32_t* entries[kGroupMax];
+  const uint16_t* X[kGroupMax];
+  uint16_t* Y[kGroupMax];
+  int sstride[kGroupMax], N[kGroupMax], Nb[kGroupMax], zero_off[kGroupMax];
+  int wg0[kGroupMax + 1];   // first workgroup of each layer; wg0[n] = the grid
+  int n;
+};
+
+template <int GSH, int XR, int R>
+__global__ __launch_bounds__(512) void k_gemv_r_group(const GroupR G, int M) {
+  const int b = (int)blockIdx.x;
+  int li = 0;
+#pragma unroll
+  for (int i = 1; i < kGroupMax; ++i) li += (i < G.n && b >= G.wg0[i]) ? 1 : 0;
+  li = __builtin_amdgcn_readfirstlane(li);
+  const DenseRes none{nullptr, nullptr, nullptr, nullptr, 0u};
+  gemv_r_block<GSH, XR, R, false>(G.tiles[li], G.scales[li], G.sstride[li], G.tile_ptr[li], G.entries[li], G.X[li],
+                                  G.Y[li], M, G.N[li], G.Nb[li], G.zero_off[li], none, (b - G.wg0[li]) * R);
 }
 
 // General decode kernel. KS waves per row block. GSH = log2(128 / G).
@@ -1029,6 +1071,50 @@ hipError_t launch_r_any(const mq_packed* p, const uint16_t* X, int M, uint16_t* 
   }
 }
 
+template <int GSH, int XR, int R>
+hipError_t launch_r_group(const GroupR& G, int grid, int M, hipStream_t s) {
+  static bool done = false;
+  if (!done) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_r_group<GSH, XR, R>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMaxBytes);
+    if (e != hipSuccess) return e;
+    done = true;
+  }
+  k_gemv_r_group<GSH, XR, R><<<dim3((unsigned)grid), dim3(512), (size_t)XR * (4096 + kXPad) * 2, s>>>(G, M);
+  return hipGetLastError();
+}
+
+template <int GSH, int XR>
+hipError_t launch_r_group_any(GroupR& G, int M, hipStream_t s) {
+  // as in launch_r_any, row blocks per workgroup so that the group fills one
+  // round of workgroups, and the most that fit the registers (4, or 2 when
+  // G = 32) when it takes more than one: each workgroup copies X once
+  constexpr int kRmax = GSH == 2 ? 2 : 4;
+  auto fill = [&](int R) {
+    int wg = 0;
+    for (int i = 0; i < G.n; ++i) {
+      G.wg0[i] = wg;
+      wg += (G.Nb[i] + R - 1) / R;
+    }
+    for (int i = G.n; i <= kGroupMax; ++i) G.wg0[i] = wg;
+    return wg;
+  };
+  int grid = fill(1);
+  if (grid <= 256) return launch_r_group<GSH, XR, 1>(G, grid, M, s);
+  grid = fill(2);
+  if (grid <= 256 || kRmax == 2) return launch_r_group<GSH, XR, 2>(G, grid, M, s);
+  if constexpr (kRmax == 4) {
+    grid = fill(4);
+    return launch_r_group<GSH, XR, 4>(G, grid, M, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int GSH>
+hipError_t launch_group_g(GroupR& G, int M, hipStream_t s) {
+  return M <= 8 ? launch_r_group_any<GSH, 8>(G, M, s) : launch_r_group_any<GSH, 16>(G, M, s);
+}
+
 // XL: X copied whole into LDS ([M][K + kXPad], at most kXldsMax bytes)
 template <int KS, int MB, int GSH, int XL, bool MWV, int TPW>
 hipError_t launch(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
@@ -1099,6 +1185,35 @@ hipError_t run_g(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipS
 }
 
 }  // namespace
+
+bool gemv_group_takes(const mq_packed* const* p, int n, int64_t M) {
+  if (n < 1 || n > kGroupMax || M < 5 || M > 16) return false;
+  for (int i = 0; i < n; ++i)
+    if (p[i]->K != 4096 || p[i]->blocks || p[i]->G != p[0]->G || p[i]->device != p[0]->device) return false;
+  return true;
+}
+
+hipError_t launch_gemv_group(const mq_packed* const* p, const uint16_t* const* X, int64_t M, uint16_t* const* Y,
+                             int n, hipStream_t s) {
+  if (!gemv_group_takes(p, n, M)) return hipErrorInvalidValue;
+  GroupR G{};
+  G.n = n;
+  for (int i = 0; i < n; ++i) {
+    G.tiles[i] = reinterpret_cast<const uint4*>(p[i]->tiles);
+    G.scales[i] = p[i]->scales;
+    G.tile_ptr[i] = p[i]->tile_ptr;
+    G.entries[i] = p[i]->entries;
+    G.X[i] = X[i];
+    G.Y[i] = Y[i];
+    G.sstride[i] = (int)p[i]->sstride;
+    G.N[i] = (int)p[i]->N;
+    G.Nb[i] = (int)p[i]->Nb;
+    G.zero_off[i] = (int)p[i]->stream_cap;
+  }
+  if (p[0]->G == 128) return launch_group_g<0>(G, (int)M, s);
+  if (p[0]->G == 64) return launch_group_g<1>(G, (int)M, s);
+  return launch_group_g<2>(G, (int)M, s);
+}
 
 hipError_t launch_gemv(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {
   // Block-residual handles carry their residual as code tiles only, which

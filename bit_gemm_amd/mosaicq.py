@@ -24,7 +24,8 @@ GEMV_MAX_M = 64
 EXPORTED = ("mq_pack", "mq_linear", "mq_linear_with", "mq_linear_noalloc", "mq_residual_add", "mq_packed_info",
             "mq_export_canonical", "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks",
             "mq_smooth_weights", "mq_smooth_activations", "mq_quantize_activations", "mq_linear_a4",
-            "mq_stream_read", "mq_concat", "mq_decode_a4", "mq_free", "mq_status_string")
+            "mq_stream_read", "mq_concat", "mq_decode_a4", "mq_linear_group", "mq_free",
+            "mq_status_string")
 
 
 class MQError(RuntimeError):
@@ -75,6 +76,8 @@ def _load():
     lib.mq_decode_a4.restype = ctypes.c_int
     lib.mq_concat.argtypes = [ctypes.POINTER(vp), i32, vp, ctypes.POINTER(vp)]
     lib.mq_concat.restype = ctypes.c_int
+    lib.mq_linear_group.argtypes = [ctypes.POINTER(vp), i64, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp]
+    lib.mq_linear_group.restype = ctypes.c_int
     lib.mq_free.argtypes = [vp]
     lib.mq_free.restype = None
     lib.mq_status_string.argtypes = [ctypes.c_int]
@@ -354,6 +357,38 @@ def mq_linear_noalloc(X, packed: Packed, Y, stream=None):
         raise ValueError(f"Y must be [{M}, {packed.N}]")
     _check(lib.mq_linear_noalloc(xp, M, packed.handle, yp, _stream_handle(stream)), "mq_linear_noalloc")
     return Y
+
+
+def mq_linear_group(Xs, packs, Ys=None, stream=None):
+    """mq_linear of several layers with their own inputs (one token count),
+    one kernel launch when they can share it (see mq_linear_group in
+    include/mosaicq.h). Returns the outputs; enqueued on `stream` (no sync)."""
+    import torch
+    Xs, packs = list(Xs), list(packs)
+    if len(Xs) != len(packs) or not packs:
+        raise ValueError("one input per layer, at least one layer")
+    M = Xs[0].shape[0] if Xs[0].dim() == 2 else -1
+    xps = []
+    for X, p in zip(Xs, packs):
+        xps.append(_dev_fp16(X, "X"))
+        if X.dim() != 2 or tuple(X.shape) != (M, p.K):
+            raise ValueError(f"every X must be [{M}, K] of its layer (K = {p.K})")
+    if Ys is None:
+        Ys = [torch.empty((M, p.N), dtype=torch.float16, device=Xs[0].device) for p in packs]
+    Ys = list(Ys)
+    if len(Ys) != len(packs):
+        raise ValueError("one output per layer")
+    yps = []
+    for Y, p in zip(Ys, packs):
+        yps.append(_dev_fp16(Y, "Y"))
+        if tuple(Y.shape) != (M, p.N):
+            raise ValueError(f"every Y must be [{M}, N] of its layer (N = {p.N})")
+    n = len(packs)
+    xa = (ctypes.c_void_p * n)(*xps)
+    ha = (ctypes.c_void_p * n)(*[p.handle for p in packs])
+    ya = (ctypes.c_void_p * n)(*yps)
+    _check(lib.mq_linear_group(xa, M, ha, ya, n, _stream_handle(stream)), "mq_linear_group")
+    return Ys
 
 
 def mq_residual_add(X, packed: Packed, Y, stream=None):

@@ -118,6 +118,37 @@ mq_status mq_linear(const void* X_dev_fp16, int64_t M, const mq_packed* p,
 mq_status mq_linear_noalloc(const void* X_dev_fp16, int64_t M, const mq_packed* p, void* Y_dev_fp16,
                             void* hip_stream);
 
+/*
+ * mq_linear_group -- mq_linear for n layers at once, each with its own input
+ * (say the linears of one transformer block at decode): Y[i] = the fused
+ * W4 + sparse-residual linear of X[i] with p[i] (MosaicQuant explainer,
+ * Methodology section 3), each equal, bit for bit, to mq_linear(X[i], M, p[i],
+ * Y[i]) on the same stream. When every layer has K = 4096, no block residual
+ * (mq_pack_blocks), one group size and one device, and 5 <= M <= 16, up to 8
+ * layers run in one kernel launch (workgroups take several row blocks of one
+ * layer, so the input is copied into LDS fewer times and the layers' ramps
+ * and tails overlap); otherwise, and for more than 8 layers, the layers are
+ * launched in order as mq_linear would.
+ *
+ *   X_dev_fp16   n pointers (host array) to [M, p[i]->K] fp16 inputs (device,
+ *                16-byte aligned); inputs may be shared between layers
+ *   M            tokens of every input, M > 0
+ *   p            n live handles (host array)
+ *   Y_dev_fp16   n pointers (host array) to [M, p[i]->N] fp16 outputs
+ *                (device, 8-byte aligned, overwritten, not overlapping each
+ *                other or any input)
+ *   n            n >= 1
+ *   hip_stream   stream to enqueue on (no synchronisation)
+ *
+ * Every argument is checked before anything is enqueued. Errors:
+ * MQ_ERR_BAD_HANDLE, MQ_ERR_INVALID_ARG (NULL arrays or pointers, misaligned
+ * pointers, M <= 0, n < 1), MQ_ERR_UNSUPPORTED (as mq_linear), MQ_ERR_DEVICE,
+ * MQ_ERR_OUT_OF_MEMORY (a layer launched on its own whose GEMM needs a
+ * workspace, as mq_linear).
+ */
+mq_status mq_linear_group(const void* const* X_dev_fp16, int64_t M, const mq_packed* const* p,
+                          void* const* Y_dev_fp16, int32_t n, void* hip_stream);
+
 /* Kernel choice for mq_linear_with. */
 typedef enum { MQ_KERNEL_AUTO = 0, MQ_KERNEL_GEMV = 1, MQ_KERNEL_GEMM = 2 } mq_kernel;
 

@@ -30,8 +30,8 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["mq_pack", "mq_linear", "mq_linear_with", "mq_linear_noalloc", "mq_residual_add", "mq_stream_read", "mq_packed_info", "mq_export_canonical",
          "mq_export_tiled", "mq_pack_blocks", "mq_block_count", "mq_export_blocks", "mq_smooth_weights",
-         "mq_smooth_activations", "mq_quantize_activations", "mq_linear_a4", "mq_decode_a4", "mq_concat", "mq_free",
-         "mq_status_string"])
+         "mq_smooth_activations", "mq_quantize_activations", "mq_linear_a4", "mq_decode_a4", "mq_concat", "mq_linear_group",
+         "mq_free", "mq_status_string"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -124,6 +124,13 @@ def test_bad_handles_are_rejected(lib):
     assert lib.mq_concat(None, 2, None, ctypes.byref(out)) == -1
     assert lib.mq_concat(arr, 0, None, ctypes.byref(out)) == -1
     assert lib.mq_concat(arr, 2, None, None) == -1
+    xs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    assert lib.mq_linear_group(xs, 16, arr, xs, 2, None) == -6
+    assert lib.mq_linear_group(None, 16, arr, xs, 2, None) == -1
+    assert lib.mq_linear_group(xs, 16, arr, None, 2, None) == -1
+    assert lib.mq_linear_group(xs, 16, None, xs, 2, None) == -1
+    assert lib.mq_linear_group(xs, 16, arr, xs, 0, None) == -1
+    assert lib.mq_linear_group(xs, 0, arr, xs, 2, None) == -1
     lib.mq_free(None)        # accepted
     lib.mq_free(bogus)       # unknown handle: ignored, no crash
 
