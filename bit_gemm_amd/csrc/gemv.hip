@@ -1086,10 +1086,14 @@ hipError_t launch_r_group(const GroupR& G, int grid, int M, hipStream_t s) {
 
 template <int GSH, int XR>
 hipError_t launch_r_group_any(GroupR& G, int M, hipStream_t s) {
-  // as in launch_r_any, row blocks per workgroup so that the group fills one
-  // round of workgroups, and the most that fit the registers (4, or 2 when
-  // G = 32) when it takes more than one: each workgroup copies X once
-  constexpr int kRmax = GSH == 2 ? 2 : 4;
+  // X fills the LDS, so the workgroups run in rounds of one per CU, and a
+  // workgroup of R row blocks takes about R + 0.64 row-block times (0.64 for
+  // its copy of X): on the six K = 4096 layers of a 4096-hidden block at 16
+  // tokens (2400 row blocks), 2 / 4 / 5 row blocks per workgroup in 5 / 3 / 2
+  // rounds took 34.9 / 36.5 / 30.7 us. R is the one with the least
+  // rounds x (R + 0.64), among those that fit the registers without spills
+  // (up to 5 for G = 128, 4 for G = 64, 2 for G = 32).
+  constexpr int kRmax = GSH == 0 ? 5 : GSH == 1 ? 4 : 2;
   auto fill = [&](int R) {
     int wg = 0;
     for (int i = 0; i < G.n; ++i) {
@@ -1099,13 +1103,26 @@ hipError_t launch_r_group_any(GroupR& G, int M, hipStream_t s) {
     for (int i = G.n; i <= kGroupMax; ++i) G.wg0[i] = wg;
     return wg;
   };
-  int grid = fill(1);
-  if (grid <= 256) return launch_r_group<GSH, XR, 1>(G, grid, M, s);
-  grid = fill(2);
-  if (grid <= 256 || kRmax == 2) return launch_r_group<GSH, XR, 2>(G, grid, M, s);
-  if constexpr (kRmax == 4) {
-    grid = fill(4);
-    return launch_r_group<GSH, XR, 4>(G, grid, M, s);
+  int best_r = 1;
+  double best = 1e300;
+  for (int R = 1; R <= kRmax; ++R) {
+    const double cost = (double)((fill(R) + 255) / 256) * (R + 0.64);
+    if (cost < best) {
+      best = cost;
+      best_r = R;
+    }
+  }
+  const int grid = fill(best_r);
+  switch (best_r) {
+    case 1: return launch_r_group<GSH, XR, 1>(G, grid, M, s);
+    case 2: return launch_r_group<GSH, XR, 2>(G, grid, M, s);
+  }
+  if constexpr (kRmax >= 4) {
+    if (best_r == 3) return launch_r_group<GSH, XR, 3>(G, grid, M, s);
+    if (best_r == 4) return launch_r_group<GSH, XR, 4>(G, grid, M, s);
+  }
+  if constexpr (kRmax >= 5) {
+    if (best_r == 5) return launch_r_group<GSH, XR, 5>(G, grid, M, s);
   }
   return hipErrorInvalidValue;
 }

@@ -1,8 +1,8 @@
 """mq_linear_group: several layers, each with its own input, in one call. Every
 output must equal that layer's own mq_linear bit for bit, whether the layers
 share one launch (K = 4096, 5..16 tokens, one group size, no block residual:
-row blocks per workgroup 1, 2 or 4 by the group's total rows) or fall back to
-launches of their own; one small group is also checked against the float64
+1 to 5 row blocks per workgroup, by the group's rows and group size) or fall
+back to launches of their own; one small group is also checked against the float64
 oracle of the dequantised weights."""
 import ctypes
 
@@ -54,8 +54,8 @@ def _check_equal_to_single(mq, packs, Xs_host, what):
 
 
 # the seven linears of a 4096-hidden block but the down projection (K = 11008):
-# 2400 row blocks, four per workgroup; one layer without residual, one with
-# dense outlier rows
+# 2400 row blocks, five per workgroup (two rounds of 240 workgroups); one
+# layer without residual, one with dense outlier rows
 BLOCK = [(4096, 0.005, ()), (4096, 0.005, ()), (4096, 0.0, ()), (4096, 0.005, (7, 8, 100)),
          (11008, 0.005, ()), (11008, 0.005, ())]
 
@@ -68,12 +68,18 @@ def test_block_group_equals_single_launches(mq, M):
         p.free()
 
 
-# (spec, group size): 194 row blocks (one per workgroup; ragged layers),
-# 319 (two per workgroup), and G = 32 (at most two per workgroup) with 832
+# (spec, group size) and the row blocks per workgroup the launcher picks:
+# 194 row blocks (1; ragged layers), 319 (2), 831 at G = 64 (4) and at
+# G = 32 (2, the most that G = 32 takes), one layer of 688 row blocks (3)
+FOUR = [(4096, 0.005, ()), (4096, 0.003, ()), (4096, 0.0, ()), (1000, 0.01, (999,))]
+
+
 @pytest.mark.parametrize("spec,G", [
     ([(2048, 0.01, ()), (1000, 0.004, (3,)), (40, 0.02, ())], 128),
     ([(4096, 0.005, ()), (1000, 0.0, ())], 64),
-    ([(4096, 0.005, ()), (4096, 0.003, ()), (4096, 0.0, ()), (1000, 0.01, (999,))], 32),
+    (FOUR, 64),
+    (FOUR, 32),
+    ([(11008, 0.005, (11000,))], 128),
 ])
 @pytest.mark.parametrize("M", [6, 13])
 def test_group_shapes_equal_single_launches(mq, spec, G, M):
