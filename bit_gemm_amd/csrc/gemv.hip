@@ -1039,6 +1039,29 @@ hipError_t launch_x_res(const mq_packed* p, const uint16_t* X, int M, uint16_t* 
   return lst ? launch_x<GSH, XR, false, 256, true>(p, X, M, Y, s) : launch_x<GSH, XR, false, 256, false>(p, X, M, Y, s);
 }
 
+// Row blocks per workgroup of the K = 4096 decode body over layers of nb[i]
+// row blocks. X fills the LDS, so the workgroups run in rounds of one per
+// CU, and a workgroup of R row blocks takes about R + 0.64 row-block times
+// (0.64 for its copy of X): on the six K = 4096 layers of a 4096-hidden
+// block at 16 tokens (2400 row blocks), 2 / 4 / 5 row blocks per workgroup
+// in 5 / 3 / 2 rounds took 34.9 / 36.5 / 30.7 us. The pick is the R with the
+// least rounds x (R + 0.64) up to rmax, the most that fit the registers
+// without spills (5 for G = 128, 4 for G = 64, 2 for G = 32).
+int rows_per_workgroup(const int* nb, int n, int rmax) {
+  int best_r = 1;
+  double best = 1e300;
+  for (int R = 1; R <= rmax; ++R) {
+    int wg = 0;
+    for (int i = 0; i < n; ++i) wg += (nb[i] + R - 1) / R;
+    const double cost = (double)((wg + 255) / 256) * (R + 0.64);
+    if (cost < best) {
+      best = cost;
+      best_r = R;
+    }
+  }
+  return best_r;
+}
+
 template <int GSH, int XR, int R, bool DR>
 hipError_t launch_r(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
   static bool done = false;
@@ -1058,7 +1081,9 @@ hipError_t launch_r(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, h
 // Row blocks per workgroup: X fills the LDS, so one workgroup runs per CU,
 // and ceil(Nb / 256) row blocks each make one round of workgroups (a few
 // workgroups past 256 would take a second round on their own). Up to 4 row
-// blocks fit the registers, 2 when G = 32 (4 scales per tile and row).
+// blocks fit the registers, 2 when G = 32 (4 scales per tile and row); past
+// one round of 4 (layers of more than 16384 rows) the rounds model of
+// rows_per_workgroup picks, with 5 for G = 128 (block residuals keep 4).
 template <int GSH, int XR, bool DR>
 hipError_t launch_r_any(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipStream_t s) {
   if (p->Nb <= 256) return launch_r<GSH, XR, 1, DR>(p, X, M, Y, s);
@@ -1067,6 +1092,19 @@ hipError_t launch_r_any(const mq_packed* p, const uint16_t* X, int M, uint16_t* 
   } else {
     if (p->Nb <= 512) return launch_r<GSH, XR, 2, DR>(p, X, M, Y, s);
     if (p->Nb <= 768) return launch_r<GSH, XR, 3, DR>(p, X, M, Y, s);
+    if constexpr (!DR) {
+      if (p->Nb > 1024) {
+        const int nb = (int)p->Nb;
+        switch (rows_per_workgroup(&nb, 1, GSH == 0 ? 5 : 4)) {
+          case 1: return launch_r<GSH, XR, 1, DR>(p, X, M, Y, s);
+          case 2: return launch_r<GSH, XR, 2, DR>(p, X, M, Y, s);
+          case 3: return launch_r<GSH, XR, 3, DR>(p, X, M, Y, s);
+          case 5:
+            if constexpr (GSH == 0) return launch_r<GSH, XR, 5, DR>(p, X, M, Y, s);
+            break;
+        }
+      }
+    }
     return launch_r<GSH, XR, 4, DR>(p, X, M, Y, s);
   }
 }
@@ -1086,43 +1124,24 @@ hipError_t launch_r_group(const GroupR& G, int grid, int M, hipStream_t s) {
 
 template <int GSH, int XR>
 hipError_t launch_r_group_any(GroupR& G, int M, hipStream_t s) {
-  // X fills the LDS, so the workgroups run in rounds of one per CU, and a
-  // workgroup of R row blocks takes about R + 0.64 row-block times (0.64 for
-  // its copy of X): on the six K = 4096 layers of a 4096-hidden block at 16
-  // tokens (2400 row blocks), 2 / 4 / 5 row blocks per workgroup in 5 / 3 / 2
-  // rounds took 34.9 / 36.5 / 30.7 us. R is the one with the least
-  // rounds x (R + 0.64), among those that fit the registers without spills
-  // (up to 5 for G = 128, 4 for G = 64, 2 for G = 32).
   constexpr int kRmax = GSH == 0 ? 5 : GSH == 1 ? 4 : 2;
-  auto fill = [&](int R) {
-    int wg = 0;
-    for (int i = 0; i < G.n; ++i) {
-      G.wg0[i] = wg;
-      wg += (G.Nb[i] + R - 1) / R;
-    }
-    for (int i = G.n; i <= kGroupMax; ++i) G.wg0[i] = wg;
-    return wg;
-  };
-  int best_r = 1;
-  double best = 1e300;
-  for (int R = 1; R <= kRmax; ++R) {
-    const double cost = (double)((fill(R) + 255) / 256) * (R + 0.64);
-    if (cost < best) {
-      best = cost;
-      best_r = R;
-    }
+  const int R = rows_per_workgroup(G.Nb, G.n, kRmax);
+  int wg = 0;
+  for (int i = 0; i < G.n; ++i) {
+    G.wg0[i] = wg;
+    wg += (G.Nb[i] + R - 1) / R;
   }
-  const int grid = fill(best_r);
-  switch (best_r) {
-    case 1: return launch_r_group<GSH, XR, 1>(G, grid, M, s);
-    case 2: return launch_r_group<GSH, XR, 2>(G, grid, M, s);
+  for (int i = G.n; i <= kGroupMax; ++i) G.wg0[i] = wg;
+  switch (R) {
+    case 1: return launch_r_group<GSH, XR, 1>(G, wg, M, s);
+    case 2: return launch_r_group<GSH, XR, 2>(G, wg, M, s);
   }
   if constexpr (kRmax >= 4) {
-    if (best_r == 3) return launch_r_group<GSH, XR, 3>(G, grid, M, s);
-    if (best_r == 4) return launch_r_group<GSH, XR, 4>(G, grid, M, s);
+    if (R == 3) return launch_r_group<GSH, XR, 3>(G, wg, M, s);
+    if (R == 4) return launch_r_group<GSH, XR, 4>(G, wg, M, s);
   }
   if constexpr (kRmax >= 5) {
-    if (best_r == 5) return launch_r_group<GSH, XR, 5>(G, grid, M, s);
+    if (R == 5) return launch_r_group<GSH, XR, 5>(G, wg, M, s);
   }
   return hipErrorInvalidValue;
 }

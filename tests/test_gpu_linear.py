@@ -142,6 +142,28 @@ def _longest_row_block(ref, N):
     return int((blk + (-blk) % 32).max())
 
 
+@pytest.mark.parametrize("N,G", [(17000, 128), (17000, 64), (22016, 128)])
+def test_decode_wide_layers(mq, N, G):
+    """Layers of more than 16384 rows at K = 4096 and 5..16 tokens: the decode
+    kernel takes 5 (G = 128) or 3 (G = 64) row blocks per workgroup on 1063
+    row blocks (the last workgroup part-filled, the last row block ragged),
+    and 3 on 1376 (two rounds of workgroups), from its rounds model."""
+    K, rho = 4096, 0.005
+    rng = np.random.default_rng(N + G)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, rng.choice(K, 8, replace=False)] *= 20
+    W = W.astype(np.float16)
+    ref = oracle.pack(W, G, rho)
+    p = mq.mq_pack(to_dev(W), G, rho)
+    Wt = oracle.dequant(ref)
+    for M in (5, 16):
+        X = _x(M, K, seed=300 + M)
+        print(f"[wide decode] N={N} G={G} M={M}", flush=True)
+        Y = mq.mq_linear(to_dev(X), p).cpu().numpy()
+        check_linear(Y, X, Wt, f"wide decode N={N} G={G} M={M}")
+    p.free()
+
+
 @pytest.mark.parametrize("N,rows,nnz,staged",
                          [(64, (20,), 2400, 64), (64, (20, 40, 41, 42), 16000, 256), (1088, (), 68 * 3277, 256)])
 def test_decode_dense_row_blocks(mq, N, rows, nnz, staged):
