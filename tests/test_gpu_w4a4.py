@@ -70,8 +70,10 @@ def _check_quant(mq, X, G):
     return qx, sx
 
 
+# the last three: more than 16000 (token, tile) units, ragged K in the last
+# two, the last workgroup part-filled in all three
 QSHAPES = [(1, 128, 128), (5, 256, 64), (37, 384, 32), (16, 4160, 64), (3, 8256, 32), (64, 4096, 128),
-           (130, 1024, 128), (2, 65536, 128)]
+           (130, 1024, 128), (2, 65536, 128), (300, 8320, 128), (520, 4160, 64), (257, 8256, 32)]
 
 
 @pytest.mark.parametrize("M,K,G", QSHAPES)
