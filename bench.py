@@ -470,6 +470,28 @@ def bench_block(args, mq, synth, torch):
         "p90_us": round(gp90 * 1e3, 2), "GBps": round(nbytes / (gmed * 1e-3) / 1e9, 1),
         "frac_hbm": round(nbytes / (gmed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes,
         "speedup_vs_separate": round(med / gmed, 3)}}
+    # the same two steps with one token per linear (batch-1 decode)
+    X1 = [torch.from_numpy(layer.X(1)).cuda() for layer in wl.layers]
+    Y1 = [torch.empty((1, layer.N), dtype=torch.float16, device="cuda") for layer in wl.layers]
+
+    def step_m1(i):
+        c = copies[i % ncopy]
+        for x, p, y in zip(X1, c, Y1):
+            mq.mq_linear(x, p, y)
+
+    def step_m1_group(i):
+        c = copies[i % ncopy]
+        mq.mq_linear_group([X1[j] for j in k4], [c[j] for j in k4], [Y1[j] for j in k4])
+        for j in kr:
+            mq.mq_linear(X1[j], c[j], Y1[j])
+    # (calls, not launches: at one token a layer with a row block of more
+    # than 16 residual chunks runs on its own inside mq_linear_group)
+    m1 = {}
+    for tag, fn, calls in (("7 launches", step_m1, len(wl.layers)),
+                           (" ".join(names[j] for j in k4) + " grouped, down", step_m1_group, 1 + len(kr))):
+        t1 = replay_spread(torch, fn, max(2, args.warmup // 4), max(10, args.steps // 4))
+        m1[tag] = {"calls_per_step": calls, "us": round(t1[0] * 1e3, 2), "p10_us": round(t1[1] * 1e3, 2),
+                   "p90_us": round(t1[2] * 1e3, 2)}
     joined = {}
     for groups in ([["q", "k", "v"], ["o"], ["gate", "up"], ["down"]],
                    [["q", "k", "v"], ["o"], ["gate"], ["up"], ["down"]]):
@@ -520,7 +542,7 @@ def bench_block(args, mq, synth, torch):
     return {"workload": wl.name, "M": M, "launches_per_step": len(wl.layers), "packed_copies": ncopy,
             "us": round(med * 1e3, 2), "p10_us": round(p10 * 1e3, 2), "p90_us": round(p90 * 1e3, 2),
             "GBps": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes": nbytes, "shared_input_joined": joined, "grouped_launch": grouped}
+            "bytes": nbytes, "shared_input_joined": joined, "grouped_launch": grouped, "batch_1": m1}
 
 
 def bench_sweep(args, mq, synth, torch):

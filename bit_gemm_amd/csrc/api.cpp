@@ -9,6 +9,7 @@
 #include <mutex>
 #include <new>
 #include <unordered_set>
+#include <vector>
 
 #include "mq_internal.h"
 #include "gemv_group.h"
@@ -335,8 +336,8 @@ MQ_API mq_status mq_linear_noalloc(const void* X_dev_fp16, int64_t M, const mq_p
 }
 
 // n layers, each with its own input: one launch of the grouped decode kernel
-// per run of up to kGroupMax layers when they all qualify, else mq_linear per
-// layer. Everything is validated before the first launch.
+// per run of up to kGroupMax layers that qualify, mq_linear for the others.
+// Everything is validated before the first launch.
 MQ_API mq_status mq_linear_group(const void* const* X_dev_fp16, int64_t M, const mq_packed* const* p,
                                  void* const* Y_dev_fp16, int32_t n, void* hip_stream) {
   if (!X_dev_fp16 || !p || !Y_dev_fp16 || n < 1 || M <= 0) return MQ_ERR_INVALID_ARG;
@@ -347,20 +348,32 @@ MQ_API mq_status mq_linear_group(const void* const* X_dev_fp16, int64_t M, const
       return MQ_ERR_INVALID_ARG;
     if (M > (int64_t(1) << 31) / p[i]->K || M > (int64_t(1) << 31) / p[i]->N) return MQ_ERR_UNSUPPORTED;
   }
-  bool grouped = true;
-  for (int32_t i0 = 0; i0 < n && grouped; i0 += mq::kGroupMax)
-    grouped = mq::gemv_group_takes(p + i0, std::min<int32_t>(mq::kGroupMax, n - i0), M);
-  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  if (grouped) {
-    for (int32_t i0 = 0; i0 < n; i0 += mq::kGroupMax) {
-      const mq_status st = from_hip(mq::launch_gemv_group(
-          p + i0, reinterpret_cast<const uint16_t* const*>(X_dev_fp16 + i0), M,
-          reinterpret_cast<uint16_t* const*>(Y_dev_fp16 + i0), std::min<int32_t>(mq::kGroupMax, n - i0), s));
-      if (st != MQ_OK) return st;
-    }
-    return MQ_OK;
-  }
+  // the layers that can share a launch (with the first such layer's group
+  // size and device) go together, in runs of up to kGroupMax; the others run
+  // on their own, as mq_linear would
+  std::vector<const mq_packed*> gp;
+  std::vector<const uint16_t*> gx;
+  std::vector<uint16_t*> gy;
+  std::vector<int32_t> solo;
   for (int32_t i = 0; i < n; ++i) {
+    const bool fits = mq::gemv_group_takes(p + i, 1, M) &&
+                      (gp.empty() || (p[i]->G == gp[0]->G && p[i]->device == gp[0]->device));
+    if (fits) {
+      gp.push_back(p[i]);
+      gx.push_back(static_cast<const uint16_t*>(X_dev_fp16[i]));
+      gy.push_back(static_cast<uint16_t*>(Y_dev_fp16[i]));
+    } else {
+      solo.push_back(i);
+    }
+  }
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const int32_t ng = (int32_t)gp.size();
+  for (int32_t i0 = 0; i0 < ng; i0 += mq::kGroupMax) {
+    const mq_status st = from_hip(mq::launch_gemv_group(gp.data() + i0, gx.data() + i0, M, gy.data() + i0,
+                                                        std::min<int32_t>(mq::kGroupMax, ng - i0), s));
+    if (st != MQ_OK) return st;
+  }
+  for (const int32_t i : solo) {
     const mq_status st = linear_impl(X_dev_fp16[i], M, p[i], Y_dev_fp16[i], hip_stream, MQ_KERNEL_AUTO);
     if (st != MQ_OK) return st;
   }

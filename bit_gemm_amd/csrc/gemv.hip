@@ -821,6 +821,27 @@ __global__ __launch_bounds__(512) void k_gemv_r_group(const GroupR G, int M) {
                                   G.Y[li], M, G.N[li], G.Nb[li], G.zero_off[li], none, (b - G.wg0[li]) * R);
 }
 
+// The same for 1..4 tokens: k_gemv_x's body, one row block per workgroup,
+// for layers whose densest row block holds at most kRegChunks residual
+// chunks (the variant with no LDS staging; wg0[i] = the row blocks before
+// layer i).
+template <int GSH, int XR>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 6 : 5, 8))) void k_gemv_x_group(
+    const GroupR G, int M) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][4096 + kXPad]
+  __shared__ float4_t red[kWaves][64];
+  __shared__ __attribute__((aligned(16))) uint8_t stg[16];
+  const int b = (int)blockIdx.x;
+  int li = 0;
+#pragma unroll
+  for (int i = 1; i < kGroupMax; ++i) li += (i < G.n && b >= G.wg0[i]) ? 1 : 0;
+  li = __builtin_amdgcn_readfirstlane(li);
+  const DenseRes none{nullptr, nullptr, nullptr, nullptr, 0u};
+  gemv_x_block<GSH, XR, false, 0, false>(G.tiles[li], G.scales[li], G.sstride[li], G.tile_ptr[li], G.entries[li],
+                                         G.X[li], G.Y[li], M, G.N[li], G.zero_off[li], none, xs, red, stg,
+                                         b - G.wg0[li], 0u, 0u);
+}
+
 // General decode kernel. KS waves per row block. GSH = log2(128 / G).
 // XR > 0: X is copied whole into LDS ([M][K] within [XR][K]) and published
 // before the code tiles are requested, else X fragments come from global
@@ -1146,8 +1167,31 @@ hipError_t launch_r_group_any(GroupR& G, int M, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int GSH, int XR>
+hipError_t launch_x_group(GroupR& G, int M, hipStream_t s) {
+  constexpr size_t lds = (size_t)XR * (4096 + kXPad) * 2;
+  static bool done = false;
+  if (!done) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_x_group<GSH, XR>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    done = true;
+  }
+  int wg = 0;
+  for (int i = 0; i < G.n; ++i) {
+    G.wg0[i] = wg;
+    wg += G.Nb[i];
+  }
+  for (int i = G.n; i <= kGroupMax; ++i) G.wg0[i] = wg;
+  k_gemv_x_group<GSH, XR><<<dim3((unsigned)wg), dim3(512), lds, s>>>(G, M);
+  return hipGetLastError();
+}
+
 template <int GSH>
 hipError_t launch_group_g(GroupR& G, int M, hipStream_t s) {
+  if (M == 1) return launch_x_group<GSH, 1>(G, M, s);
+  if (M == 2) return launch_x_group<GSH, 2>(G, M, s);
+  if (M <= 4) return launch_x_group<GSH, 4>(G, M, s);
   return M <= 8 ? launch_r_group_any<GSH, 8>(G, M, s) : launch_r_group_any<GSH, 16>(G, M, s);
 }
 
@@ -1223,9 +1267,13 @@ hipError_t run_g(const mq_packed* p, const uint16_t* X, int M, uint16_t* Y, hipS
 }  // namespace
 
 bool gemv_group_takes(const mq_packed* const* p, int n, int64_t M) {
-  if (n < 1 || n > kGroupMax || M < 5 || M > 16) return false;
-  for (int i = 0; i < n; ++i)
+  if (n < 1 || n > kGroupMax || M < 1 || M > 16) return false;
+  for (int i = 0; i < n; ++i) {
     if (p[i]->K != 4096 || p[i]->blocks || p[i]->G != p[0]->G || p[i]->device != p[0]->device) return false;
+    // up to 4 tokens, the kernel variant that holds a row block's residual
+    // chunks in registers only (the one launch_x_res picks for such layers)
+    if (M <= 4 && p[i]->max_rb / (uint32_t)kChunk > (uint32_t)kRegChunks) return false;
+  }
   return true;
 }
 

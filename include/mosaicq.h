@@ -123,12 +123,14 @@ mq_status mq_linear_noalloc(const void* X_dev_fp16, int64_t M, const mq_packed* 
  * (say the linears of one transformer block at decode): Y[i] = the fused
  * W4 + sparse-residual linear of X[i] with p[i] (MosaicQuant explainer,
  * Methodology section 3), each equal, bit for bit, to mq_linear(X[i], M, p[i],
- * Y[i]) on the same stream. When every layer has K = 4096, no block residual
- * (mq_pack_blocks), one group size and one device, and 5 <= M <= 16, up to 8
- * layers run in one kernel launch (workgroups take several row blocks of one
- * layer, so the input is copied into LDS fewer times and the layers' ramps
- * and tails overlap); otherwise, and for more than 8 layers, the layers are
- * launched in order as mq_linear would.
+ * Y[i]) on the same stream. Layers with K = 4096 and no block residual
+ * (mq_pack_blocks), at 1 <= M <= 16 (for M <= 4 also: no row block of 16 rows
+ * with more than 512 residual entries), can share a launch:
+ * the layers that meet these (with the group size and device of the first
+ * of them) run in one kernel launch per 8 (from 5 tokens on, workgroups take
+ * several row blocks of one layer, so the input is copied into LDS fewer
+ * times; at any M the layers' ramps and tails overlap), and the others are
+ * launched after them as mq_linear would.
  *
  *   X_dev_fp16   n pointers (host array) to [M, p[i]->K] fp16 inputs (device,
  *                16-byte aligned); inputs may be shared between layers

@@ -1,9 +1,11 @@
 """mq_linear_group: several layers, each with its own input, in one call. Every
 output must equal that layer's own mq_linear bit for bit, whether the layers
-share one launch (K = 4096, 5..16 tokens, one group size, no block residual:
-1 to 5 row blocks per workgroup, by the group's rows and group size) or fall
-back to launches of their own; one small group is also checked against the float64
-oracle of the dequantised weights."""
+share one launch (K = 4096, 1..16 tokens, one group size, no block residual;
+from 5 tokens on 1 to 5 row blocks per workgroup, by the group's rows and
+group size; up to 4 tokens one row block per workgroup, for layers whose row
+blocks hold at most 16 residual chunks) or fall back to launches of their
+own; one small group is also checked against the float64 oracle of the
+dequantised weights."""
 import ctypes
 
 import numpy as np
@@ -60,12 +62,30 @@ BLOCK = [(4096, 0.005, ()), (4096, 0.005, ()), (4096, 0.0, ()), (4096, 0.005, (7
          (11008, 0.005, ()), (11008, 0.005, ())]
 
 
-@pytest.mark.parametrize("M", [5, 8, 16])
+def _densest_row_block_chunks(mq, p):
+    """Residual chunks (32 entries, each row block padded) of the densest row
+    block of a handle, from its canonical CSR."""
+    rp = mq.mq_export_canonical(p)["row_ptr"].cpu().numpy().astype(np.int64)
+    per_row = np.zeros(-(-p.N // 16) * 16, dtype=np.int64)
+    per_row[:p.N] = np.diff(rp)
+    blk = per_row.reshape(-1, 16).sum(1)
+    return int(((blk + 31) // 32).max())
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16])
 def test_block_group_equals_single_launches(mq, M):
-    _, ps = _packs(mq, BLOCK, 4096, 128, seed=11)
-    _check_equal_to_single(mq, ps, _inputs(M, [4096] * len(ps), seed=M), "block")
-    for p in ps:
-        p.free()
+    """The block's layers as above (the one with outlier rows has row blocks
+    of more than 16 residual chunks, so up to 4 tokens it takes a launch of
+    its own after the others' shared one), and at a residual density of
+    0.2 % without the outlier rows (at most 16 chunks per row block: one
+    launch at any M)."""
+    for spec, what in ((BLOCK, "block"), ([(N, 0.002, ()) for N, _, _ in BLOCK], "block, rho 0.2 %")):
+        _, ps = _packs(mq, spec, 4096, 128, seed=11)
+        dense = max(_densest_row_block_chunks(mq, p) for p in ps)
+        assert (dense > 16) == (spec is BLOCK), dense   # which path up to 4 tokens
+        _check_equal_to_single(mq, ps, _inputs(M, [4096] * len(ps), seed=M), what)
+        for p in ps:
+            p.free()
 
 
 # (spec, group size) and the row blocks per workgroup the launcher picks:
@@ -81,7 +101,7 @@ FOUR = [(4096, 0.005, ()), (4096, 0.003, ()), (4096, 0.0, ()), (1000, 0.01, (999
     (FOUR, 32),
     ([(11008, 0.005, (11000,))], 128),
 ])
-@pytest.mark.parametrize("M", [6, 13])
+@pytest.mark.parametrize("M", [2, 6, 13])
 def test_group_shapes_equal_single_launches(mq, spec, G, M):
     _, ps = _packs(mq, spec, 4096, G, seed=23)
     _check_equal_to_single(mq, ps, _inputs(M, [4096] * len(ps), seed=100 + M), f"G={G}")
@@ -89,14 +109,16 @@ def test_group_shapes_equal_single_launches(mq, spec, G, M):
         p.free()
 
 
-def test_group_matches_the_oracle(mq):
-    spec = [(1000, 0.01, (5,)), (272, 0.004, ()), (40, 0.0, ())]
+@pytest.mark.parametrize("M", [1, 16])
+def test_group_matches_the_oracle(mq, M):
+    spec = [(1000, 0.002, ()), (272, 0.001, ()), (40, 0.0, ())]   # at most 16 chunks per row block
     Ws, ps = _packs(mq, spec, 4096, 128, seed=41)
-    Xs = _inputs(16, [4096] * 3, seed=5)
+    assert max(_densest_row_block_chunks(mq, p) for p in ps) <= 16   # one launch at M = 1 too
+    Xs = _inputs(M, [4096] * 3, seed=5)
     Ys = _check_equal_to_single(mq, ps, Xs, "oracle")
     for W, (N, rho, _), X, Y in zip(Ws, spec, Xs, Ys):
         Wt = oracle.dequant(oracle.pack(W, 128, rho))
-        check_linear(Y.cpu().numpy(), X, Wt, f"group N={N}")
+        check_linear(Y.cpu().numpy(), X, Wt, f"group N={N} M={M}")
     for p in ps:
         p.free()
 
@@ -112,12 +134,12 @@ def test_more_than_eight_layers_and_a_shared_input(mq):
 
 def test_layers_that_cannot_share_a_launch(mq):
     import torch
-    # another K, then too few and too many tokens for the grouped kernel
+    # another K, then too many tokens for the grouped kernels
     _, ps = _packs(mq, [(512, 0.01, ()), (300, 0.01, ())], 4096, 128, seed=71)
     _, qs = _packs(mq, [(256, 0.01, ())], 1024, 128, seed=72)
     _check_equal_to_single(mq, ps + qs, _inputs(16, [4096, 4096, 1024], seed=9), "mixed K")
-    for M in (3, 20):
-        _check_equal_to_single(mq, ps, _inputs(M, [4096, 4096], seed=M), "M outside 5..16")
+    for M in (20, 64):
+        _check_equal_to_single(mq, ps, _inputs(M, [4096, 4096], seed=M), "M above 16")
     # one group size per launch, and a block residual
     _, gs = _packs(mq, [(256, 0.01, ())], 4096, 64, seed=73)
     _check_equal_to_single(mq, ps + gs, _inputs(8, [4096] * 3, seed=4), "two group sizes")
@@ -148,12 +170,13 @@ def test_group_argument_errors(mq):
     ps[0].free()
 
 
-def test_group_graph_replay(mq):
+@pytest.mark.parametrize("M", [1, 16])
+def test_group_graph_replay(mq, M):
     import torch
     spec = [(1024, 0.005, ()), (2048, 0.01, ()), (512, 0.0, ())]
     _, ps = _packs(mq, spec, 4096, 128, seed=91)
-    Xs = [to_dev(x) for x in _inputs(16, [4096] * 3, seed=2)]
-    Ys = [torch.empty((16, p.N), dtype=torch.float16, device="cuda") for p in ps]
+    Xs = [to_dev(x) for x in _inputs(M, [4096] * 3, seed=2)]
+    Ys = [torch.empty((M, p.N), dtype=torch.float16, device="cuda") for p in ps]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
