@@ -367,10 +367,9 @@ def mq_linear_group(Xs, packs, Ys=None, stream=None):
     Xs, packs = list(Xs), list(packs)
     if len(Xs) != len(packs) or not packs:
         raise ValueError("one input per layer, at least one layer")
+    xps = [_dev_fp16(X, "X") for X in Xs]
     M = Xs[0].shape[0] if Xs[0].dim() == 2 else -1
-    xps = []
     for X, p in zip(Xs, packs):
-        xps.append(_dev_fp16(X, "X"))
         if X.dim() != 2 or tuple(X.shape) != (M, p.K):
             raise ValueError(f"every X must be [{M}, K] of its layer (K = {p.K})")
     if Ys is None:

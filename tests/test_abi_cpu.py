@@ -164,3 +164,16 @@ def test_stream_read_validation(lib):
     assert f(ctypes.c_void_p((1 << 20) + 8), 1024, 4, FAKE, None) == -1
     assert f(FAKE, 1024, 4, ctypes.c_void_p((1 << 20) + 2), None) == -1
     assert f(FAKE, 16 * 256 * 16 + 16, 1, FAKE, None) == -1      # more than 16 loads per thread
+
+
+def test_linear_group_binding_checks_arguments(lib):
+    import torch
+    from bit_gemm_amd import mosaicq
+    with pytest.raises(ValueError):
+        mosaicq.mq_linear_group([], [])                      # no layer
+    with pytest.raises(ValueError):
+        mosaicq.mq_linear_group([torch.zeros(1)], [None, None])   # one input per layer
+    with pytest.raises(TypeError):
+        mosaicq.mq_linear_group([1], [None])                 # not a tensor
+    with pytest.raises(TypeError):
+        mosaicq.mq_linear_group([torch.zeros((2, 64), dtype=torch.float16)], [None])   # host memory
