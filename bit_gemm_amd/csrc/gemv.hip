@@ -821,25 +821,26 @@ __global__ __launch_bounds__(512) void k_gemv_r_group(const GroupR G, int M) {
                                   G.Y[li], M, G.N[li], G.Nb[li], G.zero_off[li], none, (b - G.wg0[li]) * R);
 }
 
-// The same for 1..4 tokens: k_gemv_x's body, one row block per workgroup,
-// for layers whose densest row block holds at most kRegChunks residual
-// chunks (the variant with no LDS staging; wg0[i] = the row blocks before
-// layer i).
-template <int GSH, int XR>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 6 : 5, 8))) void k_gemv_x_group(
-    const GroupR G, int M) {
+// The same for 1..4 tokens: k_gemv_x's body, one row block per workgroup
+// (wg0[i] = the row blocks before layer i), with RS = 0 when every layer's
+// densest row block holds at most kRegChunks residual chunks, else with the
+// chunks past those staged in LDS, up to 64 (a row block of at most
+// kRegChunks chunks stages none, and is computed as with RS = 0).
+template <int GSH, int XR, int RS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(GSH == 0 ? 6 : GSH == 2 && RS > 0 ? 4 : 5, 8)))
+void k_gemv_x_group(const GroupR G, int M) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [XR][4096 + kXPad]
   __shared__ float4_t red[kWaves][64];
-  __shared__ __attribute__((aligned(16))) uint8_t stg[16];
+  __shared__ __attribute__((aligned(16))) uint8_t stg[RS > 0 ? RS * kChunk * 4 : 16];   // staged chunks
   const int b = (int)blockIdx.x;
   int li = 0;
 #pragma unroll
   for (int i = 1; i < kGroupMax; ++i) li += (i < G.n && b >= G.wg0[i]) ? 1 : 0;
   li = __builtin_amdgcn_readfirstlane(li);
   const DenseRes none{nullptr, nullptr, nullptr, nullptr, 0u};
-  gemv_x_block<GSH, XR, false, 0, false>(G.tiles[li], G.scales[li], G.sstride[li], G.tile_ptr[li], G.entries[li],
-                                         G.X[li], G.Y[li], M, G.N[li], G.zero_off[li], none, xs, red, stg,
-                                         b - G.wg0[li], 0u, 0u);
+  gemv_x_block<GSH, XR, false, RS, false>(G.tiles[li], G.scales[li], G.sstride[li], G.tile_ptr[li], G.entries[li],
+                                          G.X[li], G.Y[li], M, G.N[li], G.zero_off[li], none, xs, red, stg,
+                                          b - G.wg0[li], 0u, 0u);
 }
 
 // General decode kernel. KS waves per row block. GSH = log2(128 / G).
@@ -1167,12 +1168,12 @@ hipError_t launch_r_group_any(GroupR& G, int M, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int GSH, int XR>
+template <int GSH, int XR, int RS>
 hipError_t launch_x_group(GroupR& G, int M, hipStream_t s) {
   constexpr size_t lds = (size_t)XR * (4096 + kXPad) * 2;
   static bool done = false;
   if (!done) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_x_group<GSH, XR>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_x_group<GSH, XR, RS>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     done = true;
@@ -1183,15 +1184,20 @@ hipError_t launch_x_group(GroupR& G, int M, hipStream_t s) {
     wg += G.Nb[i];
   }
   for (int i = G.n; i <= kGroupMax; ++i) G.wg0[i] = wg;
-  k_gemv_x_group<GSH, XR><<<dim3((unsigned)wg), dim3(512), lds, s>>>(G, M);
+  k_gemv_x_group<GSH, XR, RS><<<dim3((unsigned)wg), dim3(512), lds, s>>>(G, M);
   return hipGetLastError();
 }
 
+template <int GSH, int XR>
+hipError_t launch_x_group_rs(GroupR& G, int M, bool staged, hipStream_t s) {
+  return staged ? launch_x_group<GSH, XR, 64>(G, M, s) : launch_x_group<GSH, XR, 0>(G, M, s);
+}
+
 template <int GSH>
-hipError_t launch_group_g(GroupR& G, int M, hipStream_t s) {
-  if (M == 1) return launch_x_group<GSH, 1>(G, M, s);
-  if (M == 2) return launch_x_group<GSH, 2>(G, M, s);
-  if (M <= 4) return launch_x_group<GSH, 4>(G, M, s);
+hipError_t launch_group_g(GroupR& G, int M, bool staged, hipStream_t s) {
+  if (M == 1) return launch_x_group_rs<GSH, 1>(G, M, staged, s);
+  if (M == 2) return launch_x_group_rs<GSH, 2>(G, M, staged, s);
+  if (M <= 4) return launch_x_group_rs<GSH, 4>(G, M, staged, s);
   return M <= 8 ? launch_r_group_any<GSH, 8>(G, M, s) : launch_r_group_any<GSH, 16>(G, M, s);
 }
 
@@ -1270,9 +1276,9 @@ bool gemv_group_takes(const mq_packed* const* p, int n, int64_t M) {
   if (n < 1 || n > kGroupMax || M < 1 || M > 16) return false;
   for (int i = 0; i < n; ++i) {
     if (p[i]->K != 4096 || p[i]->blocks || p[i]->G != p[0]->G || p[i]->device != p[0]->device) return false;
-    // up to 4 tokens, the kernel variant that holds a row block's residual
-    // chunks in registers only (the one launch_x_res picks for such layers)
-    if (M <= 4 && p[i]->max_rb / (uint32_t)kChunk > (uint32_t)kRegChunks) return false;
+    // up to 4 tokens, row blocks of at most kRegChunks + 64 residual chunks
+    // (the kernel variants of launch_x_res without the overflow loop)
+    if (M <= 4 && p[i]->max_rb / (uint32_t)kChunk > (uint32_t)kRegChunks + 64) return false;
   }
   return true;
 }
@@ -1294,9 +1300,11 @@ hipError_t launch_gemv_group(const mq_packed* const* p, const uint16_t* const* X
     G.Nb[i] = (int)p[i]->Nb;
     G.zero_off[i] = (int)p[i]->stream_cap;
   }
-  if (p[0]->G == 128) return launch_group_g<0>(G, (int)M, s);
-  if (p[0]->G == 64) return launch_group_g<1>(G, (int)M, s);
-  return launch_group_g<2>(G, (int)M, s);
+  bool staged = false;   // up to 4 tokens: some row block holds more than kRegChunks chunks
+  for (int i = 0; i < n; ++i) staged |= p[i]->max_rb / (uint32_t)kChunk > (uint32_t)kRegChunks;
+  if (p[0]->G == 128) return launch_group_g<0>(G, (int)M, staged, s);
+  if (p[0]->G == 64) return launch_group_g<1>(G, (int)M, staged, s);
+  return launch_group_g<2>(G, (int)M, staged, s);
 }
 
 hipError_t launch_gemv(const mq_packed* p, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t s) {

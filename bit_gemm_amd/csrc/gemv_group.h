@@ -7,7 +7,7 @@ namespace mq {
 
 // Up to kGroupMax layers with K = 4096, one group size, no block residual,
 // and inputs of 1..16 tokens (up to 4 tokens: every layer's densest row block
-// within 16 residual chunks of 32 entries) run in one launch; each output
+// within 80 residual chunks of 32 entries) run in one launch; each output
 // equals that layer's own launch bit for bit.
 constexpr int kGroupMax = 8;
 bool gemv_group_takes(const mq_packed* const* p, int n, int64_t M);

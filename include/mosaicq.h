@@ -125,7 +125,7 @@ mq_status mq_linear_noalloc(const void* X_dev_fp16, int64_t M, const mq_packed* 
  * Methodology section 3), each equal, bit for bit, to mq_linear(X[i], M, p[i],
  * Y[i]) on the same stream. Layers with K = 4096 and no block residual
  * (mq_pack_blocks), at 1 <= M <= 16 (for M <= 4 also: no row block of 16 rows
- * with more than 512 residual entries), can share a launch:
+ * with more than 2560 residual entries), can share a launch:
  * the layers that meet these (with the group size and device of the first
  * of them) run in one kernel launch per 8 (from 5 tokens on, workgroups take
  * several row blocks of one layer, so the input is copied into LDS fewer

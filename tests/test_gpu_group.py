@@ -3,8 +3,8 @@ output must equal that layer's own mq_linear bit for bit, whether the layers
 share one launch (K = 4096, 1..16 tokens, one group size, no block residual;
 from 5 tokens on 1 to 5 row blocks per workgroup, by the group's rows and
 group size; up to 4 tokens one row block per workgroup, for layers whose row
-blocks hold at most 16 residual chunks) or fall back to launches of their
-own; one small group is also checked against the float64 oracle of the
+blocks hold at most 80 residual chunks, staging those past 16 in LDS when
+any layer has such a row block) or fall back to launches of their own; one small group is also checked against the float64 oracle of the
 dequantised weights."""
 import ctypes
 
@@ -75,14 +75,14 @@ def _densest_row_block_chunks(mq, p):
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16])
 def test_block_group_equals_single_launches(mq, M):
     """The block's layers as above (the one with outlier rows has row blocks
-    of more than 16 residual chunks, so up to 4 tokens it takes a launch of
+    of more than 80 residual chunks, so up to 4 tokens it takes a launch of
     its own after the others' shared one), and at a residual density of
     0.2 % without the outlier rows (at most 16 chunks per row block: one
-    launch at any M)."""
+    launch at any M, nothing staged)."""
     for spec, what in ((BLOCK, "block"), ([(N, 0.002, ()) for N, _, _ in BLOCK], "block, rho 0.2 %")):
         _, ps = _packs(mq, spec, 4096, 128, seed=11)
         dense = max(_densest_row_block_chunks(mq, p) for p in ps)
-        assert (dense > 16) == (spec is BLOCK), dense   # which path up to 4 tokens
+        assert (dense > 80) == (spec is BLOCK) and (dense <= 16) == (spec is not BLOCK), dense
         _check_equal_to_single(mq, ps, _inputs(M, [4096] * len(ps), seed=M), what)
         for p in ps:
             p.free()
@@ -105,6 +105,21 @@ FOUR = [(4096, 0.005, ()), (4096, 0.003, ()), (4096, 0.0, ()), (1000, 0.01, (999
 def test_group_shapes_equal_single_launches(mq, spec, G, M):
     _, ps = _packs(mq, spec, 4096, G, seed=23)
     _check_equal_to_single(mq, ps, _inputs(M, [4096] * len(ps), seed=100 + M), f"G={G}")
+    for p in ps:
+        p.free()
+
+
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_small_batch_group_with_staged_chunks(mq, M):
+    """Up to 4 tokens, a layer whose densest row block holds 17..80 residual
+    chunks makes the shared launch stage the chunks past 16 in LDS; the
+    layers with at most 16 per row block stage none there, and every output
+    still equals the layer's own launch (which picks its variant alone)."""
+    spec = [(4096, 0.006, ()), (2048, 0.002, ()), (1000, 0.0, ()), (520, 0.001, ())]
+    _, ps = _packs(mq, spec, 4096, 128, seed=51)
+    chunks = [_densest_row_block_chunks(mq, p) for p in ps]
+    assert 16 < chunks[0] <= 80 and max(chunks[1:]) <= 16, chunks
+    _check_equal_to_single(mq, ps, _inputs(M, [4096] * len(ps), seed=70 + M), "staged")
     for p in ps:
         p.free()
 
