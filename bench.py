@@ -67,6 +67,13 @@ def decode_bytes(p, M):
     return p.canonical_bytes() + 2 * M * p.K + 2 * M * p.N
 
 
+def attainable_tflops(flops, nbytes):
+    """Roofline ceiling of a launch: min(dense fp16 MFMA peak, arithmetic
+    intensity x HBM peak), in TFLOP/s (thin GEMMs at a few dozen tokens sit
+    below the ridge, about 315 FLOP per byte)."""
+    return min(FP16_PEAK_TFLOPS, flops / nbytes * HBM_PEAK_GBS / 1e3)
+
+
 def time_events(fn, n):
     import torch
     torch.cuda.synchronize()
@@ -574,6 +581,9 @@ def bench_sweep(args, mq, synth, torch):
                 steps = max(20, args.steps // 4) if M <= 64 else 20
                 us = replay_spread(torch, one, max(2, args.warmup // 4), steps, reps=5)[0] * 1e3
                 entry["us"][str(M)] = round(us, 2)
+                flops = 2.0 * M * layer0.N * layer0.K
+                att = attainable_tflops(flops, p.canonical_bytes() + 2 * M * layer0.K + 2 * M * layer0.N)
+                entry.setdefault("frac_attainable", {})[str(M)] = round(flops / (us * 1e-6) / 1e12 / att, 4)
             for c in copies:
                 c.free()
             per[str(rho)] = entry
@@ -589,7 +599,8 @@ def bench_mid(args, mq, synth, torch):
     """Mid-size batches on the 14336x4096 sweep layer (columns placement):
     16, 32, 48 and 64 tokens through mq_linear (the mid-size kernel), at
     rho = 0 and 0.005, rotated copies, graph replay. Bytes: the packed layer
-    as stored plus X and Y; FLOPs: 2 M N K."""
+    as stored plus X and Y; FLOPs: 2 M N K; each against min(MFMA peak,
+    intensity x HBM peak)."""
     layer = synth.sweep_layer("columns", 0.0)
     W = torch.from_numpy(layer.W()).cuda()
     Ms = (16, 32, 48, 64)
@@ -606,9 +617,12 @@ def bench_mid(args, mq, synth, torch):
                 mq.mq_linear(Xs[M], copies[i % ncopy], Ys[M])
             med, p10, p90 = replay_spread(torch, one, max(2, args.warmup // 4), max(20, args.steps // 2), reps=5)
             nbytes = p.canonical_bytes() + 2 * M * layer.K + 2 * M * layer.N
+            flops = 2.0 * M * layer.N * layer.K
+            tflops = flops / (med * 1e-3) / 1e12
+            att = attainable_tflops(flops, nbytes)
             per[str(M)] = {"us": round(med * 1e3, 2), "p10_us": round(p10 * 1e3, 2), "p90_us": round(p90 * 1e3, 2),
-                           "GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
-                           "TFLOPs": round(2.0 * M * layer.N * layer.K / (med * 1e-3) / 1e12, 1)}
+                           "GBps": round(nbytes / (med * 1e-3) / 1e9, 1), "TFLOPs": round(tflops, 1),
+                           "attainable_TFLOPs": round(att, 1), "frac_attainable": round(tflops / att, 4)}
         for c in copies:
             c.free()
         out[str(rho)] = {"nnz": p.nnz, "per_M": per}
